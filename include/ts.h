@@ -1,0 +1,195 @@
+/*
+ * ts.h — C ABI of the TokenSelect decode-time hot path on MI355X (gfx950).
+ *
+ * What the library computes (TokenSelect README, "Key Takeaways"; GrooveSquid
+ * summary of the TokenSelect paper, "Medium Difficulty Summary"):
+ *   1. per-head criticality of every cached token: s[h,j] = scale * <q[h], K[j, kv(h)]>,
+ *      with grouped-query attention, kv(h) = h / (Hq / Hkv);
+ *   2. per-head soft voting: softmax of s[h,:] over all N cached tokens, summed
+ *      over the Hq heads, v[j] = sum_h softmax_h(s)[j];
+ *   3. top-k: the k_eff = min(k, N) tokens with the largest votes, ties to the
+ *      lower index, returned ascending and padded with -1 up to k;
+ *   4. sparse attention: every query head attends, with the same scale, over
+ *      the selected rows only (softmax renormalised over them);
+ *   5. Selection Cache: when the cosine of the flattened query with the stored
+ *      query exceeds theta, the stored selection is reused and steps 1-3 skip.
+ *   plus a chunked-prefill variant of 1-3 in which query i of a chunk sits at
+ *   position q_pos0 + i and sees keys 0 .. q_pos0 + i only.
+ *
+ * Conventions for every entry point:
+ *   - Pointers are DEVICE pointers unless marked [host]. The caller owns every
+ *     input, output and workspace buffer; the library never frees them.
+ *   - Calls are asynchronous on `stream` (a hipStream_t, NULL = default stream)
+ *     and never synchronise, except ts_sel_cache_create/destroy/stats, which
+ *     say so.
+ *   - The library allocates nothing on these calls, except inside
+ *     ts_sel_cache_create (freed by ts_sel_cache_destroy).
+ *   - All argument checks run on the host before anything is enqueued. On an
+ *     error nothing is enqueued, no output is touched, and ts_last_error()
+ *     describes the problem. A failed kernel launch returns TS_ERR_HIP.
+ *   - Per-sequence lengths live on the device and are not checked on the host:
+ *     0 <= seq_lens[b] <= max_len is the caller's contract. A length of 0 gives
+ *     zero outputs and an all -1 selection.
+ *   - Entry points are re-entrant; calls that share a workspace or a
+ *     ts_sel_cache must be ordered on one stream.
+ *
+ * Supported shapes: head_dim 64 or 128; dtype fp32 or bf16 (q, K and V share
+ * it; accumulation is fp32); num_kv_heads divides num_q_heads; num_kv_heads <= 64.
+ */
+#ifndef TS_H
+#define TS_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define TS_ABI_VERSION 1
+
+typedef enum ts_status {
+  TS_OK = 0,
+  TS_ERR_INVALID_ARG = 1,   /* null pointer, bad size or inconsistent shape       */
+  TS_ERR_UNSUPPORTED = 2,   /* valid but not implemented (head_dim, head counts)  */
+  TS_ERR_WORKSPACE = 3,     /* workspace smaller than the matching *_workspace_size */
+  TS_ERR_HIP = 4            /* a HIP runtime call or kernel launch failed         */
+} ts_status;
+
+typedef enum ts_dtype { TS_F32 = 0, TS_BF16 = 1 } ts_dtype;
+
+/* Shape and memory layout of one layer's KV cache.
+ *   contiguous (page_size == 0): K and V are [batch][max_len][num_kv_heads][head_dim];
+ *   paged      (page_size  > 0): K and V are pools [num_pages][page_size][num_kv_heads][head_dim]
+ *     and token j of sequence b lives in pool page page_table[b * page_table_stride + j / page_size],
+ *     slot j % page_size. page_size must be a power of two.                              */
+typedef struct ts_kv_layout {
+  int32_t num_q_heads;        /* Hq                                                  */
+  int32_t num_kv_heads;       /* Hkv, divides Hq                                     */
+  int32_t head_dim;           /* d: 64 or 128                                        */
+  int32_t dtype;              /* ts_dtype of q, K and V                              */
+  float   scale;              /* logit scale; <= 0 selects 1/sqrt(head_dim)          */
+  int32_t page_size;          /* 0 = contiguous                                      */
+  int32_t max_len;            /* token capacity of one sequence (> 0)                */
+  int32_t page_table_stride;  /* int32 entries per page-table row (paged only)       */
+} ts_kv_layout;
+
+int32_t     ts_abi_version(void);
+/* Static string for a ts_status value. */
+const char* ts_status_string(int32_t status);
+/* Detail of the last error raised on the calling thread ("" if none). */
+const char* ts_last_error(void);
+
+/* ---------------------------------------------------------------------------
+ * ts_score — steps 1-2 (scoring and per-head soft voting) for one query per
+ * sequence.
+ *   q        [batch][Hq][d] (dtype)
+ *   k_cache  see ts_kv_layout; page_table [batch][page_table_stride] int32 or NULL
+ *   seq_lens [batch] int32
+ *   votes    [batch][max_len] fp32 out; entries j >= seq_lens[b] are left unwritten.
+ *            Each row sums to Hq (up to fp32 rounding).
+ *   ws       scratch of at least ts_score_workspace_size bytes (256-byte aligned)
+ * ------------------------------------------------------------------------- */
+ts_status ts_score_workspace_size(const ts_kv_layout* layout /*[host]*/, int32_t batch,
+                                  size_t* bytes /*[host] out*/);
+ts_status ts_score(const ts_kv_layout* layout /*[host]*/, int32_t batch, const void* q,
+                   const void* k_cache, const int32_t* page_table, const int32_t* seq_lens,
+                   float* votes, void* ws, size_t ws_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * ts_topk — step 3 on `rows` independent rows.
+ *   votes    [rows][row_stride] fp32; only the first row_lens[r] entries of a row count
+ *   row_lens [rows] int32 (device), 0 <= row_lens[r] <= row_stride
+ *   idx      [rows][k] int32 out: the min(k, row_lens[r]) largest entries, ties to the
+ *            lower index, ascending, then -1 padding. Exact (a radix select on the
+ *            order-preserving integer image of the floats; -0.0 equals +0.0).
+ *   k >= 1.
+ * ------------------------------------------------------------------------- */
+ts_status ts_topk_workspace_size(int32_t rows, int32_t row_stride, int32_t k,
+                                 size_t* bytes /*[host] out*/);
+ts_status ts_topk(int32_t rows, int32_t row_stride, const float* votes, const int32_t* row_lens,
+                  int32_t k, int32_t* idx, void* ws, size_t ws_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * ts_sparse_attend — step 4: attention of every query head over the rows a
+ * selection names.
+ *   idx  [batch][k] int32: token indices < seq_lens[b]; negative entries are skipped
+ *        (any order; duplicates count twice).
+ *   out  [batch][Hq][d] fp32. A sequence with no valid index gets zeros.
+ * ------------------------------------------------------------------------- */
+ts_status ts_sparse_attend_workspace_size(const ts_kv_layout* layout /*[host]*/, int32_t batch,
+                                          int32_t k, size_t* bytes /*[host] out*/);
+ts_status ts_sparse_attend(const ts_kv_layout* layout /*[host]*/, int32_t batch, const void* q,
+                           const void* k_cache, const void* v_cache, const int32_t* page_table,
+                           const int32_t* seq_lens, const int32_t* idx, int32_t k, float* out,
+                           void* ws, size_t ws_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * Selection Cache state for up to max_batch sequences of one layer (step 5).
+ *   compare_mode 0: compare with the previous step's query (stored every step);
+ *   compare_mode 1: compare with the query of the last miss (the anchor).
+ * Per sequence it keeps the stored query (fp32, Hq*d), the last selection
+ * ([k] int32), a valid flag and hit/miss counters, all in device memory.
+ * A step hits when the state is valid and cos(q, stored) > theta (strict; the
+ * cosine is accumulated in fp64 over the flattened Hq*d query; a zero norm
+ * never hits). The first step, a step after reset and a step on an empty
+ * sequence miss; an empty sequence leaves the state invalid.
+ * ------------------------------------------------------------------------- */
+typedef struct ts_sel_cache ts_sel_cache;
+
+/* Allocates the device state (hipMalloc) and zeroes it; synchronises the device. */
+ts_status ts_sel_cache_create(int32_t max_batch, int32_t num_q_heads, int32_t head_dim, int32_t k,
+                              int32_t compare_mode, ts_sel_cache** out /*[host]*/);
+/* Marks every sequence invalid and clears the counters (asynchronous on stream). */
+ts_status ts_sel_cache_reset(ts_sel_cache* cache, void* stream);
+/* Frees the device state; synchronises the device. */
+ts_status ts_sel_cache_destroy(ts_sel_cache* cache);
+/* Copies hit and miss counts of sequences 0..n-1 to host arrays; synchronises `stream`. */
+ts_status ts_sel_cache_stats(ts_sel_cache* cache, int32_t n, int64_t* hits /*[host]*/,
+                             int64_t* misses /*[host]*/, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * ts_decode_step — one decode step of one layer for `batch` sequences:
+ * Selection-Cache check; on a miss steps 1-3 and a new stored selection; then
+ * step 4 with the current selection; then the state update.
+ *   q, k_cache, v_cache, page_table, seq_lens as in ts_score / ts_sparse_attend
+ *   theta    cosine threshold (a hit needs cos > theta)
+ *   out      [batch][Hq][d] fp32
+ *   idx_out  [batch][k] int32 or NULL: the selection used this step
+ *   hit_out  [batch] int32 or NULL: 1 where the stored selection was reused
+ * The layout's num_q_heads and head_dim must match the cache; batch <= max_batch.
+ * ------------------------------------------------------------------------- */
+ts_status ts_decode_step_workspace_size(const ts_kv_layout* layout /*[host]*/, int32_t batch,
+                                        int32_t k, size_t* bytes /*[host] out*/);
+ts_status ts_decode_step(ts_sel_cache* cache, const ts_kv_layout* layout /*[host]*/,
+                         int32_t batch, const void* q, const void* k_cache, const void* v_cache,
+                         const int32_t* page_table, const int32_t* seq_lens, double theta,
+                         float* out, int32_t* idx_out, int32_t* hit_out, void* ws,
+                         size_t ws_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * ts_score_prefill — steps 1-2 for a chunk of `chunk` consecutive queries
+ * (bf16 MFMA for the query-key products; fp32 softmax and votes).
+ *   q        [chunk][Hq][d] bf16, query i at absolute position q_pos0 + i
+ *   k_cache  [n_ctx][Hkv][d] bf16 contiguous (layout.page_size must be 0,
+ *            layout.dtype TS_BF16, layout.max_len >= n_ctx)
+ *   votes    [chunk][n_ctx] fp32 out: row i holds the soft vote over keys
+ *            0 .. q_pos0 + i; entries past that are written as 0.
+ *   Requires q_pos0 >= 0 and q_pos0 + chunk <= n_ctx.
+ * ts_select_prefill additionally runs step 3 on every row:
+ *   idx      [chunk][k] int32 out (row i selects from its q_pos0 + i + 1 keys).
+ * ------------------------------------------------------------------------- */
+ts_status ts_score_prefill_workspace_size(const ts_kv_layout* layout /*[host]*/, int32_t chunk,
+                                          int32_t n_ctx, int32_t k, size_t* bytes /*[host] out*/);
+ts_status ts_score_prefill(const ts_kv_layout* layout /*[host]*/, int32_t chunk, int32_t q_pos0,
+                           const void* q, const void* k_cache, int32_t n_ctx, float* votes,
+                           void* ws, size_t ws_bytes, void* stream);
+ts_status ts_select_prefill(const ts_kv_layout* layout /*[host]*/, int32_t chunk, int32_t q_pos0,
+                            const void* q, const void* k_cache, int32_t n_ctx, int32_t k,
+                            float* votes, int32_t* idx, void* ws, size_t ws_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TS_H */

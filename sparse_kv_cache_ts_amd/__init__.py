@@ -1,0 +1,332 @@
+"""TokenSelect decode-time hot path on MI355X: Python binding of libts.so.
+
+Argument marshalling only: every step runs in the HIP kernels behind the C
+ABI declared in include/ts.h. PyTorch supplies device memory and the current
+stream. If libts.so is missing the functions raise; there is no CPU fallback.
+
+    import sparse_kv_cache_ts_amd as ts
+    votes = ts.score(q, k_cache, seq_lens)                 # per-head soft votes
+    idx = ts.topk(votes, seq_lens, k)                      # [B][k] ascending, -1 padded
+    out = ts.sparse_attend(q, k_cache, v_cache, seq_lens, idx)
+    cache = ts.SelCache(max_batch, Hq, d, k)
+    out, idx, hit = cache.decode_step(q, k_cache, v_cache, seq_lens, theta=0.9)
+    votes, idx = ts.select_prefill(q_chunk, k_ctx, q_pos0, k)
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+__all__ = [
+    "load", "lib_path", "TsError", "KvLayout", "make_layout", "score", "topk", "sparse_attend",
+    "SelCache", "score_prefill", "select_prefill", "Workspace", "EXPORTS",
+]
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+_LIB = None
+
+TS_OK, TS_ERR_INVALID_ARG, TS_ERR_UNSUPPORTED, TS_ERR_WORKSPACE, TS_ERR_HIP = range(5)
+TS_F32, TS_BF16 = 0, 1
+
+# every symbol include/ts.h declares
+EXPORTS = [
+    "ts_abi_version", "ts_status_string", "ts_last_error",
+    "ts_score_workspace_size", "ts_score",
+    "ts_topk_workspace_size", "ts_topk",
+    "ts_sparse_attend_workspace_size", "ts_sparse_attend",
+    "ts_sel_cache_create", "ts_sel_cache_reset", "ts_sel_cache_destroy", "ts_sel_cache_stats",
+    "ts_decode_step_workspace_size", "ts_decode_step",
+    "ts_score_prefill_workspace_size", "ts_score_prefill", "ts_select_prefill",
+]
+
+
+class TsError(RuntimeError):
+    def __init__(self, status: int, where: str, detail: str):
+        self.status = status
+        super().__init__(f"{where}: status {status}: {detail}")
+
+
+class KvLayout(ctypes.Structure):
+    _fields_ = [
+        ("num_q_heads", ctypes.c_int32), ("num_kv_heads", ctypes.c_int32),
+        ("head_dim", ctypes.c_int32), ("dtype", ctypes.c_int32), ("scale", ctypes.c_float),
+        ("page_size", ctypes.c_int32), ("max_len", ctypes.c_int32),
+        ("page_table_stride", ctypes.c_int32),
+    ]
+
+
+def lib_path() -> str:
+    return os.path.join(_PKG, "libts.so")
+
+
+def load():
+    """Load libts.so (built by `python -m sparse_kv_cache_ts_amd._build`)."""
+    global _LIB
+    if _LIB is not None:
+        return _LIB
+    path = lib_path()
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is not built; run `python -m sparse_kv_cache_ts_amd._build`")
+    lib = ctypes.CDLL(path)
+    P, I32, SZ, F32, F64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t, ctypes.c_float, ctypes.c_double
+    L = ctypes.POINTER(KvLayout)
+    SZP = ctypes.POINTER(ctypes.c_size_t)
+    sig = {
+        "ts_abi_version": ([], I32),
+        "ts_status_string": ([I32], ctypes.c_char_p),
+        "ts_last_error": ([], ctypes.c_char_p),
+        "ts_score_workspace_size": ([L, I32, SZP], I32),
+        "ts_score": ([L, I32, P, P, P, P, P, P, SZ, P], I32),
+        "ts_topk_workspace_size": ([I32, I32, I32, SZP], I32),
+        "ts_topk": ([I32, I32, P, P, I32, P, P, SZ, P], I32),
+        "ts_sparse_attend_workspace_size": ([L, I32, I32, SZP], I32),
+        "ts_sparse_attend": ([L, I32, P, P, P, P, P, P, I32, P, P, SZ, P], I32),
+        "ts_sel_cache_create": ([I32, I32, I32, I32, I32, ctypes.POINTER(P)], I32),
+        "ts_sel_cache_reset": ([P, P], I32),
+        "ts_sel_cache_destroy": ([P], I32),
+        "ts_sel_cache_stats": ([P, I32, P, P, P], I32),
+        "ts_decode_step_workspace_size": ([L, I32, I32, SZP], I32),
+        "ts_decode_step": ([P, L, I32, P, P, P, P, P, F64, P, P, P, P, SZ, P], I32),
+        "ts_score_prefill_workspace_size": ([L, I32, I32, I32, SZP], I32),
+        "ts_score_prefill": ([L, I32, I32, P, P, I32, P, P, SZ, P], I32),
+        "ts_select_prefill": ([L, I32, I32, P, P, I32, I32, P, P, P, SZ, P], I32),
+    }
+    for name, (args, res) in sig.items():
+        fn = getattr(lib, name)
+        fn.argtypes = args
+        fn.restype = res
+    _LIB = lib
+    return lib
+
+
+def _check(st: int, where: str):
+    if st != TS_OK:
+        lib = load()
+        raise TsError(st, where, lib.ts_last_error().decode())
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream=None):
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return TS_BF16
+    if t.dtype == torch.float32:
+        return TS_F32
+    raise TypeError(f"unsupported dtype {t.dtype} (bf16 or fp32)")
+
+
+def _need_cuda(*ts):
+    for t in ts:
+        if t is not None and (not t.is_cuda or not t.is_contiguous()):
+            raise ValueError("tensors must be contiguous CUDA (HIP) tensors")
+
+
+def make_layout(q: torch.Tensor, k_cache: torch.Tensor, page_table: Optional[torch.Tensor] = None,
+                scale: Optional[float] = None) -> KvLayout:
+    """Layout from tensor shapes: q [B][Hq][d]; K contiguous [B][max_len][Hkv][d]
+    or, with a page table [B][stride], a pool [P][page_size][Hkv][d]."""
+    B, Hq, d = q.shape
+    if page_table is None:
+        _, max_len, Hkv, dk = k_cache.shape
+        ps, stride = 0, 0
+    else:
+        _, ps, Hkv, dk = k_cache.shape
+        stride = page_table.shape[1]
+        max_len = stride * ps
+    if dk != d:
+        raise ValueError("q and K head_dim differ")
+    if k_cache.dtype != q.dtype:
+        raise ValueError("q and K dtypes differ")
+    return KvLayout(Hq, Hkv, d, _dtype_code(q), float(scale or 0.0), ps, max_len, stride)
+
+
+class Workspace:
+    """A reusable device scratch buffer (256-byte aligned by the allocator)."""
+
+    def __init__(self):
+        self.buf = None
+
+    def get(self, nbytes: int, device) -> torch.Tensor:
+        if self.buf is None or self.buf.numel() < nbytes or self.buf.device != device:
+            self.buf = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
+        return self.buf
+
+
+def _ws(nbytes: int, device, ws: Optional[Workspace]):
+    if ws is not None:
+        return ws.get(nbytes, device)
+    return torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
+
+
+def score(q, k_cache, seq_lens, page_table=None, scale=None, votes=None, ws=None, stream=None):
+    """Per-head soft votes [B][max_len] fp32 (entries past seq_lens[b] unspecified)."""
+    lib = load()
+    _need_cuda(q, k_cache, seq_lens, page_table)
+    L = make_layout(q, k_cache, page_table, scale)
+    B = q.shape[0]
+    if votes is None:
+        votes = torch.empty(B, L.max_len, dtype=torch.float32, device=q.device)
+    n = ctypes.c_size_t()
+    _check(lib.ts_score_workspace_size(ctypes.byref(L), B, ctypes.byref(n)), "ts_score_workspace_size")
+    w = _ws(n.value, q.device, ws)
+    _check(lib.ts_score(ctypes.byref(L), B, _ptr(q), _ptr(k_cache), _ptr(page_table), _ptr(seq_lens),
+                        _ptr(votes), _ptr(w), w.numel(), _stream(stream)), "ts_score")
+    return votes
+
+
+def topk(votes, row_lens, k, idx=None, ws=None, stream=None):
+    """Top-k of each row: [rows][k] int32, ascending, -1 padded, ties to the lower index."""
+    lib = load()
+    _need_cuda(votes, row_lens)
+    if votes.dtype != torch.float32 or row_lens.dtype != torch.int32:
+        raise TypeError("votes must be fp32 and row_lens int32")
+    rows, stride = votes.shape
+    if idx is None:
+        idx = torch.empty(rows, k, dtype=torch.int32, device=votes.device)
+    n = ctypes.c_size_t()
+    _check(lib.ts_topk_workspace_size(rows, stride, k, ctypes.byref(n)), "ts_topk_workspace_size")
+    w = _ws(n.value, votes.device, ws)
+    _check(lib.ts_topk(rows, stride, _ptr(votes), _ptr(row_lens), k, _ptr(idx), _ptr(w), w.numel(),
+                       _stream(stream)), "ts_topk")
+    return idx
+
+
+def sparse_attend(q, k_cache, v_cache, seq_lens, idx, page_table=None, scale=None, out=None,
+                  ws=None, stream=None):
+    """Attention of every query head over the rows idx names: [B][Hq][d] fp32."""
+    lib = load()
+    _need_cuda(q, k_cache, v_cache, seq_lens, idx, page_table)
+    if idx.dtype != torch.int32:
+        raise TypeError("idx must be int32")
+    L = make_layout(q, k_cache, page_table, scale)
+    B, Hq, d = q.shape
+    k = idx.shape[1]
+    if out is None:
+        out = torch.empty(B, Hq, d, dtype=torch.float32, device=q.device)
+    n = ctypes.c_size_t()
+    _check(lib.ts_sparse_attend_workspace_size(ctypes.byref(L), B, k, ctypes.byref(n)),
+           "ts_sparse_attend_workspace_size")
+    w = _ws(n.value, q.device, ws)
+    _check(lib.ts_sparse_attend(ctypes.byref(L), B, _ptr(q), _ptr(k_cache), _ptr(v_cache),
+                                _ptr(page_table), _ptr(seq_lens), _ptr(idx), k, _ptr(out), _ptr(w),
+                                w.numel(), _stream(stream)), "ts_sparse_attend")
+    return out
+
+
+class SelCache:
+    """Selection-Cache state of up to max_batch sequences (device memory)."""
+
+    def __init__(self, max_batch: int, num_q_heads: int, head_dim: int, k: int, mode: int = 0):
+        self._lib = load()
+        self.max_batch, self.num_q_heads, self.head_dim, self.k, self.mode = (
+            max_batch, num_q_heads, head_dim, k, mode)
+        h = ctypes.c_void_p()
+        _check(self._lib.ts_sel_cache_create(max_batch, num_q_heads, head_dim, k, mode,
+                                             ctypes.byref(h)), "ts_sel_cache_create")
+        self._h = h
+        self.ws = Workspace()
+
+    def close(self):
+        if self._h is not None and self._h.value:
+            _check(self._lib.ts_sel_cache_destroy(self._h), "ts_sel_cache_destroy")
+        self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def reset(self, stream=None):
+        _check(self._lib.ts_sel_cache_reset(self._h, _stream(stream)), "ts_sel_cache_reset")
+
+    def stats(self, n: Optional[int] = None, stream=None):
+        n = self.max_batch if n is None else n
+        hits = (ctypes.c_int64 * n)()
+        misses = (ctypes.c_int64 * n)()
+        _check(self._lib.ts_sel_cache_stats(self._h, n, hits, misses, _stream(stream)),
+               "ts_sel_cache_stats")
+        return list(hits), list(misses)
+
+    def workspace_size(self, layout: KvLayout, batch: int) -> int:
+        n = ctypes.c_size_t()
+        _check(self._lib.ts_decode_step_workspace_size(ctypes.byref(layout), batch, self.k,
+                                                       ctypes.byref(n)),
+               "ts_decode_step_workspace_size")
+        return n.value
+
+    def decode_step(self, q, k_cache, v_cache, seq_lens, theta: float, page_table=None, scale=None,
+                    out=None, idx_out=None, hit_out=None, want_idx=True, stream=None):
+        """One decode step: returns (out [B][Hq][d] fp32, idx [B][k] or None, hit [B] int32)."""
+        _need_cuda(q, k_cache, v_cache, seq_lens, page_table)
+        L = make_layout(q, k_cache, page_table, scale)
+        B = q.shape[0]
+        dev = q.device
+        if out is None:
+            out = torch.empty(B, self.num_q_heads, self.head_dim, dtype=torch.float32, device=dev)
+        if idx_out is None and want_idx:
+            idx_out = torch.empty(B, self.k, dtype=torch.int32, device=dev)
+        if hit_out is None:
+            hit_out = torch.empty(B, dtype=torch.int32, device=dev)
+        w = self.ws.get(self.workspace_size(L, B), dev)
+        _check(self._lib.ts_decode_step(self._h, ctypes.byref(L), B, _ptr(q), _ptr(k_cache),
+                                        _ptr(v_cache), _ptr(page_table), _ptr(seq_lens),
+                                        float(theta), _ptr(out), _ptr(idx_out), _ptr(hit_out),
+                                        _ptr(w), w.numel(), _stream(stream)), "ts_decode_step")
+        return out, idx_out, hit_out
+
+
+def _prefill_layout(q, k_ctx, scale):
+    C, Hq, d = q.shape
+    n_ctx, Hkv, dk = k_ctx.shape
+    if dk != d or q.dtype != k_ctx.dtype:
+        raise ValueError("q and K shapes/dtypes differ")
+    return KvLayout(Hq, Hkv, d, _dtype_code(q), float(scale or 0.0), 0, n_ctx, 0)
+
+
+def score_prefill(q, k_ctx, q_pos0: int, scale=None, votes=None, ws=None, stream=None):
+    """Causal soft votes of a prefill chunk: [chunk][n_ctx] fp32 (zeros past q_pos0+i)."""
+    lib = load()
+    _need_cuda(q, k_ctx)
+    L = _prefill_layout(q, k_ctx, scale)
+    C, n_ctx = q.shape[0], k_ctx.shape[0]
+    if votes is None:
+        votes = torch.empty(C, n_ctx, dtype=torch.float32, device=q.device)
+    n = ctypes.c_size_t()
+    _check(lib.ts_score_prefill_workspace_size(ctypes.byref(L), C, n_ctx, 1, ctypes.byref(n)),
+           "ts_score_prefill_workspace_size")
+    w = _ws(n.value, q.device, ws)
+    _check(lib.ts_score_prefill(ctypes.byref(L), C, q_pos0, _ptr(q), _ptr(k_ctx), n_ctx, _ptr(votes),
+                                _ptr(w), w.numel(), _stream(stream)), "ts_score_prefill")
+    return votes
+
+
+def select_prefill(q, k_ctx, q_pos0: int, k: int, scale=None, votes=None, idx=None, ws=None,
+                   stream=None):
+    """Soft votes and per-query top-k of a prefill chunk: (votes [C][n_ctx], idx [C][k])."""
+    lib = load()
+    _need_cuda(q, k_ctx)
+    L = _prefill_layout(q, k_ctx, scale)
+    C, n_ctx = q.shape[0], k_ctx.shape[0]
+    if votes is None:
+        votes = torch.empty(C, n_ctx, dtype=torch.float32, device=q.device)
+    if idx is None:
+        idx = torch.empty(C, k, dtype=torch.int32, device=q.device)
+    n = ctypes.c_size_t()
+    _check(lib.ts_score_prefill_workspace_size(ctypes.byref(L), C, n_ctx, k, ctypes.byref(n)),
+           "ts_score_prefill_workspace_size")
+    w = _ws(n.value, q.device, ws)
+    _check(lib.ts_select_prefill(ctypes.byref(L), C, q_pos0, _ptr(q), _ptr(k_ctx), n_ctx, k,
+                                 _ptr(votes), _ptr(idx), _ptr(w), w.numel(), _stream(stream)),
+           "ts_select_prefill")
+    return votes, idx

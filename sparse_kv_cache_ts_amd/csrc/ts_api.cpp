@@ -1,0 +1,629 @@
+// ts_api.cpp — the C ABI declared in include/ts.h: host-side validation,
+// workspace planning and launch sequencing. No kernel code lives here.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+
+#include "../../include/ts.h"
+#include "ts_internal.h"
+
+using namespace ts;
+
+struct ts_sel_cache {
+  SelCacheDev dev;
+  int device;
+};
+
+namespace {
+
+thread_local std::string g_last_error;
+
+ts_status fail(ts_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return st;
+}
+
+ts_status ok() {
+  g_last_error.clear();
+  return TS_OK;
+}
+
+ts_status hip_check(hipError_t e, const char* what) {
+  if (e != hipSuccess) return fail(TS_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+  return TS_OK;
+}
+
+struct Carve {
+  size_t off = 0;
+  size_t take(size_t bytes) {
+    size_t o = off;
+    off = align256(off + bytes);
+    return o;
+  }
+};
+
+template <typename T>
+T* at(void* ws, size_t off) {
+  return reinterpret_cast<T*>(static_cast<char*>(ws) + off);
+}
+
+bool is_pow2(int x) { return x > 0 && (x & (x - 1)) == 0; }
+int log2i(int x) {
+  int r = 0;
+  while ((1 << r) < x) ++r;
+  return r;
+}
+
+// Validated layout plus the derived launch geometry.
+struct Geo {
+  int Hq, Hkv, G, d, dtype, max_len, ps, ps_log2, pt_stride;
+  bool paged;
+  float scale;
+  int GS, nslices;   // query heads per KV head handled by one work-group, and slices
+};
+
+ts_status check_layout(const ts_kv_layout* L, int batch, Geo* g) {
+  if (!L) return fail(TS_ERR_INVALID_ARG, "layout is NULL");
+  if (batch < 1) return fail(TS_ERR_INVALID_ARG, "batch must be >= 1 (got %d)", batch);
+  if (L->num_q_heads < 1 || L->num_kv_heads < 1)
+    return fail(TS_ERR_INVALID_ARG, "head counts must be >= 1");
+  if (L->num_q_heads % L->num_kv_heads != 0)
+    return fail(TS_ERR_INVALID_ARG, "num_kv_heads (%d) must divide num_q_heads (%d)",
+                L->num_kv_heads, L->num_q_heads);
+  if (L->head_dim != 64 && L->head_dim != 128)
+    return fail(TS_ERR_UNSUPPORTED, "head_dim %d unsupported (64 or 128)", L->head_dim);
+  if (L->dtype != TS_F32 && L->dtype != TS_BF16)
+    return fail(TS_ERR_INVALID_ARG, "unknown dtype %d", L->dtype);
+  if (L->max_len < 1) return fail(TS_ERR_INVALID_ARG, "max_len must be >= 1");
+  if (L->num_kv_heads > kMaxHeadsPerWG)
+    return fail(TS_ERR_UNSUPPORTED, "num_kv_heads %d > %d", L->num_kv_heads, kMaxHeadsPerWG);
+  if (L->num_q_heads > kMaxQHeads)
+    return fail(TS_ERR_UNSUPPORTED, "num_q_heads %d > %d", L->num_q_heads, kMaxQHeads);
+  if (L->page_size < 0) return fail(TS_ERR_INVALID_ARG, "page_size must be >= 0");
+  if (L->page_size > 0) {
+    if (!is_pow2(L->page_size)) return fail(TS_ERR_INVALID_ARG, "page_size must be a power of two");
+    const long need = ((long)L->max_len + L->page_size - 1) / L->page_size;
+    if (L->page_table_stride < need)
+      return fail(TS_ERR_INVALID_ARG, "page_table_stride %d < pages of max_len (%ld)",
+                  L->page_table_stride, need);
+  }
+  if (!(std::isfinite(L->scale))) return fail(TS_ERR_INVALID_ARG, "scale is not finite");
+  g->Hq = L->num_q_heads;
+  g->Hkv = L->num_kv_heads;
+  g->G = g->Hq / g->Hkv;
+  g->d = L->head_dim;
+  g->dtype = L->dtype;
+  g->max_len = L->max_len;
+  g->ps = L->page_size;
+  g->paged = L->page_size > 0;
+  g->ps_log2 = g->paged ? log2i(L->page_size) : 0;
+  g->pt_stride = L->page_table_stride;
+  g->scale = L->scale > 0.f ? L->scale : 1.0f / std::sqrt((float)L->head_dim);
+  // heads per slice: the largest divisor of G that is <= 8 and keeps the
+  // scoring work-group's logit tile (Hkv * GS rows) within kMaxHeadsPerWG
+  g->GS = 1;
+  for (int s = 8; s >= 1; --s)
+    if (g->G % s == 0 && g->Hkv * s <= kMaxHeadsPerWG) { g->GS = s; break; }
+  g->nslices = g->G / g->GS;
+  // the scoring work-group keeps one KV head per row group
+  const int esz = g->dtype == TS_BF16 ? 2 : 4;
+  const int lpr = g->d * esz / 32;
+  if (g->Hkv > 256 / lpr)
+    return fail(TS_ERR_UNSUPPORTED, "num_kv_heads %d too large for this head_dim/dtype (max %d)",
+                g->Hkv, 256 / lpr);
+  return TS_OK;
+}
+
+// ---- workspace plans -----------------------------------------------------------
+
+struct ScorePlan {
+  int ntiles, Lpad;
+  size_t ctrl, lse, partials, logits;
+};
+void plan_score(const Geo& g, int B, Carve& c, ScorePlan& s) {
+  s.ntiles = cdiv(g.max_len, kScoreTile);
+  s.Lpad = cdiv(g.max_len, kVoteTile) * kVoteTile;
+  s.ctrl = c.take((size_t)B * kCtrlStride * 4);
+  s.lse = c.take((size_t)B * g.Hq * 4);
+  s.partials = c.take((size_t)B * g.Hq * s.ntiles * 8);
+  s.logits = c.take((size_t)B * g.Hq * s.Lpad * 4);
+}
+
+struct AttendPlan {
+  int split, nsplit;
+  size_t pm, pl, pacc;
+};
+void plan_attend(const Geo& g, int B, int k, Carve& c, AttendPlan& a) {
+  // enough work-groups to cover the chip twice, without splits under 16 rows
+  const long cols = (long)B * g.Hkv * g.nslices;
+  int split = 256;
+  while (split > 16 && cols * cdiv(k, split) < 512) split >>= 1;
+  a.split = split;
+  a.nsplit = cdiv(k, split);
+  a.pm = c.take((size_t)B * g.Hq * a.nsplit * 4);
+  a.pl = c.take((size_t)B * g.Hq * a.nsplit * 4);
+  a.pacc = c.take((size_t)B * g.Hq * a.nsplit * g.d * 4);
+}
+
+struct TopkPlan {
+  int max_chunks;
+  size_t ctrl, flags;
+};
+void plan_topk(int rows, int row_stride, Carve& c, TopkPlan& t, bool own_ctrl) {
+  t.max_chunks = cdiv(row_stride, kTopkChunk);
+  if (own_ctrl) t.ctrl = c.take((size_t)rows * kCtrlStride * 4);
+  t.flags = c.take((size_t)rows * t.max_chunks * 8);
+}
+
+struct DecodePlan {
+  ScorePlan s;
+  TopkPlan t;
+  AttendPlan a;
+  size_t votes;
+  size_t total;
+};
+void plan_decode(const Geo& g, int B, int k, DecodePlan& p) {
+  Carve c;
+  plan_score(g, B, c, p.s);
+  plan_topk(B, g.max_len, c, p.t, false);
+  p.t.ctrl = p.s.ctrl;
+  p.votes = c.take((size_t)B * g.max_len * 4);
+  plan_attend(g, B, k, c, p.a);
+  p.total = c.off;
+}
+
+ScoreParams score_params(const Geo& g, const ScorePlan& s, int B, void* ws, const void* q,
+                         const void* kc, const int32_t* pt, const int32_t* lens, const int32_t* hit) {
+  ScoreParams p{};
+  p.q = q;
+  p.k = kc;
+  p.page_table = pt;
+  p.seq_lens = lens;
+  p.hit = hit;
+  p.logits = at<float>(ws, s.logits);
+  p.partials = at<float2>(ws, s.partials);
+  p.lse = at<float>(ws, s.lse);
+  p.ctrl = at<uint32_t>(ws, s.ctrl);
+  p.B = B;
+  p.Hq = g.Hq;
+  p.Hkv = g.Hkv;
+  p.G = g.G;
+  p.GS = g.GS;
+  p.nslices = g.nslices;
+  p.max_len = g.max_len;
+  p.Lpad = s.Lpad;
+  p.ntiles = s.ntiles;
+  p.ps_log2 = g.ps_log2;
+  p.pt_stride = g.pt_stride;
+  p.scale2 = g.scale * kLog2eHost;
+  return p;
+}
+
+VoteParams vote_params(const Geo& g, const ScorePlan& s, int B, void* ws, const int32_t* lens,
+                       const int32_t* hit, float* votes, int vote_stride, int k, int do_hist) {
+  VoteParams v{};
+  v.logits = at<float>(ws, s.logits);
+  v.lse = at<float>(ws, s.lse);
+  v.seq_lens = lens;
+  v.hit = hit;
+  v.votes = votes;
+  v.ctrl = at<uint32_t>(ws, s.ctrl);
+  v.B = B;
+  v.Hq = g.Hq;
+  v.Lpad = s.Lpad;
+  v.vote_stride = vote_stride;
+  v.k = k;
+  v.do_hist = do_hist;
+  return v;
+}
+
+AttendParams attend_params(const Geo& g, const AttendPlan& a, int B, void* ws, const void* q,
+                           const void* kc, const void* vc, const int32_t* pt, const int32_t* lens,
+                           const int32_t* idx, int k) {
+  AttendParams p{};
+  p.q = q;
+  p.k = kc;
+  p.v = vc;
+  p.page_table = pt;
+  p.seq_lens = lens;
+  p.idx = idx;
+  p.pm = at<float>(ws, a.pm);
+  p.pl = at<float>(ws, a.pl);
+  p.pacc = at<float>(ws, a.pacc);
+  p.B = B;
+  p.Hq = g.Hq;
+  p.Hkv = g.Hkv;
+  p.G = g.G;
+  p.GS = g.GS;
+  p.nslices = g.nslices;
+  p.max_len = g.max_len;
+  p.ps_log2 = g.ps_log2;
+  p.pt_stride = g.pt_stride;
+  p.nidx = k;
+  p.nsplit = a.nsplit;
+  p.split = a.split;
+  p.scale2 = g.scale * kLog2eHost;
+  return p;
+}
+
+CombineParams combine_params(const Geo& g, const AttendPlan& a, int B, void* ws, float* out) {
+  CombineParams c{};
+  c.pm = at<float>(ws, a.pm);
+  c.pl = at<float>(ws, a.pl);
+  c.pacc = at<float>(ws, a.pacc);
+  c.out = out;
+  c.B = B;
+  c.Hq = g.Hq;
+  c.d = g.d;
+  c.nsplit = a.nsplit;
+  return c;
+}
+
+ts_status check_ws(const void* ws, size_t have, size_t need) {
+  if (need > 0 && ws == nullptr) return fail(TS_ERR_INVALID_ARG, "workspace is NULL");
+  if (have < need)
+    return fail(TS_ERR_WORKSPACE, "workspace too small: %zu bytes given, %zu needed", have, need);
+  if ((reinterpret_cast<uintptr_t>(ws) & 255u) != 0)
+    return fail(TS_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
+  return TS_OK;
+}
+
+#define TS_TRY(expr)                  \
+  do {                                \
+    ts_status _st = (expr);           \
+    if (_st != TS_OK) return _st;     \
+  } while (0)
+
+#define TS_LAUNCH(expr, what) TS_TRY(hip_check((expr), what))
+
+}  // namespace
+
+extern "C" {
+
+int32_t ts_abi_version(void) { return TS_ABI_VERSION; }
+
+const char* ts_status_string(int32_t st) {
+  switch (st) {
+    case TS_OK: return "TS_OK";
+    case TS_ERR_INVALID_ARG: return "TS_ERR_INVALID_ARG: invalid argument";
+    case TS_ERR_UNSUPPORTED: return "TS_ERR_UNSUPPORTED: shape or dtype not supported";
+    case TS_ERR_WORKSPACE: return "TS_ERR_WORKSPACE: workspace too small";
+    case TS_ERR_HIP: return "TS_ERR_HIP: HIP runtime error";
+    default: return "unknown ts_status";
+  }
+}
+
+const char* ts_last_error(void) { return g_last_error.c_str(); }
+
+// ---------------------------------------------------------------- ts_score
+
+ts_status ts_score_workspace_size(const ts_kv_layout* L, int32_t batch, size_t* bytes) {
+  Geo g;
+  TS_TRY(check_layout(L, batch, &g));
+  if (!bytes) return fail(TS_ERR_INVALID_ARG, "bytes is NULL");
+  Carve c;
+  ScorePlan s;
+  plan_score(g, batch, c, s);
+  *bytes = c.off;
+  return ok();
+}
+
+ts_status ts_score(const ts_kv_layout* L, int32_t batch, const void* q, const void* k_cache,
+                   const int32_t* page_table, const int32_t* seq_lens, float* votes, void* ws,
+                   size_t ws_bytes, void* stream) {
+  Geo g;
+  TS_TRY(check_layout(L, batch, &g));
+  if (!q || !k_cache || !seq_lens || !votes) return fail(TS_ERR_INVALID_ARG, "NULL tensor pointer");
+  if (g.paged && !page_table) return fail(TS_ERR_INVALID_ARG, "paged layout needs a page_table");
+  Carve c;
+  ScorePlan s;
+  plan_score(g, batch, c, s);
+  TS_TRY(check_ws(ws, ws_bytes, c.off));
+  hipStream_t st = static_cast<hipStream_t>(stream);
+
+  PrologueParams pp{};
+  pp.ctrl = at<uint32_t>(ws, s.ctrl);
+  pp.rows = batch;
+  TS_LAUNCH(launch_prologue(pp, batch, st), "prologue");
+  ScoreParams sp = score_params(g, s, batch, ws, q, k_cache, g.paged ? page_table : nullptr,
+                                seq_lens, nullptr);
+  TS_LAUNCH(launch_score_pass1(g.dtype, g.d, g.paged, sp, st), "score pass 1");
+  VoteParams vp = vote_params(g, s, batch, ws, seq_lens, nullptr, votes, g.max_len, 1, 0);
+  TS_LAUNCH(launch_votes(vp, cdiv(g.max_len, kVoteTile), st), "votes");
+  return ok();
+}
+
+// ----------------------------------------------------------------- ts_topk
+
+ts_status ts_topk_workspace_size(int32_t rows, int32_t row_stride, int32_t k, size_t* bytes) {
+  if (rows < 1 || row_stride < 1 || k < 1)
+    return fail(TS_ERR_INVALID_ARG, "rows, row_stride and k must be >= 1");
+  if (!bytes) return fail(TS_ERR_INVALID_ARG, "bytes is NULL");
+  Carve c;
+  TopkPlan t;
+  plan_topk(rows, row_stride, c, t, true);
+  *bytes = c.off;
+  return ok();
+}
+
+static ts_status run_topk(int rows, int row_stride, const float* votes, const int32_t* row_lens,
+                          int row_len_base, int k, int32_t* idx, void* ws, const TopkPlan& t,
+                          int max_row_len, hipStream_t st) {
+  PrologueParams pp{};
+  pp.ctrl = at<uint32_t>(ws, t.ctrl);
+  pp.flags = at<unsigned long long>(ws, t.flags);
+  pp.rows = rows;
+  pp.max_chunks = t.max_chunks;
+  TS_LAUNCH(launch_prologue(pp, rows, st), "prologue");
+  TopkParams tp{};
+  tp.votes = votes;
+  tp.row_lens = row_lens;
+  tp.row_len_base = row_len_base;
+  tp.idx = idx;
+  tp.ctrl = at<uint32_t>(ws, t.ctrl);
+  tp.flags = at<unsigned long long>(ws, t.flags);
+  tp.rows = rows;
+  tp.row_stride = row_stride;
+  tp.k = k;
+  tp.max_chunks = t.max_chunks;
+  const int gx = cdiv(max_row_len, kTopkChunk);
+  TS_LAUNCH(launch_topk_hist(tp, 0, gx, st), "top-k pass 0");
+  TS_LAUNCH(launch_topk_hist(tp, 1, gx, st), "top-k pass 1");
+  TS_LAUNCH(launch_topk_hist(tp, 2, gx, st), "top-k pass 2");
+  TS_LAUNCH(launch_topk_compact(tp, gx, st), "top-k compaction");
+  return TS_OK;
+}
+
+ts_status ts_topk(int32_t rows, int32_t row_stride, const float* votes, const int32_t* row_lens,
+                  int32_t k, int32_t* idx, void* ws, size_t ws_bytes, void* stream) {
+  if (rows < 1 || row_stride < 1 || k < 1)
+    return fail(TS_ERR_INVALID_ARG, "rows, row_stride and k must be >= 1");
+  if (!votes || !row_lens || !idx) return fail(TS_ERR_INVALID_ARG, "NULL tensor pointer");
+  Carve c;
+  TopkPlan t;
+  plan_topk(rows, row_stride, c, t, true);
+  TS_TRY(check_ws(ws, ws_bytes, c.off));
+  TS_TRY(run_topk(rows, row_stride, votes, row_lens, 0, k, idx, ws, t, row_stride,
+                  static_cast<hipStream_t>(stream)));
+  return ok();
+}
+
+// -------------------------------------------------------- ts_sparse_attend
+
+ts_status ts_sparse_attend_workspace_size(const ts_kv_layout* L, int32_t batch, int32_t k,
+                                          size_t* bytes) {
+  Geo g;
+  TS_TRY(check_layout(L, batch, &g));
+  if (k < 1) return fail(TS_ERR_INVALID_ARG, "k must be >= 1");
+  if (!bytes) return fail(TS_ERR_INVALID_ARG, "bytes is NULL");
+  Carve c;
+  AttendPlan a;
+  plan_attend(g, batch, k, c, a);
+  *bytes = c.off;
+  return ok();
+}
+
+ts_status ts_sparse_attend(const ts_kv_layout* L, int32_t batch, const void* q, const void* k_cache,
+                           const void* v_cache, const int32_t* page_table, const int32_t* seq_lens,
+                           const int32_t* idx, int32_t k, float* out, void* ws, size_t ws_bytes,
+                           void* stream) {
+  Geo g;
+  TS_TRY(check_layout(L, batch, &g));
+  if (k < 1) return fail(TS_ERR_INVALID_ARG, "k must be >= 1");
+  if (!q || !k_cache || !v_cache || !seq_lens || !idx || !out)
+    return fail(TS_ERR_INVALID_ARG, "NULL tensor pointer");
+  if (g.paged && !page_table) return fail(TS_ERR_INVALID_ARG, "paged layout needs a page_table");
+  Carve c;
+  AttendPlan a;
+  plan_attend(g, batch, k, c, a);
+  TS_TRY(check_ws(ws, ws_bytes, c.off));
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  AttendParams ap = attend_params(g, a, batch, ws, q, k_cache, v_cache,
+                                  g.paged ? page_table : nullptr, seq_lens, idx, k);
+  TS_LAUNCH(launch_attend(g.dtype, g.d, g.paged, ap, st), "sparse attention");
+  CombineParams cp = combine_params(g, a, batch, ws, out);
+  TS_LAUNCH(launch_combine(cp, st), "combine");
+  return ok();
+}
+
+// ------------------------------------------------------------ Selection Cache
+
+ts_status ts_sel_cache_create(int32_t max_batch, int32_t num_q_heads, int32_t head_dim, int32_t k,
+                              int32_t compare_mode, ts_sel_cache** out) {
+  if (!out) return fail(TS_ERR_INVALID_ARG, "out is NULL");
+  *out = nullptr;
+  if (max_batch < 1 || num_q_heads < 1 || head_dim < 1 || k < 1)
+    return fail(TS_ERR_INVALID_ARG, "max_batch, num_q_heads, head_dim and k must be >= 1");
+  if (compare_mode != 0 && compare_mode != 1)
+    return fail(TS_ERR_INVALID_ARG, "compare_mode must be 0 or 1");
+  ts_sel_cache* c = new ts_sel_cache();
+  std::memset(&c->dev, 0, sizeof(c->dev));
+  c->dev.max_batch = max_batch;
+  c->dev.Hq = num_q_heads;
+  c->dev.d = head_dim;
+  c->dev.k = k;
+  c->dev.mode = compare_mode;
+  hipError_t e = hipGetDevice(&c->device);
+  const size_t n = (size_t)max_batch;
+  void* ptrs[7] = {nullptr};
+  const size_t sizes[7] = {n * num_q_heads * head_dim * 4, n * k * 4, n * 4, n * 4, n * 8, n * 8, n * 8};
+  for (int i = 0; i < 7 && e == hipSuccess; ++i) {
+    e = hipMalloc(&ptrs[i], sizes[i]);
+    if (e == hipSuccess) e = hipMemset(ptrs[i], 0, sizes[i]);
+  }
+  if (e == hipSuccess) e = hipDeviceSynchronize();
+  if (e != hipSuccess) {
+    for (void* p : ptrs)
+      if (p) (void)hipFree(p);
+    delete c;
+    return fail(TS_ERR_HIP, "ts_sel_cache_create: %s", hipGetErrorString(e));
+  }
+  c->dev.prev_q = (float*)ptrs[0];
+  c->dev.sel = (int32_t*)ptrs[1];
+  c->dev.valid = (int32_t*)ptrs[2];
+  c->dev.hit = (int32_t*)ptrs[3];
+  c->dev.cos = (double*)ptrs[4];
+  c->dev.hits = (long long*)ptrs[5];
+  c->dev.misses = (long long*)ptrs[6];
+  *out = c;
+  return ok();
+}
+
+ts_status ts_sel_cache_reset(ts_sel_cache* c, void* stream) {
+  if (!c) return fail(TS_ERR_INVALID_ARG, "cache is NULL");
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const size_t n = (size_t)c->dev.max_batch;
+  TS_LAUNCH(launch_fill_zero(c->dev.valid, n, st), "reset");
+  TS_LAUNCH(launch_fill_zero(c->dev.hits, 2 * n, st), "reset");
+  TS_LAUNCH(launch_fill_zero(c->dev.misses, 2 * n, st), "reset");
+  return ok();
+}
+
+ts_status ts_sel_cache_destroy(ts_sel_cache* c) {
+  if (!c) return ok();
+  hipError_t e = hipDeviceSynchronize();
+  void* ptrs[7] = {c->dev.prev_q, c->dev.sel, c->dev.valid, c->dev.hit, c->dev.cos, c->dev.hits,
+                   c->dev.misses};
+  for (void* p : ptrs) {
+    hipError_t f = hipFree(p);
+    if (e == hipSuccess) e = f;
+  }
+  delete c;
+  if (e != hipSuccess) return fail(TS_ERR_HIP, "ts_sel_cache_destroy: %s", hipGetErrorString(e));
+  return ok();
+}
+
+ts_status ts_sel_cache_stats(ts_sel_cache* c, int32_t n, int64_t* hits, int64_t* misses,
+                             void* stream) {
+  if (!c || !hits || !misses) return fail(TS_ERR_INVALID_ARG, "NULL argument");
+  if (n < 0 || n > c->dev.max_batch) return fail(TS_ERR_INVALID_ARG, "n out of range");
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  TS_LAUNCH(hipMemcpyAsync(hits, c->dev.hits, (size_t)n * 8, hipMemcpyDeviceToHost, st), "stats");
+  TS_LAUNCH(hipMemcpyAsync(misses, c->dev.misses, (size_t)n * 8, hipMemcpyDeviceToHost, st), "stats");
+  TS_LAUNCH(hipStreamSynchronize(st), "stats");
+  return ok();
+}
+
+// ------------------------------------------------------------ ts_decode_step
+
+ts_status ts_decode_step_workspace_size(const ts_kv_layout* L, int32_t batch, int32_t k,
+                                        size_t* bytes) {
+  Geo g;
+  TS_TRY(check_layout(L, batch, &g));
+  if (k < 1) return fail(TS_ERR_INVALID_ARG, "k must be >= 1");
+  if (!bytes) return fail(TS_ERR_INVALID_ARG, "bytes is NULL");
+  DecodePlan p;
+  plan_decode(g, batch, k, p);
+  *bytes = p.total;
+  return ok();
+}
+
+ts_status ts_decode_step(ts_sel_cache* cache, const ts_kv_layout* L, int32_t batch, const void* q,
+                         const void* k_cache, const void* v_cache, const int32_t* page_table,
+                         const int32_t* seq_lens, double theta, float* out, int32_t* idx_out,
+                         int32_t* hit_out, void* ws, size_t ws_bytes, void* stream) {
+  if (!cache) return fail(TS_ERR_INVALID_ARG, "cache is NULL");
+  Geo g;
+  TS_TRY(check_layout(L, batch, &g));
+  if (batch > cache->dev.max_batch)
+    return fail(TS_ERR_INVALID_ARG, "batch %d > cache max_batch %d", batch, cache->dev.max_batch);
+  if (g.Hq != cache->dev.Hq || g.d != cache->dev.d)
+    return fail(TS_ERR_INVALID_ARG, "layout heads/head_dim differ from the cache's");
+  if (std::isnan(theta)) return fail(TS_ERR_INVALID_ARG, "theta is NaN");
+  if (!q || !k_cache || !v_cache || !seq_lens || !out)
+    return fail(TS_ERR_INVALID_ARG, "NULL tensor pointer");
+  if (g.paged && !page_table) return fail(TS_ERR_INVALID_ARG, "paged layout needs a page_table");
+  const int k = cache->dev.k;
+  DecodePlan p;
+  plan_decode(g, batch, k, p);
+  TS_TRY(check_ws(ws, ws_bytes, p.total));
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const int32_t* pt = g.paged ? page_table : nullptr;
+
+  // 1. reset control blocks; Selection-Cache decision per sequence
+  PrologueParams pp{};
+  pp.ctrl = at<uint32_t>(ws, p.s.ctrl);
+  pp.flags = at<unsigned long long>(ws, p.t.flags);
+  pp.rows = batch;
+  pp.max_chunks = p.t.max_chunks;
+  pp.cache = cache->dev;
+  pp.q = q;
+  pp.dtype = g.dtype;
+  pp.seq_lens = seq_lens;
+  pp.B = batch;
+  pp.theta = theta;
+  TS_LAUNCH(launch_prologue(pp, batch, st), "prologue");
+  const int32_t* hit = cache->dev.hit;
+
+  // 2. K-scan (misses only)
+  ScoreParams sp = score_params(g, p.s, batch, ws, q, k_cache, pt, seq_lens, hit);
+  TS_LAUNCH(launch_score_pass1(g.dtype, g.d, g.paged, sp, st), "score pass 1");
+  // 3. votes + first radix histogram
+  float* votes = at<float>(ws, p.votes);
+  VoteParams vp = vote_params(g, p.s, batch, ws, seq_lens, hit, votes, g.max_len, k, 1);
+  TS_LAUNCH(launch_votes(vp, cdiv(g.max_len, kVoteTile), st), "votes");
+  // 4. top-k into the cache's stored selection
+  TopkParams tp{};
+  tp.votes = votes;
+  tp.row_lens = seq_lens;
+  tp.hit = hit;
+  tp.idx = cache->dev.sel;
+  tp.ctrl = at<uint32_t>(ws, p.s.ctrl);
+  tp.flags = at<unsigned long long>(ws, p.t.flags);
+  tp.rows = batch;
+  tp.row_stride = g.max_len;
+  tp.k = k;
+  tp.max_chunks = p.t.max_chunks;
+  const int gx = cdiv(g.max_len, kTopkChunk);
+  TS_LAUNCH(launch_topk_hist(tp, 1, gx, st), "top-k pass 1");
+  TS_LAUNCH(launch_topk_hist(tp, 2, gx, st), "top-k pass 2");
+  TS_LAUNCH(launch_topk_compact(tp, gx, st), "top-k compaction");
+  // 5. sparse attention over the current selection; 6. combine + state update
+  AttendParams ap = attend_params(g, p.a, batch, ws, q, k_cache, v_cache, pt, seq_lens,
+                                  cache->dev.sel, k);
+  TS_LAUNCH(launch_attend(g.dtype, g.d, g.paged, ap, st), "sparse attention");
+  CombineParams cp = combine_params(g, p.a, batch, ws, out);
+  cp.cache = cache->dev;
+  cp.q = q;
+  cp.dtype = g.dtype;
+  cp.seq_lens = seq_lens;
+  cp.idx_out = idx_out;
+  cp.hit_out = hit_out;
+  TS_LAUNCH(launch_combine(cp, st), "combine");
+  return ok();
+}
+
+// ------------------------------------------------------------ prefill
+
+ts_status ts_score_prefill_workspace_size(const ts_kv_layout* L, int32_t chunk, int32_t n_ctx,
+                                          int32_t k, size_t* bytes) {
+  (void)L; (void)chunk; (void)n_ctx; (void)k; (void)bytes;
+  return fail(TS_ERR_UNSUPPORTED, "prefill scoring not built yet");
+}
+
+ts_status ts_score_prefill(const ts_kv_layout* L, int32_t chunk, int32_t q_pos0, const void* q,
+                           const void* k_cache, int32_t n_ctx, float* votes, void* ws,
+                           size_t ws_bytes, void* stream) {
+  (void)L; (void)chunk; (void)q_pos0; (void)q; (void)k_cache; (void)n_ctx; (void)votes;
+  (void)ws; (void)ws_bytes; (void)stream;
+  return fail(TS_ERR_UNSUPPORTED, "prefill scoring not built yet");
+}
+
+ts_status ts_select_prefill(const ts_kv_layout* L, int32_t chunk, int32_t q_pos0, const void* q,
+                            const void* k_cache, int32_t n_ctx, int32_t k, float* votes,
+                            int32_t* idx, void* ws, size_t ws_bytes, void* stream) {
+  (void)L; (void)chunk; (void)q_pos0; (void)q; (void)k_cache; (void)n_ctx; (void)k; (void)votes;
+  (void)idx; (void)ws; (void)ws_bytes; (void)stream;
+  return fail(TS_ERR_UNSUPPORTED, "prefill scoring not built yet");
+}
+
+}  // extern "C"

@@ -1,0 +1,153 @@
+// ts_internal.h — kernel parameter blocks, workspace plan and launcher
+// declarations shared by the C-ABI layer (ts_api.cpp) and the HIP sources.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace ts {
+
+// ---- tiling constants -------------------------------------------------------
+constexpr int kScoreTile = 256;    // tokens per scoring work-group (pass 1)
+constexpr int kVoteTile = 1024;    // tokens per vote work-group (pass 2)
+constexpr int kTopkChunk = 4096;   // elements per top-k work-group
+constexpr int kMaxHeadsPerWG = 64; // Hkv * heads-per-slice held by one scoring WG
+constexpr int kMaxQHeads = 256;
+constexpr float kLog2eHost = 1.4426950408889634f;
+
+// ---- per-row control block (uint32 words) ----------------------------------
+// Zeroed by the prologue kernel at the start of every call that uses it.
+enum CtrlWord : int {
+  kCtlCntScore = 0,   // scoring work-groups finished (per sequence)
+  kCtlCntVote = 1,    // vote work-groups finished
+  kCtlCntHist1 = 2,   // top-k pass-1 work-groups finished
+  kCtlCntHist2 = 3,   // top-k pass-2 work-groups finished
+  kCtlTicket = 4,     // compaction ticket
+  kCtlPrefix = 5,     // key bits fixed so far (after pass 2: the full threshold key)
+  kCtlNeed = 6,       // elements still to take among those matching the prefix
+  kCtlErr = 7,        // non-zero if a bounded wait gave up
+  kCtlHist0 = 16,     // 2048 bins: key bits 31..21
+  kCtlHist1 = 16 + 2048,  // 2048 bins: key bits 20..10
+  kCtlHist2 = 16 + 4096,  // 1024 bins: key bits 9..0
+  kCtlWords = 16 + 4096 + 1024,
+};
+constexpr int kCtrlStride = ((kCtlWords + 63) / 64) * 64;   // 256-byte rows
+
+inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+inline int cdiv(long a, long b) { return (int)((a + b - 1) / b); }
+
+// ---- Selection-Cache device state -------------------------------------------
+struct SelCacheDev {
+  float* prev_q;      // [max_batch][Hq*d] stored query (fp32)
+  int32_t* sel;       // [max_batch][k] stored selection
+  int32_t* valid;     // [max_batch]
+  int32_t* hit;       // [max_batch] decision of the current step
+  double* cos;        // [max_batch] cosine of the current step (NaN if not computed)
+  long long* hits;    // [max_batch] counters
+  long long* misses;  // [max_batch]
+  int max_batch, Hq, d, k, mode;
+};
+
+// ---- kernel parameter blocks -------------------------------------------------
+struct PrologueParams {
+  uint32_t* ctrl;       // [rows][kCtrlStride] or null
+  unsigned long long* flags;  // [rows][max_chunks] or null
+  int rows, max_chunks;
+  // selection-cache check (cache.prev_q == null: none)
+  SelCacheDev cache;
+  const void* q;        // [B][Hq][d]
+  int dtype;            // 0 f32, 1 bf16
+  const int32_t* seq_lens;
+  int B;
+  double theta;
+};
+
+struct ScoreParams {
+  const void* q;            // [B][Hq][d]
+  const void* k;            // contiguous [B][max_len][Hkv][d] or pool [P][ps][Hkv][d]
+  const int32_t* page_table;
+  const int32_t* seq_lens;
+  const int32_t* hit;       // [B] or null: sequences with hit != 0 are skipped
+  float* logits;            // [B][Hq][Lpad] base-2 logits (scale * log2 e * q.k)
+  float2* partials;         // [B][Hq][ntiles] (tile max, tile sum of exp2)
+  float* lse;               // [B][Hq] base-2 log-sum-exp over all tokens
+  uint32_t* ctrl;           // [B][kCtrlStride]
+  int B, Hq, Hkv, G, GS, nslices, max_len, Lpad, ntiles, ps_log2, pt_stride;
+  float scale2;
+};
+
+struct VoteParams {
+  const float* logits;
+  const float* lse;
+  const int32_t* seq_lens;
+  const int32_t* hit;
+  float* votes;             // [B][vote_stride]
+  uint32_t* ctrl;
+  int B, Hq, Lpad, vote_stride, k;
+  int do_hist;              // 1: build the first top-k histogram and resolve it
+};
+
+struct TopkParams {
+  const float* votes;       // [rows][row_stride]
+  const int32_t* row_lens;  // [rows] (null: q_pos0 + r + 1, the causal prefill rows)
+  int row_len_base;         // used when row_lens is null
+  const int32_t* hit;       // [rows] or null
+  int32_t* idx;             // [rows][k]
+  int32_t* idx2;            // optional second copy of the result (or null)
+  uint32_t* ctrl;
+  unsigned long long* flags;  // [rows][max_chunks]
+  int rows, row_stride, k, max_chunks;
+};
+
+struct AttendParams {
+  const void* q;
+  const void* k;
+  const void* v;
+  const int32_t* page_table;
+  const int32_t* seq_lens;
+  const int32_t* idx;       // [B][nidx]
+  float* pm;                // [B][Hq][nsplit] running max (base 2)
+  float* pl;                // [B][Hq][nsplit] sum of exp2
+  float* pacc;              // [B][Hq][nsplit][d] weighted value sums
+  int B, Hq, Hkv, G, GS, nslices, max_len, ps_log2, pt_stride, nidx, nsplit, split;
+  float scale2;
+};
+
+struct CombineParams {
+  const float* pm;
+  const float* pl;
+  const float* pacc;
+  float* out;               // [B][Hq][d]
+  int B, Hq, d, nsplit;
+  // optional state update of a decode step (cache.prev_q == null: none)
+  SelCacheDev cache;
+  const void* q;
+  int dtype;
+  const int32_t* seq_lens;
+  int32_t* idx_out;         // [B][k] or null
+  int32_t* hit_out;         // [B] or null
+};
+
+struct PrefillParams {
+  const void* q;            // [chunk][Hq][d] bf16
+  const void* k;            // [n_ctx][Hkv][d] bf16
+  float* lse;               // [chunk][Hq] base-2 log-sum-exp per query and head
+  float* votes;             // [chunk][n_ctx]
+  int chunk, q_pos0, n_ctx, Hq, Hkv, G;
+  float scale2;
+};
+
+// ---- launchers (defined in the .hip sources) --------------------------------
+hipError_t launch_prologue(const PrologueParams& p, int grid, hipStream_t s);
+hipError_t launch_fill_zero(void* ptr, size_t words, hipStream_t s);   // 32-bit words
+hipError_t launch_score_pass1(int dtype, int d, bool paged, const ScoreParams& p, hipStream_t s);
+hipError_t launch_votes(const VoteParams& p, int grid_x, hipStream_t s);
+hipError_t launch_topk_hist(const TopkParams& p, int pass, int grid_x, hipStream_t s);
+hipError_t launch_topk_compact(const TopkParams& p, int grid_x, hipStream_t s);
+hipError_t launch_attend(int dtype, int d, bool paged, const AttendParams& p, hipStream_t s);
+hipError_t launch_combine(const CombineParams& p, hipStream_t s);
+hipError_t launch_prefill_lse(const PrefillParams& p, hipStream_t s);
+hipError_t launch_prefill_votes(const PrefillParams& p, hipStream_t s);
+
+}  // namespace ts

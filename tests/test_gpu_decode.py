@@ -1,0 +1,318 @@
+"""GPU parity of the decode path (scoring, votes, top-k, sparse attention,
+Selection Cache, decode step) against the fp64 oracle, through the C ABI."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import workloads as W
+from oracle import ts_oracle as O
+from tests.parity import check_attention, check_selection, np32, np64
+
+pytestmark = pytest.mark.gpu
+
+# vote tolerance, derived in the design doc: fp32 logits carry an absolute error of
+# at most a few 1e-5 (base e) for logits of O(50); a vote is a sum of
+# exp(s - lse) terms, so its relative error is bounded by about twice that.
+VOTE_RTOL = 2e-4
+VOTE_ATOL_REL_MAX = 1e-7
+
+
+def _tol(dtype):
+    return 1e-5 if dtype == torch.float32 else 1e-2
+
+
+def _small_cfg(name, B, Hq, Hkv, d, N, dtype, k, seed, heavy=0.01, planted=0, max_len=None):
+    return W.DecodeConfig(name, batch=B, num_q_heads=Hq, num_kv_heads=Hkv, head_dim=d, seq_len=N,
+                          dtype=dtype, k=k, seed=seed, heavy_frac=heavy, planted=planted,
+                          max_len=max_len)
+
+
+SMALL = [
+    _small_cfg("g2-d64-f32", 1, 4, 2, 64, 4096, "f32", 256, 0, heavy=0, planted=16),
+    _small_cfg("g1-d128-bf16", 2, 4, 4, 128, 3001, "bf16", 100, 11),
+    _small_cfg("g7-d128-bf16", 1, 28, 4, 128, 5000, "bf16", 300, 12),
+    _small_cfg("g4-d64-bf16", 2, 32, 8, 64, 2777, "bf16", 512, 13, max_len=3000),
+    _small_cfg("g8-d128-f32", 1, 16, 2, 128, 1500, "f32", 64, 14),
+    _small_cfg("g2-d128-bf16-ragged", 3, 4, 2, 128, 257, "bf16", 300, 15, heavy=0.05),
+    _small_cfg("g16-d64-bf16", 1, 16, 1, 64, 999, "bf16", 77, 16),   # G > 8: two head slices
+]
+
+
+def _oracle_votes(q64, K32, n):
+    return O.soft_vote(O.head_softmax(O.logits(q64, K32[:n])))
+
+
+def _varlen(x, lens):
+    x["seq_lens"] = torch.tensor(lens, dtype=torch.int32, device=x["q"].device)
+    return x
+
+
+def _to_paged(K, V, lens, ps, seed):
+    """Scatter contiguous [B][max_len][Hkv][d] caches into a shuffled page pool."""
+    B, max_len, Hkv, d = K.shape
+    g = torch.Generator(device="cpu").manual_seed(seed)
+    pages = [(n + ps - 1) // ps for n in lens]
+    total = sum(pages)
+    perm = torch.randperm(total, generator=g).to(torch.int32)
+    stride = (max_len + ps - 1) // ps
+    pt = torch.full((B, stride), -1, dtype=torch.int32)
+    kp = torch.zeros(total, ps, Hkv, d, dtype=K.dtype, device=K.device)
+    vp = torch.zeros_like(kp)
+    off = 0
+    for b in range(B):
+        pt[b, :pages[b]] = perm[off:off + pages[b]]
+        off += pages[b]
+        for p in range(pages[b]):
+            n = min(ps, lens[b] - p * ps)
+            kp[pt[b, p].item(), :n] = K[b, p * ps:p * ps + n]
+            vp[pt[b, p].item(), :n] = V[b, p * ps:p * ps + n]
+    return kp, vp, pt.to(K.device)
+
+
+@pytest.mark.parametrize("cfg", SMALL, ids=lambda c: c.name)
+def test_score_votes(gpu_lib, cfg):
+    ts = gpu_lib
+    x = W.gen_decode(cfg, device="cuda")
+    lens = [cfg.seq_len - 37 * b for b in range(cfg.batch)]
+    _varlen(x, lens)
+    votes = ts.score(x["q"], x["k_cache"], x["seq_lens"])
+    torch.cuda.synchronize()
+    q64, K32 = np64(x["q"]), np32(x["k_cache"])
+    for b, n in enumerate(lens):
+        v = np64(votes[b, :n])
+        ref = _oracle_votes(q64[b], K32[b], n)
+        assert abs(v.sum() - cfg.num_q_heads) < 1e-4 * cfg.num_q_heads
+        err = np.abs(v - ref)
+        bound = VOTE_RTOL * ref + VOTE_ATOL_REL_MAX * ref.max()
+        assert (err <= bound).all(), f"max rel err {(err / np.maximum(ref, 1e-30)).max():.3e}"
+
+
+def test_score_votes_paged_matches_contiguous(gpu_lib):
+    ts = gpu_lib
+    cfg = _small_cfg("pg", 3, 16, 4, 128, 2000, "bf16", 128, 21, max_len=2048)
+    x = W.gen_decode(cfg, device="cuda")
+    lens = [2000, 700, 1]
+    _varlen(x, lens)
+    v_cont = ts.score(x["q"], x["k_cache"], x["seq_lens"])
+    kp, vp, pt = _to_paged(x["k_cache"], x["v_cache"], lens, 16, 5)
+    v_pag = ts.score(x["q"], kp, x["seq_lens"], page_table=pt)
+    torch.cuda.synchronize()
+    for b, n in enumerate(lens):
+        # same kernels, same arithmetic order: bit-identical
+        assert torch.equal(v_cont[b, :n], v_pag[b, :n])
+
+
+def _topk_rows(seed):
+    g = torch.Generator(device="cpu").manual_seed(seed)
+    lens = [0, 1, 5, 255, 4095, 4096, 4097, 10000, 70001]
+    stride = 70010
+    rows = []
+    for i, n in enumerate(lens):
+        kind = i % 4
+        if kind == 0:
+            r = torch.rand(stride, generator=g)
+        elif kind == 1:
+            r = torch.randint(0, 4, (stride,), generator=g).float()        # heavy ties
+        elif kind == 2:
+            r = torch.randn(stride, generator=g)                             # negatives
+            r[::7] = -0.0
+            r[1::7] = 0.0
+        else:
+            r = torch.exp(torch.randn(stride, generator=g) * 8)              # wide range
+        rows.append(r)
+    return torch.stack(rows), lens
+
+
+@pytest.mark.parametrize("k", [1, 7, 256, 4096, 5000])
+def test_topk_exact(gpu_lib, k):
+    ts = gpu_lib
+    votes, lens = _topk_rows(k)
+    vd = votes.cuda()
+    ld = torch.tensor(lens, dtype=torch.int32, device="cuda")
+    idx = ts.topk(vd, ld, k)
+    torch.cuda.synchronize()
+    got = idx.cpu().numpy()
+    v = votes.numpy().astype(np.float64)
+    for r, n in enumerate(lens):
+        want = O.top_k(v[r, :n], k)
+        assert np.array_equal(got[r], want), f"row {r} (len {n})"
+
+
+def test_topk_repeat_is_deterministic(gpu_lib):
+    ts = gpu_lib
+    votes, lens = _topk_rows(3)
+    vd = votes.cuda()
+    ld = torch.tensor(lens, dtype=torch.int32, device="cuda")
+    a = ts.topk(vd, ld, 300).clone()
+    b = ts.topk(vd, ld, 300)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
+
+
+ATT = [
+    ("f32-d64-g2", 2, 4, 2, 64, torch.float32, 3000, 256),
+    ("f32-d128-g8", 1, 16, 2, 128, torch.float32, 1000, 100),
+    ("bf16-d128-g7", 2, 28, 4, 128, torch.bfloat16, 5000, 2048),
+    ("bf16-d64-g4", 3, 32, 8, 64, torch.bfloat16, 777, 300),
+    ("bf16-d128-g16", 1, 16, 1, 128, torch.bfloat16, 600, 40),
+]
+
+
+@pytest.mark.parametrize("case", ATT, ids=lambda c: c[0])
+@pytest.mark.parametrize("paged", [False, True])
+def test_sparse_attend(gpu_lib, case, paged):
+    ts = gpu_lib
+    name, B, Hq, Hkv, d, dt, N, k = case
+    g = torch.Generator(device="cpu").manual_seed(sum(map(ord, name)))
+    q = torch.randn(B, Hq, d, generator=g).to(dt)
+    K = torch.randn(B, N, Hkv, d, generator=g).to(dt)
+    V = torch.randn(B, N, Hkv, d, generator=g).to(dt)
+    lens = [N - 13 * b for b in range(B)]
+    idx = torch.full((B, k), -1, dtype=torch.int32)
+    for b in range(B):
+        m = min(k, lens[b]) - b        # a few -1 slots in later rows
+        sel = torch.randperm(lens[b], generator=g)[:m]
+        idx[b, :m] = torch.sort(sel).values.int()
+    qd, Kd, Vd = q.cuda(), K.cuda(), V.cuda()
+    ld = torch.tensor(lens, dtype=torch.int32, device="cuda")
+    if paged:
+        Kd, Vd, pt = _to_paged(Kd, Vd, lens, 16, 7)
+        out = ts.sparse_attend(qd, Kd, Vd, ld, idx.cuda(), page_table=pt)
+    else:
+        out = ts.sparse_attend(qd, Kd, Vd, ld, idx.cuda())
+    torch.cuda.synchronize()
+    o = np64(out)
+    q64, K64, V64 = np64(q), np64(K), np64(V)
+    ref = np.stack([O.sparse_attention(q64[b], K64[b, :lens[b]], V64[b, :lens[b]], idx[b].numpy())
+                    for b in range(B)])
+    check_attention(o, ref, _tol(dt))
+    check_attention(o, ref, 2e-5)     # the kernel is far inside the stated bound
+
+
+@pytest.mark.parametrize("cfg", SMALL, ids=lambda c: c.name)
+def test_decode_step_miss(gpu_lib, cfg):
+    ts = gpu_lib
+    x = W.gen_decode(cfg, device="cuda")
+    lens = [cfg.seq_len - 37 * b for b in range(cfg.batch)]
+    _varlen(x, lens)
+    cache = ts.SelCache(cfg.batch, cfg.num_q_heads, cfg.head_dim, cfg.k)
+    out, idx, hit = cache.decode_step(x["q"], x["k_cache"], x["v_cache"], x["seq_lens"], 0.9)
+    torch.cuda.synchronize()
+    assert hit.cpu().tolist() == [0] * cfg.batch
+    q64, K32, V32 = np64(x["q"]), np32(x["k_cache"]), np32(x["v_cache"])
+    o = np64(out)
+    gidx = idx.cpu().numpy()
+    for b, n in enumerate(lens):
+        v_ref = _oracle_votes(q64[b], K32[b], n)
+        check_selection(gidx[b], v_ref, cfg.k)
+        ref = O.sparse_attention(q64[b], K32[b, :n], V32[b, :n], gidx[b])
+        check_attention(o[b], ref, _tol(x["q"].dtype))
+        sp = x["special"][b].cpu().numpy()
+        sp = sp[sp < n]
+        if cfg.planted or cfg.heavy_frac:
+            if len(sp) <= cfg.k:
+                assert set(sp.tolist()) <= set(gidx[b].tolist())
+    hits, misses = cache.stats(cfg.batch)
+    assert hits == [0] * cfg.batch and misses == [1] * cfg.batch
+    cache.close()
+
+
+def test_decode_step_edge_cases(gpu_lib):
+    """Empty sequence, k > N, and a one-token sequence in one batch."""
+    ts = gpu_lib
+    cfg = _small_cfg("edge", 3, 8, 2, 64, 50, "bf16", 64, 31, heavy=0)
+    x = W.gen_decode(cfg, device="cuda")
+    lens = [0, 50, 1]
+    _varlen(x, lens)
+    cache = ts.SelCache(3, 8, 64, 64)
+    for step in range(2):
+        out, idx, hit = cache.decode_step(x["q"], x["k_cache"], x["v_cache"], x["seq_lens"], 0.5)
+        torch.cuda.synchronize()
+        gidx = idx.cpu().numpy()
+        assert (gidx[0] == -1).all() and (np32(out)[0] == 0).all()
+        assert list(gidx[1][:50]) == list(range(50)) and (gidx[1][50:] == -1).all()
+        assert gidx[2][0] == 0 and (gidx[2][1:] == -1).all()
+        # step 0: all miss; step 1: same query -> hit, except the empty sequence
+        assert hit.cpu().tolist() == ([0, 0, 0] if step == 0 else [0, 1, 1])
+        q64, K32, V32 = np64(x["q"]), np32(x["k_cache"]), np32(x["v_cache"])
+        for b in (1, 2):
+            ref = O.sparse_attention(q64[b], K32[b, :lens[b]], V32[b, :lens[b]], gidx[b])
+            check_attention(np64(out)[b], ref, 1e-2)
+
+
+def _run_case(ts, rc, mode, theta):
+    x = W.gen_run(rc, device="cuda")
+    lens = x["seq_lens"].tolist()
+    B = rc.batch
+    cache = ts.SelCache(B, rc.num_q_heads, rc.head_dim, rc.k, mode=mode)
+    pool_k, pool_v, pt = x["k_pool"], x["v_pool"], x["page_table"]
+    hits, sels, outs = [], [], []
+    for t in range(rc.steps):
+        out, idx, hit = cache.decode_step(x["queries"][t], pool_k, pool_v, x["seq_lens"], theta,
+                                          page_table=pt)
+        hits.append(hit.clone())
+        sels.append(idx.clone())
+        outs.append(out.clone())
+    torch.cuda.synchronize()
+    hits = torch.stack(hits).cpu().numpy()
+    sels = torch.stack(sels).cpu().numpy()
+    outs = torch.stack(outs).cpu().numpy().astype(np.float64)
+    kp, vp, ptn = np32(pool_k), np32(pool_v), pt.cpu().numpy()
+    Q = np64(x["queries"])
+    for b in range(B):
+        Kb = O.paged_to_contiguous(kp, ptn[b], lens[b])
+        Vb = O.paged_to_contiguous(vp, ptn[b], lens[b])
+        ref_cache = O.SelectionCache(mode)
+        for t in range(rc.steps):
+            hit_ref, c = ref_cache.decide(Q[t, b], theta)
+            if abs(c - theta) > 1e-9 or math.isnan(c):
+                assert bool(hits[t, b]) == hit_ref, f"seq {b} step {t}: cos {c}"
+            if not hits[t, b]:
+                v_ref = _oracle_votes(Q[t, b], Kb, lens[b])
+                check_selection(sels[t, b], v_ref, rc.k)
+            else:
+                assert np.array_equal(sels[t, b], sels[t - 1, b])
+            ref = O.sparse_attention(Q[t, b], Kb, Vb, sels[t, b])
+            check_attention(outs[t, b], ref, 1e-2)
+            # advance the oracle state with the GPU's decision and selection
+            if mode == 0 or not hits[t, b]:
+                ref_cache.prev_q = Q[t, b].copy()
+            ref_cache.prev_S = sels[t, b]
+            ref_cache.valid = True
+    h, m = cache.stats(B)
+    assert h == hits.sum(axis=0).tolist() and m == (rc.steps - hits.sum(axis=0)).tolist()
+    cache.close()
+    return hits
+
+
+def test_selcache_run_mode0(gpu_lib):
+    rc = W.RunConfig("small-run", steps=70, batch=3, num_q_heads=8, num_kv_heads=2, head_dim=64,
+                     min_len=300, max_len=3000, dtype="bf16", k=64, seed=41)
+    hits = _run_case(gpu_lib, rc, 0, 0.9)
+    # drift (cos ~0.95) hits, the jumps at t % 32 == 0 miss
+    for t in range(rc.steps):
+        assert (hits[t] == (0 if t % 32 == 0 else 1)).all()
+
+
+def test_selcache_run_mode1(gpu_lib):
+    rc = W.RunConfig("small-run-anchor", steps=40, batch=2, num_q_heads=8, num_kv_heads=2,
+                     head_dim=128, min_len=500, max_len=2000, dtype="bf16", k=100, seed=42)
+    hits = _run_case(gpu_lib, rc, 1, 0.9)
+    assert 0 < hits.sum() < hits.size
+
+
+def test_selcache_reset(gpu_lib):
+    ts = gpu_lib
+    cfg = _small_cfg("reset", 2, 8, 2, 64, 300, "bf16", 32, 51, heavy=0)
+    x = W.gen_decode(cfg, device="cuda")
+    cache = ts.SelCache(2, 8, 64, 32)
+    args = (x["q"], x["k_cache"], x["v_cache"], x["seq_lens"], 0.5)
+    _, _, h0 = cache.decode_step(*args)
+    _, _, h1 = cache.decode_step(*args)
+    cache.reset()
+    _, _, h2 = cache.decode_step(*args)
+    torch.cuda.synchronize()
+    assert h0.tolist() == [0, 0] and h1.tolist() == [1, 1] and h2.tolist() == [0, 0]
+    assert cache.stats(2) == ([0, 0], [1, 1])
