@@ -1,0 +1,215 @@
+#!/usr/bin/env python3
+"""Decode-step throughput of the TokenSelect hot path on one MI355X.
+
+Workload (default): one decode step of one layer at the Qwen2-7B attention
+shape (28 query / 4 KV heads, head_dim 128, bf16 KV) over N = 131072 cached
+tokens, batch 1, top-k 2048, 1% heavy keys. theta = 1.0 forces a full
+selection on every step (cos <= 1 never exceeds it), so each step runs the
+whole path: Selection-Cache check, K-scan scoring, soft vote, radix top-k,
+sparse attention over the gathered rows, combine and state update.
+
+Inputs are resident in HBM before timing starts. The step rotates over
+`--kv-copies` identical copies of K/V so the 256 MB Infinity Cache cannot
+serve the 134 MB K-scan from the previous step.
+
+One JSON line on stdout:
+  value          decode steps/s (miss steps; wall clock between synchronizes)
+  roofline       the K-scan kernel's algorithmic bytes / its average duration,
+                 measured with HIP events around each of its launches on its
+                 own stream (ts_profile_*), against MI355X's 8 TB/s
+  cpu_baseline   the fp64 oracle timed on this host's cores on a bounded
+                 sample of the same workload
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+HBM_PEAK_GBPS = 8000.0
+
+
+def _die_multi_gpu(n):
+    print(f"bench.py measures one GPU; --gpus {n} is not supported (this path has no "
+          f"multi-GPU mode; see DESIGN.md for how it would shard)", file=sys.stderr)
+    sys.exit(2)
+
+
+def kv_bytes_per_token(cfg) -> int:
+    return cfg.num_kv_heads * cfg.head_dim * (2 if cfg.dtype == "bf16" else 4)
+
+
+def measure_decode(ts, W, cfg, steps, warmup, copies, theta, profile, tag):
+    """Times `steps` decode steps; returns a dict of figures."""
+    import torch
+
+    x = W.gen_decode(cfg, device="cuda")
+    Ks = [x["k_cache"]] + [x["k_cache"].clone() for _ in range(copies - 1)]
+    Vs = [x["v_cache"]] + [x["v_cache"].clone() for _ in range(copies - 1)]
+    q, lens = x["q"], x["seq_lens"]
+    B, Hq, d, k = cfg.batch, cfg.num_q_heads, cfg.head_dim, cfg.k
+    cache = ts.SelCache(B, Hq, d, k)
+    out = torch.empty(B, Hq, d, dtype=torch.float32, device="cuda")
+    idx = torch.empty(B, k, dtype=torch.int32, device="cuda")
+    hit = torch.empty(B, dtype=torch.int32, device="cuda")
+
+    def step(i):
+        c = i % copies
+        cache.decode_step(q, Ks[c], Vs[c], lens, theta, out=out, idx_out=idx, hit_out=hit)
+
+    for i in range(warmup):
+        step(i)
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record()
+    for i in range(steps):
+        step(i)
+    e1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    gpu_ms = e0.elapsed_time(e1)
+    hits = int(hit.sum().item())
+
+    res = {"tag": tag, "wall_s": wall, "ms_per_step": 1e3 * wall / steps,
+           "gpu_ms_per_step": gpu_ms / steps, "steps_per_s": steps / wall,
+           "last_step_hits": hits}
+    if profile:
+        ts.profile_reset()
+        ts.profile_enable(True)
+        t1 = time.perf_counter()
+        for i in range(steps):
+            step(i)
+        torch.cuda.synchronize()
+        res["profiled_ms_per_step"] = 1e3 * (time.perf_counter() - t1) / steps
+        ts.profile_enable(False)
+        kern = ts.profile_read()
+        res["kernels_us"] = {n: 1e3 * ms / c for n, (c, ms) in kern.items() if c}
+        res["kernel_launches_per_step"] = {n: c / steps for n, (c, ms) in kern.items() if c}
+    cache.close()
+    del Ks, Vs
+    torch.cuda.empty_cache()
+    return res, x
+
+
+def cpu_baseline(O, W, cfg, x, seconds):
+    """The fp64 oracle (as written, untuned) on host copies of the same inputs."""
+    import numpy as np
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()
+                       if p.get("user_api") == "blas"] or [1])
+    except Exception:
+        threads = 1
+    q = x["q"][0].float().double().cpu().numpy()
+    K = x["k_cache"][0].float().cpu().numpy()
+    V = x["v_cache"][0].float().cpu().numpy()
+    n = 0
+    t0 = time.perf_counter()
+    while True:
+        S, _ = O.select(q, K, cfg.k)
+        O.sparse_attention(q, K, V, S)
+        n += 1
+        el = time.perf_counter() - t0
+        if el >= seconds or n >= 50:
+            break
+    return {"value": n / el, "unit": "steps/s", "cores": threads, "kind": "oracle",
+            "sample": f"{n} full decode steps (selection + sparse attention, fp64 NumPy) of the "
+                      f"same workload on host copies; {el:.1f} s; BLAS threads {threads} of "
+                      f"{len(os.sched_getaffinity(0))} host cores"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--kv-copies", type=int, default=6)
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-profile", action="store_true")
+    ap.add_argument("--no-hit", action="store_true", help="skip the selection-reuse measurement")
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        _die_multi_gpu(max(args.gpus, world))
+
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    sys.path.insert(0, os.path.dirname(os.path.abspath(__file__)))
+    import sparse_kv_cache_ts_amd as ts
+    import workloads as W
+    ts.load()
+
+    cfg = W.QWEN_128K
+    miss, x = measure_decode(ts, W, cfg, args.steps, args.warmup, args.kv_copies, 1.0,
+                             not args.no_profile, "miss")
+    extra = {}
+    if not args.no_hit:
+        hitres, _ = measure_decode(ts, W, cfg, args.steps, args.warmup, args.kv_copies, 0.9,
+                                   not args.no_profile, "hit")
+        extra["hit_step"] = hitres
+
+    N, bpt = cfg.seq_len, kv_bytes_per_token(cfg)
+    kscan_bytes = cfg.batch * N * bpt
+    gather_bytes = cfg.batch * cfg.k * bpt * 2
+    roof = None
+    if "kernels_us" in miss:
+        ku = miss["kernels_us"]
+        t_scan = ku["score_pass1"] * 1e-6
+        achieved = kscan_bytes / t_scan / 1e9
+        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
+                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": None,
+                "kernel": "score_pass1 (K-scan)", "bytes_per_launch": kscan_bytes,
+                "avg_launch_us": round(ku["score_pass1"], 2)}
+        t_att = ku["attend"] * 1e-6
+        extra["kscan_plus_gather"] = {
+            "bytes": kscan_bytes + gather_bytes,
+            "GBps": round((kscan_bytes + gather_bytes) / (t_scan + t_att) / 1e9, 1),
+            "frac": round((kscan_bytes + gather_bytes) / (t_scan + t_att) / 1e9 / HBM_PEAK_GBPS, 4)}
+        extra["kernels_us"] = {kk: round(v, 2) for kk, v in ku.items()}
+        extra["profiled_ms_per_step"] = round(miss["profiled_ms_per_step"], 4)
+    extra["gpu_event_ms_per_step"] = round(miss["gpu_ms_per_step"], 4)
+    extra["attention_layer_latency_us"] = round(1e3 * miss["ms_per_step"], 2)
+    extra["step_algorithmic_bytes"] = kscan_bytes + gather_bytes
+    extra["whole_step_hbm_frac"] = round(
+        (kscan_bytes + gather_bytes) / (miss["ms_per_step"] * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4)
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        from oracle import ts_oracle as O
+        cpu = cpu_baseline(O, W, cfg, x, args.cpu_seconds)
+
+    line = {
+        "metric": "decode steps/sec + K-scan HBM GB/s (frac. of peak), Qwen2-7B shape, N=128K",
+        "value": round(miss["steps_per_s"], 2),
+        "unit": "steps/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(miss["ms_per_step"], 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "qwen2-7b-shape decode step, N=131072, batch 1, top-k 2048, "
+                               "selection every step (theta=1.0)",
+                   "num_q_heads": cfg.num_q_heads, "num_kv_heads": cfg.num_kv_heads,
+                   "head_dim": cfg.head_dim, "seq_len": N, "batch": cfg.batch, "k": cfg.k,
+                   "kv_dtype": "bf16", "accumulate": "f32", "kv_copies": args.kv_copies},
+        "roofline": roof,
+        "cpu_baseline": cpu,
+        "extra": extra,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -188,6 +188,24 @@ ts_status ts_select_prefill(const ts_kv_layout* layout /*[host]*/, int32_t chunk
                             const void* q, const void* k_cache, int32_t n_ctx, int32_t k,
                             float* votes, int32_t* idx, void* ws, size_t ws_bytes, void* stream);
 
+
+/* ---------------------------------------------------------------------------
+ * Kernel-level timing for measurement harnesses. While enabled, every kernel
+ * launch of every entry point is bracketed by two HIP events recorded on the
+ * launch's own stream, so the device-side duration of each kernel can be read
+ * back per kernel kind. Enabling/disabling is a process-wide host switch: do
+ * not toggle it while another thread launches. Events add a little queue
+ * overhead, so time throughput with it off.
+ *   ts_profile_read synchronizes every pending event and returns the number of
+ *   launches and their summed duration (ms) for kernel kind `id`
+ *   (0 <= id < ts_profile_num_kernels(); names from ts_profile_kernel_name).
+ * ------------------------------------------------------------------------- */
+int32_t     ts_profile_num_kernels(void);
+const char* ts_profile_kernel_name(int32_t id);
+ts_status   ts_profile_enable(int32_t on);
+ts_status   ts_profile_reset(void);
+ts_status   ts_profile_read(int32_t id, int64_t* launches /*[host]*/, double* total_ms /*[host]*/);
+
 #ifdef __cplusplus
 }
 #endif

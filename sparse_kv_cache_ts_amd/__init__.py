@@ -23,6 +23,7 @@ import torch
 __all__ = [
     "load", "lib_path", "TsError", "KvLayout", "make_layout", "score", "topk", "sparse_attend",
     "SelCache", "score_prefill", "select_prefill", "Workspace", "EXPORTS",
+    "profile_enable", "profile_reset", "profile_read",
 ]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -40,6 +41,8 @@ EXPORTS = [
     "ts_sel_cache_create", "ts_sel_cache_reset", "ts_sel_cache_destroy", "ts_sel_cache_stats",
     "ts_decode_step_workspace_size", "ts_decode_step",
     "ts_score_prefill_workspace_size", "ts_score_prefill", "ts_select_prefill",
+    "ts_profile_num_kernels", "ts_profile_kernel_name", "ts_profile_enable", "ts_profile_reset",
+    "ts_profile_read",
 ]
 
 
@@ -93,6 +96,11 @@ def load():
         "ts_score_prefill_workspace_size": ([L, I32, I32, I32, SZP], I32),
         "ts_score_prefill": ([L, I32, I32, P, P, I32, P, P, SZ, P], I32),
         "ts_select_prefill": ([L, I32, I32, P, P, I32, I32, P, P, P, SZ, P], I32),
+        "ts_profile_num_kernels": ([], I32),
+        "ts_profile_kernel_name": ([I32], ctypes.c_char_p),
+        "ts_profile_enable": ([I32], I32),
+        "ts_profile_reset": ([], I32),
+        "ts_profile_read": ([I32, ctypes.POINTER(ctypes.c_int64), ctypes.POINTER(F64)], I32),
     }
     for name, (args, res) in sig.items():
         fn = getattr(lib, name)
@@ -330,3 +338,24 @@ def select_prefill(q, k_ctx, q_pos0: int, k: int, scale=None, votes=None, idx=No
                                  _ptr(votes), _ptr(idx), _ptr(w), w.numel(), _stream(stream)),
            "ts_select_prefill")
     return votes, idx
+
+
+def profile_enable(on: bool = True):
+    """Bracket every kernel launch with HIP events on its own stream (see ts.h)."""
+    _check(load().ts_profile_enable(1 if on else 0), "ts_profile_enable")
+
+
+def profile_reset():
+    _check(load().ts_profile_reset(), "ts_profile_reset")
+
+
+def profile_read() -> dict:
+    """{kernel kind: (launches, total_ms)}; synchronizes the pending events."""
+    lib = load()
+    out = {}
+    for i in range(lib.ts_profile_num_kernels()):
+        n = ctypes.c_int64()
+        ms = ctypes.c_double()
+        _check(lib.ts_profile_read(i, ctypes.byref(n), ctypes.byref(ms)), "ts_profile_read")
+        out[lib.ts_profile_kernel_name(i).decode()] = (n.value, ms.value)
+    return out

@@ -2,8 +2,11 @@
 // workspace planning and launch sequencing. No kernel code lives here.
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <cmath>
 #include <cstdarg>
+#include <mutex>
+#include <vector>
 #include <cstdio>
 #include <cstring>
 #include <string>
@@ -40,6 +43,81 @@ ts_status ok() {
 ts_status hip_check(hipError_t e, const char* what) {
   if (e != hipSuccess) return fail(TS_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
   return TS_OK;
+}
+
+
+// ---- kernel-level timing (ts_profile_*) ---------------------------------------
+enum KernelKind {
+  kKPrologue, kKScore, kKVotes, kKTopkHist, kKTopkCompact, kKAttend, kKCombine,
+  kKPrefillLse, kKPrefillVotes, kKFill, kKNum
+};
+const char* const kKernelNames[kKNum] = {
+  "prologue", "score_pass1", "votes", "topk_hist", "topk_compact", "attend", "combine",
+  "prefill_lse", "prefill_votes", "fill_zero"
+};
+
+struct Prof {
+  std::atomic<bool> on{false};
+  std::mutex mu;
+  struct Rec { int kind; hipEvent_t a, b; };
+  std::vector<Rec> pending;
+  std::vector<hipEvent_t> pool;
+  double total_ms[kKNum] = {};
+  long long count[kKNum] = {};
+};
+Prof& prof() {
+  static Prof* p = new Prof();   // never destroyed: events may outlive static teardown
+  return *p;
+}
+
+hipEvent_t prof_event() {
+  Prof& P = prof();
+  std::lock_guard<std::mutex> g(P.mu);
+  if (!P.pool.empty()) {
+    hipEvent_t e = P.pool.back();
+    P.pool.pop_back();
+    return e;
+  }
+  hipEvent_t e = nullptr;
+  if (hipEventCreate(&e) != hipSuccess) return nullptr;
+  return e;
+}
+
+template <class F>
+ts_status launch_timed(int kind, hipStream_t st, F&& f, const char* what) {
+  Prof& P = prof();
+  if (!P.on.load(std::memory_order_relaxed)) return hip_check(f(), what);
+  hipEvent_t a = prof_event(), b = prof_event();
+  if (a) (void)hipEventRecord(a, st);
+  hipError_t e = f();
+  if (b) (void)hipEventRecord(b, st);
+  if (a && b) {
+    std::lock_guard<std::mutex> g(P.mu);
+    P.pending.push_back({kind, a, b});
+  }
+  return hip_check(e, what);
+}
+
+// fold every pending event pair into the totals (synchronizes on the events)
+ts_status prof_drain() {
+  Prof& P = prof();
+  std::lock_guard<std::mutex> g(P.mu);
+  ts_status st = TS_OK;
+  for (auto& r : P.pending) {
+    float ms = 0.f;
+    hipError_t e = hipEventSynchronize(r.b);
+    if (e == hipSuccess) e = hipEventElapsedTime(&ms, r.a, r.b);
+    if (e == hipSuccess) {
+      P.total_ms[r.kind] += ms;
+      P.count[r.kind] += 1;
+    } else if (st == TS_OK) {
+      st = fail(TS_ERR_HIP, "profile events: %s", hipGetErrorString(e));
+    }
+    P.pool.push_back(r.a);
+    P.pool.push_back(r.b);
+  }
+  P.pending.clear();
+  return st;
 }
 
 struct Carve {
@@ -284,6 +362,7 @@ ts_status check_ws(const void* ws, size_t have, size_t need) {
   } while (0)
 
 #define TS_LAUNCH(expr, what) TS_TRY(hip_check((expr), what))
+#define TS_LAUNCH_K(kind, expr, what) TS_TRY(launch_timed((kind), st, [&]() { return (expr); }, what))
 
 }  // namespace
 
@@ -333,12 +412,12 @@ ts_status ts_score(const ts_kv_layout* L, int32_t batch, const void* q, const vo
   PrologueParams pp{};
   pp.ctrl = at<uint32_t>(ws, s.ctrl);
   pp.rows = batch;
-  TS_LAUNCH(launch_prologue(pp, batch, st), "prologue");
+  TS_LAUNCH_K(kKPrologue, launch_prologue(pp, batch, st), "prologue");
   ScoreParams sp = score_params(g, s, batch, ws, q, k_cache, g.paged ? page_table : nullptr,
                                 seq_lens, nullptr);
-  TS_LAUNCH(launch_score_pass1(g.dtype, g.d, g.paged, sp, st), "score pass 1");
+  TS_LAUNCH_K(kKScore, launch_score_pass1(g.dtype, g.d, g.paged, sp, st), "score pass 1");
   VoteParams vp = vote_params(g, s, batch, ws, seq_lens, nullptr, votes, g.max_len, 1, 0);
-  TS_LAUNCH(launch_votes(vp, cdiv(g.max_len, kVoteTile), st), "votes");
+  TS_LAUNCH_K(kKVotes, launch_votes(vp, cdiv(g.max_len, kVoteTile), st), "votes");
   return ok();
 }
 
@@ -363,7 +442,7 @@ static ts_status run_topk(int rows, int row_stride, const float* votes, const in
   pp.flags = at<unsigned long long>(ws, t.flags);
   pp.rows = rows;
   pp.max_chunks = t.max_chunks;
-  TS_LAUNCH(launch_prologue(pp, rows, st), "prologue");
+  TS_LAUNCH_K(kKPrologue, launch_prologue(pp, rows, st), "prologue");
   TopkParams tp{};
   tp.votes = votes;
   tp.row_lens = row_lens;
@@ -376,10 +455,10 @@ static ts_status run_topk(int rows, int row_stride, const float* votes, const in
   tp.k = k;
   tp.max_chunks = t.max_chunks;
   const int gx = cdiv(max_row_len, kTopkChunk);
-  TS_LAUNCH(launch_topk_hist(tp, 0, gx, st), "top-k pass 0");
-  TS_LAUNCH(launch_topk_hist(tp, 1, gx, st), "top-k pass 1");
-  TS_LAUNCH(launch_topk_hist(tp, 2, gx, st), "top-k pass 2");
-  TS_LAUNCH(launch_topk_compact(tp, gx, st), "top-k compaction");
+  TS_LAUNCH_K(kKTopkHist, launch_topk_hist(tp, 0, gx, st), "top-k pass 0");
+  TS_LAUNCH_K(kKTopkHist, launch_topk_hist(tp, 1, gx, st), "top-k pass 1");
+  TS_LAUNCH_K(kKTopkHist, launch_topk_hist(tp, 2, gx, st), "top-k pass 2");
+  TS_LAUNCH_K(kKTopkCompact, launch_topk_compact(tp, gx, st), "top-k compaction");
   return TS_OK;
 }
 
@@ -429,9 +508,9 @@ ts_status ts_sparse_attend(const ts_kv_layout* L, int32_t batch, const void* q, 
   hipStream_t st = static_cast<hipStream_t>(stream);
   AttendParams ap = attend_params(g, a, batch, ws, q, k_cache, v_cache,
                                   g.paged ? page_table : nullptr, seq_lens, idx, k);
-  TS_LAUNCH(launch_attend(g.dtype, g.d, g.paged, ap, st), "sparse attention");
+  TS_LAUNCH_K(kKAttend, launch_attend(g.dtype, g.d, g.paged, ap, st), "sparse attention");
   CombineParams cp = combine_params(g, a, batch, ws, out);
-  TS_LAUNCH(launch_combine(cp, st), "combine");
+  TS_LAUNCH_K(kKCombine, launch_combine(cp, st), "combine");
   return ok();
 }
 
@@ -482,9 +561,9 @@ ts_status ts_sel_cache_reset(ts_sel_cache* c, void* stream) {
   if (!c) return fail(TS_ERR_INVALID_ARG, "cache is NULL");
   hipStream_t st = static_cast<hipStream_t>(stream);
   const size_t n = (size_t)c->dev.max_batch;
-  TS_LAUNCH(launch_fill_zero(c->dev.valid, n, st), "reset");
-  TS_LAUNCH(launch_fill_zero(c->dev.hits, 2 * n, st), "reset");
-  TS_LAUNCH(launch_fill_zero(c->dev.misses, 2 * n, st), "reset");
+  TS_LAUNCH_K(kKFill, launch_fill_zero(c->dev.valid, n, st), "reset");
+  TS_LAUNCH_K(kKFill, launch_fill_zero(c->dev.hits, 2 * n, st), "reset");
+  TS_LAUNCH_K(kKFill, launch_fill_zero(c->dev.misses, 2 * n, st), "reset");
   return ok();
 }
 
@@ -561,16 +640,16 @@ ts_status ts_decode_step(ts_sel_cache* cache, const ts_kv_layout* L, int32_t bat
   pp.seq_lens = seq_lens;
   pp.B = batch;
   pp.theta = theta;
-  TS_LAUNCH(launch_prologue(pp, batch, st), "prologue");
+  TS_LAUNCH_K(kKPrologue, launch_prologue(pp, batch, st), "prologue");
   const int32_t* hit = cache->dev.hit;
 
   // 2. K-scan (misses only)
   ScoreParams sp = score_params(g, p.s, batch, ws, q, k_cache, pt, seq_lens, hit);
-  TS_LAUNCH(launch_score_pass1(g.dtype, g.d, g.paged, sp, st), "score pass 1");
+  TS_LAUNCH_K(kKScore, launch_score_pass1(g.dtype, g.d, g.paged, sp, st), "score pass 1");
   // 3. votes + first radix histogram
   float* votes = at<float>(ws, p.votes);
   VoteParams vp = vote_params(g, p.s, batch, ws, seq_lens, hit, votes, g.max_len, k, 1);
-  TS_LAUNCH(launch_votes(vp, cdiv(g.max_len, kVoteTile), st), "votes");
+  TS_LAUNCH_K(kKVotes, launch_votes(vp, cdiv(g.max_len, kVoteTile), st), "votes");
   // 4. top-k into the cache's stored selection
   TopkParams tp{};
   tp.votes = votes;
@@ -584,13 +663,13 @@ ts_status ts_decode_step(ts_sel_cache* cache, const ts_kv_layout* L, int32_t bat
   tp.k = k;
   tp.max_chunks = p.t.max_chunks;
   const int gx = cdiv(g.max_len, kTopkChunk);
-  TS_LAUNCH(launch_topk_hist(tp, 1, gx, st), "top-k pass 1");
-  TS_LAUNCH(launch_topk_hist(tp, 2, gx, st), "top-k pass 2");
-  TS_LAUNCH(launch_topk_compact(tp, gx, st), "top-k compaction");
+  TS_LAUNCH_K(kKTopkHist, launch_topk_hist(tp, 1, gx, st), "top-k pass 1");
+  TS_LAUNCH_K(kKTopkHist, launch_topk_hist(tp, 2, gx, st), "top-k pass 2");
+  TS_LAUNCH_K(kKTopkCompact, launch_topk_compact(tp, gx, st), "top-k compaction");
   // 5. sparse attention over the current selection; 6. combine + state update
   AttendParams ap = attend_params(g, p.a, batch, ws, q, k_cache, v_cache, pt, seq_lens,
                                   cache->dev.sel, k);
-  TS_LAUNCH(launch_attend(g.dtype, g.d, g.paged, ap, st), "sparse attention");
+  TS_LAUNCH_K(kKAttend, launch_attend(g.dtype, g.d, g.paged, ap, st), "sparse attention");
   CombineParams cp = combine_params(g, p.a, batch, ws, out);
   cp.cache = cache->dev;
   cp.q = q;
@@ -598,7 +677,7 @@ ts_status ts_decode_step(ts_sel_cache* cache, const ts_kv_layout* L, int32_t bat
   cp.seq_lens = seq_lens;
   cp.idx_out = idx_out;
   cp.hit_out = hit_out;
-  TS_LAUNCH(launch_combine(cp, st), "combine");
+  TS_LAUNCH_K(kKCombine, launch_combine(cp, st), "combine");
   return ok();
 }
 
@@ -624,6 +703,41 @@ ts_status ts_select_prefill(const ts_kv_layout* L, int32_t chunk, int32_t q_pos0
   (void)L; (void)chunk; (void)q_pos0; (void)q; (void)k_cache; (void)n_ctx; (void)k; (void)votes;
   (void)idx; (void)ws; (void)ws_bytes; (void)stream;
   return fail(TS_ERR_UNSUPPORTED, "prefill scoring not built yet");
+}
+
+// ------------------------------------------------------------ kernel timing
+
+int32_t ts_profile_num_kernels(void) { return kKNum; }
+
+const char* ts_profile_kernel_name(int32_t id) {
+  return (id >= 0 && id < kKNum) ? kKernelNames[id] : "";
+}
+
+ts_status ts_profile_enable(int32_t on) {
+  prof().on.store(on != 0);
+  return ok();
+}
+
+ts_status ts_profile_reset(void) {
+  TS_TRY(prof_drain());
+  Prof& P = prof();
+  std::lock_guard<std::mutex> g(P.mu);
+  for (int i = 0; i < kKNum; ++i) {
+    P.total_ms[i] = 0.0;
+    P.count[i] = 0;
+  }
+  return ok();
+}
+
+ts_status ts_profile_read(int32_t id, int64_t* launches, double* total_ms) {
+  if (id < 0 || id >= kKNum || !launches || !total_ms)
+    return fail(TS_ERR_INVALID_ARG, "bad kernel id or NULL output");
+  TS_TRY(prof_drain());
+  Prof& P = prof();
+  std::lock_guard<std::mutex> g(P.mu);
+  *launches = P.count[id];
+  *total_ms = P.total_ms[id];
+  return ok();
 }
 
 }  // extern "C"
