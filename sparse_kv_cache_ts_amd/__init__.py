@@ -62,7 +62,8 @@ class KvLayout(ctypes.Structure):
 
 
 def lib_path() -> str:
-    return os.path.join(_PKG, "libts.so")
+    """The in-tree library; TS_LIBRARY may name another build of the same sources."""
+    return os.environ.get("TS_LIBRARY") or os.path.join(_PKG, "libts.so")
 
 
 def load():

@@ -33,30 +33,32 @@ def sources() -> list:
     return [os.path.join(CSRC, f) for f in names]
 
 
-def _compile(src: str) -> str:
-    obj = os.path.join(OUT_DIR, os.path.basename(src) + ".o")
-    cmd = [HIPCC, *COMMON, "-x", "hip", "-c", src, "-o", obj]
+def _compile(src: str, out_dir: str = OUT_DIR, defines=()) -> str:
+    obj = os.path.join(out_dir, os.path.basename(src) + ".o")
+    cmd = [HIPCC, *COMMON, *[f"-D{d}" for d in defines], "-x", "hip", "-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed on {src}:\n{r.stderr}")
     return obj
 
 
-def build(verbose: bool = True) -> str:
-    os.makedirs(OUT_DIR, exist_ok=True)
+def build(verbose: bool = True, lib: str = LIB, defines=()) -> str:
+    """Compile every source and link `lib` (default: the in-tree libts.so)."""
+    out_dir = OUT_DIR if lib == LIB else lib + ".objs"
+    os.makedirs(out_dir, exist_ok=True)
     srcs = sources()
     jobs = min(len(srcs), int(os.environ.get("MAX_JOBS", "8")), 16)
     with ThreadPoolExecutor(max_workers=max(1, jobs)) as ex:
-        objs = list(ex.map(_compile, srcs))
-    tmp = LIB + ".tmp"
+        objs = list(ex.map(lambda f: _compile(f, out_dir, defines), srcs))
+    tmp = lib + ".tmp"
     cmd = [HIPCC, "-shared", "-fPIC", f"--offload-arch={ARCH}", *objs, "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stderr}")
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib)
     if verbose:
-        print(f"built {LIB} from {len(srcs)} sources for {ARCH}")
-    return LIB
+        print(f"built {lib} from {len(srcs)} sources for {ARCH}")
+    return lib
 
 
 if __name__ == "__main__":

@@ -25,12 +25,13 @@ __global__ __launch_bounds__(256) void attend_kernel(AttendParams p) {
   constexpr int CPL = ROWB / (16 * LPR);                   // 16-byte chunks per lane
   constexpr int EPC = 16 / ESZ;                            // elements per chunk
   constexpr int EPL = EPC * CPL;                           // elements per lane
-  constexpr int RG = 256 / LPR;
   constexpr int W = 4 * CPL;                               // 32-bit words per lane
+  constexpr int UA = 4;                                    // gathered rows in flight per row group
+  constexpr int RG = 256 / LPR;
 
-  __shared__ float s_m[RG][GS];
-  __shared__ float s_l[RG][GS];
-  __shared__ float s_acc[RG * D];
+  __shared__ float s_m[4][GS];
+  __shared__ float s_l[4][GS];
+  __shared__ float s_acc[4 * GS * D];
 
   const int split = blockIdx.x;
   const int kvh = blockIdx.y / p.nslices;
@@ -39,8 +40,21 @@ __global__ __launch_bounds__(256) void attend_kernel(AttendParams p) {
   const int tid = threadIdx.x;
   const int j = tid % LPR;
   const int rg = tid / LPR;
+  const int wv = tid >> 6, lane = tid & 63;
   const int len = p.seq_lens[b];
+  const int pbeg = split * p.split;
+  const int pend = min(pbeg + p.split, p.nidx);
+  const int32_t* idx = p.idx + (size_t)b * p.nidx;
+  const int Hkv = p.Hkv;
 
+  // first batch of indices together with the query slice
+  int tok[UA];
+#pragma unroll
+  for (int u = 0; u < UA; ++u) {
+    const int pos = pbeg + rg + u * RG;
+    const int t = pos < pend ? idx[pos] : -1;
+    tok[u] = (t >= 0 && t < len) ? t : -1;
+  }
   uint32_t qw[GS][W];
 #pragma unroll
   for (int hh = 0; hh < GS; ++hh) {
@@ -48,7 +62,7 @@ __global__ __launch_bounds__(256) void attend_kernel(AttendParams p) {
     const char* qb = (const char*)p.q + ((size_t)b * p.Hq + head) * ROWB;
 #pragma unroll
     for (int c = 0; c < CPL; ++c) {
-      uint4 v = ld16(qb + (c * LPR + j) * 16);
+      const uint4 v = ld16(qb + (c * LPR + j) * 16);
       qw[hh][4 * c + 0] = v.x; qw[hh][4 * c + 1] = v.y;
       qw[hh][4 * c + 2] = v.z; qw[hh][4 * c + 3] = v.w;
     }
@@ -63,136 +77,200 @@ __global__ __launch_bounds__(256) void attend_kernel(AttendParams p) {
     for (int e = 0; e < EPL; ++e) acc[hh][e] = 0.f;
   }
 
-  const int pbeg = split * p.split;
-  const int pend = min(pbeg + p.split, p.nidx);
-  const int32_t* idx = p.idx + (size_t)b * p.nidx;
-  const int Hkv = p.Hkv;
-  for (int pos = pbeg + rg; pos < pend; pos += RG) {
-    const int tok = idx[pos];
-    if (tok < 0 || tok >= len) continue;
-    size_t row;
-    if constexpr (PAGED) {
-      const int pg = p.page_table[(size_t)b * p.pt_stride + (tok >> p.ps_log2)];
-      row = ((((size_t)pg << p.ps_log2) + (tok & ((1 << p.ps_log2) - 1))) * Hkv + kvh);
-    } else {
-      row = (((size_t)b * p.max_len + tok) * Hkv + kvh);
-    }
-    const char* kp = (const char*)p.k + row * ROWB;
-    const char* vp = (const char*)p.v + row * ROWB;
-    uint32_t kw[W], vw[W];
+  for (int pos0 = pbeg + rg; pos0 < pend; pos0 += RG * UA) {
+    if (pos0 != pbeg + rg) {
 #pragma unroll
-    for (int c = 0; c < CPL; ++c) {
-      uint4 a = ld16(kp + (c * LPR + j) * 16);
-      uint4 v = ld16(vp + (c * LPR + j) * 16);
-      kw[4 * c + 0] = a.x; kw[4 * c + 1] = a.y; kw[4 * c + 2] = a.z; kw[4 * c + 3] = a.w;
-      vw[4 * c + 0] = v.x; vw[4 * c + 1] = v.y; vw[4 * c + 2] = v.z; vw[4 * c + 3] = v.w;
-    }
-    float vf[EPL];
-#pragma unroll
-    for (int w = 0; w < W; ++w) {
-      if constexpr (DT == 1) {
-        vf[2 * w] = bf16_lo(vw[w]);
-        vf[2 * w + 1] = bf16_hi(vw[w]);
-      } else {
-        vf[w] = __uint_as_float(vw[w]);
+      for (int u = 0; u < UA; ++u) {
+        const int pos = pos0 + u * RG;
+        const int t = pos < pend ? idx[pos] : -1;
+        tok[u] = (t >= 0 && t < len) ? t : -1;
       }
     }
+    uint32_t kw[UA][W], vw[UA][W];
+#pragma unroll
+    for (int u = 0; u < UA; ++u) {
+      if (tok[u] >= 0) {
+        size_t row;
+        if constexpr (PAGED) {
+          const int pg = p.page_table[(size_t)b * p.pt_stride + (tok[u] >> p.ps_log2)];
+          row = ((((size_t)pg << p.ps_log2) + (tok[u] & ((1 << p.ps_log2) - 1))) * Hkv + kvh);
+        } else {
+          row = (((size_t)b * p.max_len + tok[u]) * Hkv + kvh);
+        }
+        const char* kp = (const char*)p.k + row * ROWB;
+        const char* vp = (const char*)p.v + row * ROWB;
+#pragma unroll
+        for (int c = 0; c < CPL; ++c) {
+          const uint4 a = ld16(kp + (c * LPR + j) * 16);
+          const uint4 v = ld16(vp + (c * LPR + j) * 16);
+          kw[u][4 * c + 0] = a.x; kw[u][4 * c + 1] = a.y; kw[u][4 * c + 2] = a.z; kw[u][4 * c + 3] = a.w;
+          vw[u][4 * c + 0] = v.x; vw[u][4 * c + 1] = v.y; vw[u][4 * c + 2] = v.z; vw[u][4 * c + 3] = v.w;
+        }
+      } else {
+#pragma unroll
+        for (int w = 0; w < W; ++w) { kw[u][w] = 0u; vw[u][w] = 0u; }
+      }
+    }
+    // scores of the batch, one rescale of the running sums per batch
 #pragma unroll
     for (int hh = 0; hh < GS; ++hh) {
-      float a = 0.f;
+      float sc[UA];
+      float bm = m[hh];
 #pragma unroll
-      for (int w = 0; w < W; ++w) {
-        if constexpr (DT == 1) a = dot2_bf16(kw[w], qw[hh][w], a);
-        else a = fmaf(__uint_as_float(kw[w]), __uint_as_float(qw[hh][w]), a);
+      for (int u = 0; u < UA; ++u) {
+        float a = 0.f;
+#pragma unroll
+        for (int w = 0; w < W; ++w) {
+          if constexpr (DT == 1) a = dot2_bf16(kw[u][w], qw[hh][w], a);
+          else a = fmaf(__uint_as_float(kw[u][w]), __uint_as_float(qw[hh][w]), a);
+        }
+        sc[u] = (tok[u] >= 0) ? group_sum<LPR>(a) * p.scale2 : -INFINITY;
+        bm = fmaxf(bm, sc[u]);
       }
-      const float s = group_sum<LPR>(a) * p.scale2;
-      const float nm = fmaxf(m[hh], s);
-      const float corr = exp2f(m[hh] - nm);   // 0 when m was -inf
-      const float pw = exp2f(s - nm);
-      l[hh] = l[hh] * corr + pw;
+      if (bm == -INFINITY) continue;           // nothing valid yet for this row group
+      const float corr = ex2(m[hh] - bm);      // 0 when m was -inf
+      float pw[UA];
+      float ls = l[hh] * corr;
 #pragma unroll
-      for (int e = 0; e < EPL; ++e) acc[hh][e] = fmaf(pw, vf[e], acc[hh][e] * corr);
-      m[hh] = nm;
+      for (int u = 0; u < UA; ++u) {
+        pw[u] = ex2(sc[u] - bm);               // 0 for invalid rows
+        ls += pw[u];
+      }
+      l[hh] = ls;
+      m[hh] = bm;
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) {
+        float a = acc[hh][e] * corr;
+#pragma unroll
+        for (int u = 0; u < UA; ++u) {
+          float vf;
+          if constexpr (DT == 1) vf = (e & 1) ? bf16_hi(vw[u][e >> 1]) : bf16_lo(vw[u][e >> 1]);
+          else vf = __uint_as_float(vw[u][e]);
+          a = fmaf(pw[u], vf, a);
+        }
+        acc[hh][e] = a;
+      }
     }
   }
 
-  // merge the row groups (fixed order: deterministic)
-  if (j == 0) {
+  // merge the row groups (fixed order: deterministic): the common max and the
+  // sums over a wave's row groups by lane shuffles, over the 4 waves in LDS
 #pragma unroll
-    for (int hh = 0; hh < GS; ++hh) {
-      s_m[rg][hh] = m[hh];
-      s_l[rg][hh] = l[hh];
-    }
+  for (int hh = 0; hh < GS; ++hh) {
+    float mw = m[hh];
+#pragma unroll
+    for (int o = LPR; o < 64; o <<= 1) mw = fmaxf(mw, __shfl_xor(mw, o));
+    if (lane == 0) s_m[wv][hh] = mw;
   }
   __syncthreads();
 #pragma unroll
   for (int hh = 0; hh < GS; ++hh) {
-    float M = -INFINITY;
-    for (int r = 0; r < RG; ++r)
-      if (s_l[r][hh] > 0.f) M = fmaxf(M, s_m[r][hh]);
-    const float f = (l[hh] > 0.f) ? exp2f(m[hh] - M) : 0.f;
+    const float M = fmaxf(fmaxf(s_m[0][hh], s_m[1][hh]), fmaxf(s_m[2][hh], s_m[3][hh]));
+    const float f = (l[hh] > 0.f) ? ex2(m[hh] - M) : 0.f;
+    float lw = l[hh] * f;
 #pragma unroll
-    for (int c = 0; c < CPL; ++c)
+    for (int o = LPR; o < 64; o <<= 1) lw += __shfl_xor(lw, o);
 #pragma unroll
-      for (int e = 0; e < EPC; ++e)
-        s_acc[rg * D + (c * LPR + j) * EPC + e] = acc[hh][c * EPC + e] * f;
-    __syncthreads();
+    for (int e = 0; e < EPL; ++e) {
+      float v = acc[hh][e] * f;
+#pragma unroll
+      for (int o = LPR; o < 64; o <<= 1) v += __shfl_xor(v, o);
+      acc[hh][e] = v;
+    }
+    if (lane < LPR) {
+#pragma unroll
+      for (int c = 0; c < CPL; ++c)
+#pragma unroll
+        for (int e = 0; e < EPC; ++e)
+          s_acc[(wv * GS + hh) * D + (c * LPR + j) * EPC + e] = acc[hh][c * EPC + e];
+    }
+    if (lane == 0) s_l[wv][hh] = lw;
+  }
+  __syncthreads();
+  for (int i = tid; i < GS * D; i += 256) {
+    const int hh = i / D, d = i - hh * D;
+    const float sum = (s_acc[(0 * GS + hh) * D + d] + s_acc[(1 * GS + hh) * D + d]) +
+                      (s_acc[(2 * GS + hh) * D + d] + s_acc[(3 * GS + hh) * D + d]);
     const int head = kvh * p.G + slice * GS + hh;
     const size_t o = ((size_t)b * p.Hq + head) * p.nsplit + split;
-    for (int d = tid; d < D; d += 256) {
-      float sum = 0.f;
-      for (int r = 0; r < RG; ++r) sum += s_acc[r * D + d];
-      p.pacc[o * D + d] = sum;
+    p.pacc[o * D + d] = sum;
+    if (d == 0) {
+      p.pm[o] = fmaxf(fmaxf(s_m[0][hh], s_m[1][hh]), fmaxf(s_m[2][hh], s_m[3][hh]));
+      p.pl[o] = (s_l[0][hh] + s_l[1][hh]) + (s_l[2][hh] + s_l[3][hh]);
     }
-    if (tid == 0) {
-      float L = 0.f;
-      for (int r = 0; r < RG; ++r)
-        if (s_l[r][hh] > 0.f) L += s_l[r][hh] * exp2f(s_m[r][hh] - M);
-      p.pm[o] = M;
-      p.pl[o] = L;
-    }
-    __syncthreads();
   }
 }
 
 __global__ __launch_bounds__(128) void combine_kernel(CombineParams p) {
+  __shared__ float s_w[kMaxSplits];
+  __shared__ float s_red[4];
   const int h = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
+  const int lane = tid & 63, wv = tid >> 6;
   const size_t base = ((size_t)b * p.Hq + h) * p.nsplit;
-  float M = -INFINITY;
-  for (int s = 0; s < p.nsplit; ++s)
-    if (p.pl[base + s] > 0.f) M = fmaxf(M, p.pm[base + s]);
-  float L = 0.f;
-  for (int s = 0; s < p.nsplit; ++s)
-    if (p.pl[base + s] > 0.f) L += p.pl[base + s] * exp2f(p.pm[base + s] - M);
+  float m = -INFINITY;
+  for (int s = tid; s < p.nsplit; s += 128)
+    if (p.pl[base + s] > 0.f) m = fmaxf(m, p.pm[base + s]);
+  m = wave_max(m);
+  if (lane == 0) s_red[wv] = m;
+  __syncthreads();
+  const float M = fmaxf(s_red[0], s_red[1]);
+  float lsum = 0.f;
+  for (int s = tid; s < p.nsplit; s += 128) {
+    const float pl = p.pl[base + s];
+    const float w = pl > 0.f ? ex2(p.pm[base + s] - M) : 0.f;
+    s_w[s] = w;
+    lsum += pl * w;
+  }
+  lsum = wave_sum(lsum);
+  __syncthreads();
+  if (lane == 0) s_red[2 + wv] = lsum;
+  __syncthreads();
+  const float L = s_red[2] + s_red[3];
   for (int d = tid; d < p.d; d += 128) {
-    float o = 0.f;
-    for (int s = 0; s < p.nsplit; ++s)
-      if (p.pl[base + s] > 0.f) o += p.pacc[(base + s) * p.d + d] * exp2f(p.pm[base + s] - M);
+    // every split's acc was written (zeros for an empty split, whose weight is 0)
+    const float* pa = p.pacc + base * p.d + d;
+    float o0 = 0.f, o1 = 0.f, o2 = 0.f, o3 = 0.f;
+    int s = 0;
+    for (; s + 8 <= p.nsplit; s += 8) {
+      float a[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) a[u] = pa[(size_t)(s + u) * p.d];
+      o0 = fmaf(a[0], s_w[s], o0);
+      o1 = fmaf(a[1], s_w[s + 1], o1);
+      o2 = fmaf(a[2], s_w[s + 2], o2);
+      o3 = fmaf(a[3], s_w[s + 3], o3);
+      o0 = fmaf(a[4], s_w[s + 4], o0);
+      o1 = fmaf(a[5], s_w[s + 5], o1);
+      o2 = fmaf(a[6], s_w[s + 6], o2);
+      o3 = fmaf(a[7], s_w[s + 7], o3);
+    }
+    for (; s < p.nsplit; ++s) o0 = fmaf(pa[(size_t)s * p.d], s_w[s], o0);
+    const float o = (o0 + o1) + (o2 + o3);
     p.out[((size_t)b * p.Hq + h) * p.d + d] = (L > 0.f) ? o / L : 0.f;
   }
 
-  // Selection-Cache state update, once per sequence
-  if (p.cache.prev_q == nullptr || h != 0) return;
+  // Selection-Cache state update, spread over the head blocks of a sequence
+  if (p.cache.prev_q == nullptr) return;
   const SelCacheDev& c = p.cache;
   const int hit = c.hit[b];
-  const int len = p.seq_lens[b];
   const int n = c.Hq * c.d;
   if (c.mode == 0 || !hit) {
-    float* pq = c.prev_q + (size_t)b * n;
-    if (p.dtype == 1) {
-      const uint16_t* q = (const uint16_t*)p.q + (size_t)b * n;
-      for (int i = tid; i < n; i += 128) pq[i] = __uint_as_float((uint32_t)q[i] << 16);
-    } else {
-      const float* q = (const float*)p.q + (size_t)b * n;
-      for (int i = tid; i < n; i += 128) pq[i] = q[i];
+    float* pq = c.prev_q + (size_t)b * n + (size_t)h * c.d;
+    for (int i = tid; i < c.d; i += 128) {
+      if (p.dtype == 1)
+        pq[i] = __uint_as_float((uint32_t)((const uint16_t*)p.q)[(size_t)b * n + (size_t)h * c.d + i] << 16);
+      else
+        pq[i] = ((const float*)p.q)[(size_t)b * n + (size_t)h * c.d + i];
     }
   }
   if (p.idx_out) {
+    const int per = (c.k + p.Hq - 1) / p.Hq;
+    const int lo = h * per, hi = min(c.k, lo + per);
     const int32_t* sel = c.sel + (size_t)b * c.k;
-    for (int i = tid; i < c.k; i += 128) p.idx_out[(size_t)b * c.k + i] = sel[i];
+    for (int i = lo + tid; i < hi; i += 128) p.idx_out[(size_t)b * c.k + i] = sel[i];
   }
-  if (tid == 0) {
-    c.valid[b] = len > 0 ? 1 : 0;
+  if (h == 0 && tid == 0) {
+    c.valid[b] = p.seq_lens[b] > 0 ? 1 : 0;
     if (hit) c.hits[b] += 1;
     else c.misses[b] += 1;
     if (p.hit_out) p.hit_out[b] = hit;

@@ -16,38 +16,51 @@
 // use v_dot2c_f32_bf16 (two bf16 products per instruction, fp32 accumulate);
 // the LPR partial sums are combined with DPP row operations. Logits (base 2:
 // scale*log2(e)*q.k) land in LDS, are written once, coalesced, to the logit
-// buffer, and each (head, tile) leaves its max and sum of exp2. The last
-// work-group of a sequence to finish (device-scope counter) folds the tile
-// partials into each head's log-sum-exp.
+// buffer, and each (head, tile) leaves its max and sum of exp2.
 //
-// Pass 2 (votes_kernel) turns the logits into votes v[j] = sum_h
-// exp2(s[h,j] - lse[h]) and, for the decode path, builds the first radix
-// histogram of the top-k on the fly.
+// Pass 2 (votes_kernel): every work-group first folds the tile partials into
+// each head's log-sum-exp (redundantly: a few KB from L2, and no cross-work-
+// group synchronisation, whose device-scope fences cost far more on this
+// multi-XCD part), then turns its logits into votes v[j] = sum_h
+// exp2(s[h,j] - lse[h]) and, for the decode path, adds them to the first
+// radix histogram of the top-k.
 #include "ts_device.h"
 
 namespace ts {
 
-template <int DT, int D, int GS, bool PAGED>
-__global__ __launch_bounds__(256) void score_pass1_kernel(ScoreParams p) {
-  constexpr int ESZ = DT ? 2 : 4;
-  constexpr int ROWB = D * ESZ;      // bytes per (token, KV head) row
-  constexpr int LPR = ROWB / 32;     // lanes per row, 32 bytes each
-  constexpr int RG = 256 / LPR;      // row groups per work-group
-  constexpr int U = 4;               // rows in flight per lane
-  static_assert(LPR >= 4 && LPR <= 16, "row split");
+// Row split: LPR lanes per (token, KV head) row, CPL 16-byte chunks per lane;
+// chunk c of lane j covers bytes c*16*LPR + 16*j of the row, so one load
+// instruction reads 16*LPR contiguous bytes of every row it touches.
+template <int DT, int D, int LPR>
+struct RowSplit {
+  static constexpr int ESZ = DT ? 2 : 4;
+  static constexpr int ROWB = D * ESZ;
+  static constexpr int CPL = ROWB / (16 * LPR);
+  static constexpr int WPL = 4 * CPL;            // 32-bit words per lane per row
+  static constexpr int RG = 256 / LPR;           // row groups per work-group
+  static_assert(CPL >= 1 && CPL * 16 * LPR == ROWB, "row split");
+};
 
-  extern __shared__ float s_log[];   // [Hkv*GS][kScoreTile]
-  __shared__ int s_page[kScoreTile];
-  __shared__ int s_last;
+template <int DT, int D, int GS, bool PAGED, int TILE, int LPR>
+__global__ __launch_bounds__(256) void score_pass1_kernel(ScoreParams p) {
+  using RS = RowSplit<DT, D, LPR>;
+  constexpr int ROWB = RS::ROWB, CPL = RS::CPL, WPL = RS::WPL, RG = RS::RG;
+  constexpr int U = (8 / CPL) > 0 ? (8 / CPL) : 1;   // rows per lane per batch (8 loads)
+  constexpr int NW = (GS + LPR - 1) / LPR;           // logits each lane stores per row
+  constexpr int LS = TILE + 1;                       // padded LDS row: stores spread over banks
+  static_assert(TILE % 64 == 0 && TILE <= kScoreTileMax, "tile");
+
+  extern __shared__ float s_log[];   // [Hkv*GS][TILE+1]
+  __shared__ long long s_page[PAGED ? TILE : 1];
 
   const int tile = blockIdx.x;
   const int b = blockIdx.y / p.nslices;
   const int slice = blockIdx.y - b * p.nslices;
   if (p.hit && p.hit[b]) return;
   const int len = p.seq_lens[b];
-  const int t0 = tile * kScoreTile;
+  const int t0 = tile * TILE;
   if (t0 >= len) return;
-  const int tl = min(kScoreTile, len - t0);
+  const int tl = min(TILE, len - t0);
 
   const int tid = threadIdx.x;
   const int j = tid % LPR;
@@ -59,145 +72,188 @@ __global__ __launch_bounds__(256) void score_pass1_kernel(ScoreParams p) {
   const int toff = rg / Hkv;
   const int NH = Hkv * GS;                   // heads this work-group scores
 
+  const char* kbase;
   if constexpr (PAGED) {
+    // byte offset of every page this tile touches, relative to the pool
     const int ps_log2 = p.ps_log2;
     const int npg = ((tl - 1) >> ps_log2) + 1;
     const int* pt = p.page_table + (size_t)b * p.pt_stride + (t0 >> ps_log2);
-    for (int i = tid; i < npg; i += 256) s_page[i] = pt[i];
+    for (int i = tid; i < npg; i += 256)
+      s_page[i] = ((long long)pt[i] << ps_log2) * Hkv * ROWB;
+    kbase = (const char*)p.k;
     __syncthreads();
+  } else {
+    kbase = (const char*)p.k + ((size_t)b * p.max_len + t0) * Hkv * ROWB;
   }
 
-  // query slice of this lane's KV-head group: 8 words (bf16 pairs or fp32)
-  uint32_t qw[GS][8];
+  auto row_ptr = [&](int t) -> const char* {
+    if constexpr (PAGED) {
+      const int ps_log2 = p.ps_log2;
+      return kbase + s_page[t >> ps_log2] +
+             (uint32_t)(((((t0 + t) & ((1 << ps_log2) - 1)) * Hkv) + kvh) * ROWB);
+    } else {
+      return kbase + (uint32_t)((t * Hkv + kvh) * ROWB);
+    }
+  };
+  const int n_iter = active ? (tl - toff + TPI - 1) / TPI : 0;
+  // full tiles with every row group busy need no per-row guards
+  const bool full = (tl == TILE) && (TPI * Hkv == RG) && (TILE % (TPI * U) == 0);
+
+  auto load_batch = [&](int i0, uint4 (&kc)[U][CPL], bool guard) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      if (!guard || i0 + u < n_iter) {
+        const char* rp = row_ptr(toff + (i0 + u) * TPI) + j * 16;
+#pragma unroll
+        for (int c = 0; c < CPL; ++c) kc[u][c] = ld16_nt(rp + c * 16 * LPR);
+      } else {
+#pragma unroll
+        for (int c = 0; c < CPL; ++c) kc[u][c] = make_uint4(0, 0, 0, 0);
+      }
+    }
+  };
+
+  uint4 bufA[U][CPL], bufB[U][CPL];
+  if (n_iter > 0) load_batch(0, bufA, !full);
+
+  // query slice of this lane's KV-head group (bf16 pairs or fp32 words)
+  uint32_t qw[GS][WPL];
 #pragma unroll
   for (int hh = 0; hh < GS; ++hh) {
     const int head = kvh * p.G + slice * GS + hh;
-    const char* qb = (const char*)p.q + ((size_t)b * p.Hq + (active ? head : 0)) * ROWB;
-    uint4 c0 = ld16(qb + j * 16);
-    uint4 c1 = ld16(qb + ROWB / 2 + j * 16);
-    qw[hh][0] = c0.x; qw[hh][1] = c0.y; qw[hh][2] = c0.z; qw[hh][3] = c0.w;
-    qw[hh][4] = c1.x; qw[hh][5] = c1.y; qw[hh][6] = c1.z; qw[hh][7] = c1.w;
-  }
-
-  const char* kbase = (const char*)p.k;
-  const int n_iter = active ? (tl - toff + TPI - 1) / TPI : 0;
-  for (int i0 = 0; i0 < n_iter; i0 += U) {
-    uint4 kc[U][2];
+    const char* qb = (const char*)p.q + ((size_t)b * p.Hq + (active ? head : 0)) * ROWB + j * 16;
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int t = toff + (i0 + u) * TPI;
-      if (i0 + u < n_iter) {
-        size_t row;
-        if constexpr (PAGED) {
-          const int tok = t0 + t;
-          const int pg = s_page[t >> p.ps_log2];
-          row = ((((size_t)pg << p.ps_log2) + (tok & ((1 << p.ps_log2) - 1))) * Hkv + kvh);
-        } else {
-          row = (((size_t)b * p.max_len + t0 + t) * Hkv + kvh);
-        }
-        const char* rp = kbase + row * ROWB;
-        kc[u][0] = ld16_nt(rp + j * 16);
-        kc[u][1] = ld16_nt(rp + ROWB / 2 + j * 16);
-      } else {
-        kc[u][0] = make_uint4(0, 0, 0, 0);
-        kc[u][1] = make_uint4(0, 0, 0, 0);
-      }
+    for (int c = 0; c < CPL; ++c) {
+      const uint4 v = ld16(qb + c * 16 * LPR);
+      qw[hh][4 * c + 0] = v.x; qw[hh][4 * c + 1] = v.y; qw[hh][4 * c + 2] = v.z; qw[hh][4 * c + 3] = v.w;
     }
+  }
+  const float scale2 = p.scale2;
+
+  auto compute_batch = [&](int i0, const uint4 (&kc)[U][CPL], bool guard) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const uint32_t kw[8] = {kc[u][0].x, kc[u][0].y, kc[u][0].z, kc[u][0].w,
-                              kc[u][1].x, kc[u][1].y, kc[u][1].z, kc[u][1].w};
+      uint32_t kw[WPL];
+#pragma unroll
+      for (int c = 0; c < CPL; ++c) {
+        kw[4 * c + 0] = kc[u][c].x; kw[4 * c + 1] = kc[u][c].y;
+        kw[4 * c + 2] = kc[u][c].z; kw[4 * c + 3] = kc[u][c].w;
+      }
       float acc[GS];
 #pragma unroll
       for (int hh = 0; hh < GS; ++hh) {
         float a = 0.f;
         if constexpr (DT == 1) {
 #pragma unroll
-          for (int w = 0; w < 8; ++w) a = dot2_bf16(kw[w], qw[hh][w], a);
+          for (int w = 0; w < WPL; ++w) a = dot2_bf16(kw[w], qw[hh][w], a);
         } else {
 #pragma unroll
-          for (int w = 0; w < 8; ++w) a = fmaf(__uint_as_float(kw[w]), __uint_as_float(qw[hh][w]), a);
+          for (int w = 0; w < WPL; ++w) a = fmaf(__uint_as_float(kw[w]), __uint_as_float(qw[hh][w]), a);
         }
         acc[hh] = group_sum<LPR>(a);
       }
       const int t = toff + (i0 + u) * TPI;
-      if (i0 + u < n_iter) {
+      // lane j of the row group stores the logits of heads j, j+LPR, ...
 #pragma unroll
-        for (int hh = 0; hh < GS; ++hh)
-          if ((hh % LPR) == j) s_log[(kvh * GS + hh) * kScoreTile + t] = acc[hh] * p.scale2;
+      for (int r = 0; r < NW; ++r) {
+        float v = acc[0];
+#pragma unroll
+        for (int hh = 1; hh < GS; ++hh) v = (r * LPR + j == hh) ? acc[hh] : v;
+        const int hh = r * LPR + j;
+        if ((!guard || i0 + u < n_iter) && hh < GS) s_log[(kvh * GS + hh) * LS + t] = v * scale2;
       }
+    }
+  };
+
+  if (full) {
+    for (int i0 = 0; i0 < n_iter; i0 += 2 * U) {
+      if (i0 + U < n_iter) load_batch(i0 + U, bufB, false);
+      compute_batch(i0, bufA, false);
+      if (i0 + 2 * U < n_iter) load_batch(i0 + 2 * U, bufA, false);
+      if (i0 + U < n_iter) compute_batch(i0 + U, bufB, false);
+    }
+  } else {
+    for (int i0 = 0; i0 < n_iter; i0 += 2 * U) {
+      load_batch(i0 + U, bufB, true);
+      compute_batch(i0, bufA, true);
+      load_batch(i0 + 2 * U, bufA, true);
+      compute_batch(i0 + U, bufB, true);
     }
   }
   __syncthreads();
 
-  // logits -> global, coalesced float4 per head row (padding past tl is never read)
-  for (int i = tid; i < NH * (kScoreTile / 4); i += 256) {
-    const int hl = i / (kScoreTile / 4);
-    const int t = (i % (kScoreTile / 4)) * 4;
+  // logits -> global, coalesced per head row (padding past tl is never read)
+  for (int i = tid; i < NH * (TILE / 4); i += 256) {
+    const int hl = i / (TILE / 4);
+    const int t = (i % (TILE / 4)) * 4;
     if (t < tl) {
       const int head = (hl / GS) * p.G + slice * GS + (hl % GS);
-      float4 v = *reinterpret_cast<const float4*>(&s_log[hl * kScoreTile + t]);
-      *reinterpret_cast<float4*>(p.logits + ((size_t)b * p.Hq + head) * p.Lpad + t0 + t) = v;
+      const float* sp = &s_log[hl * LS + t];
+      *reinterpret_cast<float4*>(p.logits + ((size_t)b * p.Hq + head) * p.Lpad + t0 + t) =
+          make_float4(sp[0], sp[1], sp[2], sp[3]);
     }
   }
 
-  // per (head, tile): max and sum of exp2
+  // per (head, tile): max and sum of exp2, consumed by the lse kernel
+  constexpr int EPT = TILE / 64;
   const int lane = tid & 63, wv = tid >> 6;
   for (int hl = wv; hl < NH; hl += 4) {
-    float x[4];
+    float x[EPT];
     float m = -INFINITY;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int t = lane * 4 + e;
-      x[e] = (t < tl) ? s_log[hl * kScoreTile + t] : -INFINITY;
+    for (int e = 0; e < EPT; ++e) {
+      const int t = e * 64 + lane;
+      x[e] = (t < tl) ? s_log[hl * LS + t] : -INFINITY;
       m = fmaxf(m, x[e]);
     }
     m = wave_max(m);
     float l = 0.f;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) l += (lane * 4 + e < tl) ? exp2f(x[e] - m) : 0.f;
+    for (int e = 0; e < EPT; ++e) l += (e * 64 + lane < tl) ? ex2(x[e] - m) : 0.f;
     l = wave_sum(l);
     if (lane == 0) {
       const int head = (hl / GS) * p.G + slice * GS + (hl % GS);
       p.partials[((size_t)b * p.Hq + head) * p.ntiles + tile] = make_float2(m, l);
     }
   }
-
-  // the last work-group of this sequence folds the partials into lse[b][:]
-  __threadfence();
-  __syncthreads();
-  if (tid == 0) {
-    const int nt = (len + kScoreTile - 1) / kScoreTile;
-    const uint32_t prev = atomicAdd(p.ctrl + (size_t)b * kCtrlStride + kCtlCntScore, 1u);
-    s_last = (prev == (uint32_t)(nt * p.nslices - 1));
-  }
-  __syncthreads();
-  if (!s_last) return;
-  __threadfence();
-  const int nt = (len + kScoreTile - 1) / kScoreTile;
-  for (int h = wv; h < p.Hq; h += 4) {
-    const unsigned long long* pp =
-        reinterpret_cast<const unsigned long long*>(p.partials + ((size_t)b * p.Hq + h) * p.ntiles);
-    float M = -INFINITY, L = 0.f;
-    for (int t = lane; t < nt; t += 64) {
-      const unsigned long long w = __hip_atomic_load(pp + t, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      const float tm = __uint_as_float((uint32_t)w);
-      const float tlv = __uint_as_float((uint32_t)(w >> 32));
-      const float nm = fmaxf(M, tm);
-      L = L * exp2f(M - nm) + tlv * exp2f(tm - nm);
-      M = nm;
-    }
-    const float Mw = wave_max(M);
-    const float Lw = wave_sum(M == -INFINITY ? 0.f : L * exp2f(M - Mw));
-    if (lane == 0) p.lse[(size_t)b * p.Hq + h] = Mw + log2f(Lw);
-  }
 }
 
+// Each (sequence, head): fold the tile partials into the log-sum-exp (base 2)
+// over all N tokens. One wave per (head, sequence); all loads issued at once.
+__global__ __launch_bounds__(64) void lse_kernel(LseParams p) {
+  const int h = blockIdx.x, b = blockIdx.y, lane = threadIdx.x;
+  if (p.hit && p.hit[b]) return;
+  const int len = p.seq_lens[b];
+  if (len <= 0) return;
+  const int nt = (len + p.tile - 1) / p.tile;
+  const float2* pp = p.partials + ((size_t)b * p.Hq + h) * p.ntiles;
+  float M = -INFINITY, L = 0.f;
+  for (int t0 = 0; t0 < nt; t0 += 64 * 16) {
+    float2 pr[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int t = t0 + i * 64 + lane;
+      pr[i] = t < nt ? pp[t] : make_float2(-INFINITY, 0.f);
+    }
+    float m = M;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) m = fmaxf(m, pr[i].x);
+    float l = (M == -INFINITY) ? 0.f : L * ex2(M - m);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) l += (pr[i].y > 0.f) ? pr[i].y * ex2(pr[i].x - m) : 0.f;
+    M = m;
+    L = l;
+  }
+  const float Mw = wave_max(M);
+  const float Lw = wave_sum(M == -INFINITY ? 0.f : L * ex2(M - Mw));
+  if (lane == 0) p.lse[(size_t)b * p.Hq + h] = Mw + log2f(Lw);
+}
+
+// votes: kVoteTile tokens per work-group, two per thread; all logit loads of a
+// thread are issued before any exp2.
 __global__ __launch_bounds__(256) void votes_kernel(VoteParams p) {
   __shared__ float s_lse[kMaxQHeads];
-  __shared__ uint32_t s_hist[2048];
-  __shared__ uint32_t s_sh[260];
-  __shared__ int s_last;
+  __shared__ uint32_t s_hist[1 << kHist0Bits];
 
   const int b = blockIdx.y;
   if (p.hit && p.hit[b]) return;
@@ -205,65 +261,67 @@ __global__ __launch_bounds__(256) void votes_kernel(VoteParams p) {
   const int start = blockIdx.x * kVoteTile;
   if (start >= len) return;
   const int tid = threadIdx.x;
-  uint32_t* ctrl = p.ctrl + (size_t)b * kCtrlStride;
-
   for (int h = tid; h < p.Hq; h += 256) s_lse[h] = p.lse[(size_t)b * p.Hq + h];
   if (p.do_hist)
-    for (int i = tid; i < 2048; i += 256) s_hist[i] = 0u;
+    for (int i = tid; i < (1 << kHist0Bits); i += 256) s_hist[i] = 0u;
   __syncthreads();
 
-  const int j0 = start + tid * 4;
-  float v0 = 0.f, v1 = 0.f, v2 = 0.f, v3 = 0.f;
+  const int j0 = start + tid * 2;
   if (j0 < len) {
     const float* lg = p.logits + (size_t)b * p.Hq * p.Lpad + j0;
-    for (int h = 0; h < p.Hq; ++h) {
-      const float4 s = ldf4(lg + (size_t)h * p.Lpad);
-      const float c = s_lse[h];
-      v0 += exp2f(s.x - c);
-      v1 += exp2f(s.y - c);
-      v2 += exp2f(s.z - c);
-      v3 += exp2f(s.w - c);
+    float v0 = 0.f, v1 = 0.f;
+    constexpr int HB = 16;
+    for (int h0 = 0; h0 < p.Hq; h0 += HB) {
+      float2 sv[HB];
+#pragma unroll
+      for (int u = 0; u < HB; ++u)
+        sv[u] = (h0 + u < p.Hq) ? *reinterpret_cast<const float2*>(lg + (size_t)(h0 + u) * p.Lpad)
+                                : make_float2(-INFINITY, -INFINITY);
+#pragma unroll
+      for (int u = 0; u < HB; ++u) {
+        if (h0 + u < p.Hq) {
+          const float c = s_lse[h0 + u];
+          v0 += ex2(sv[u].x - c);
+          v1 += ex2(sv[u].y - c);
+        }
+      }
     }
     float* vo = p.votes + (size_t)b * p.vote_stride + j0;
-    const float vv[4] = {v0, v1, v2, v3};
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      if (j0 + e < len) {
-        vo[e] = vv[e];
-        if (p.do_hist) atomicAdd(&s_hist[float_key(vv[e]) >> 21], 1u);
-      }
+    vo[0] = v0;
+    if (p.do_hist) atomicAdd(&s_hist[float_key(v0) >> (32 - kHist0Bits)], 1u);
+    if (j0 + 1 < len) {
+      vo[1] = v1;
+      if (p.do_hist) atomicAdd(&s_hist[float_key(v1) >> (32 - kHist0Bits)], 1u);
     }
   }
   if (!p.do_hist) return;
   __syncthreads();
-  for (int i = tid; i < 2048; i += 256)
-    if (s_hist[i]) atomicAdd(ctrl + kCtlHist0 + i, s_hist[i]);
-  __threadfence();
-  __syncthreads();
-  if (tid == 0) {
-    const int nb = (len + kVoteTile - 1) / kVoteTile;
-    const uint32_t prev = atomicAdd(ctrl + kCtlCntVote, 1u);
-    s_last = (prev == (uint32_t)(nb - 1));
-  }
-  __syncthreads();
-  if (!s_last) return;
-  __threadfence();
-  const uint32_t need = (uint32_t)min(p.k, len);
-  resolve_bin(ctrl + kCtlHist0, 2048, need, s_sh);
-  if (tid == 0) {
-    ctrl[kCtlPrefix] = s_sh[256];
-    ctrl[kCtlNeed] = s_sh[257];
-  }
+  uint32_t* gh = p.ctrl + (size_t)b * kCtrlStride + kCtlHist0;
+  for (int i = tid; i < (1 << kHist0Bits); i += 256)
+    if (s_hist[i]) atomicAdd(gh + i, s_hist[i]);
 }
 
 // ---- launchers ---------------------------------------------------------------
 
-template <int DT, int D, bool PAGED>
+// lanes per row (32 bytes each): 8 for bf16 d=128, 4 for bf16 d=64, 8/16 for
+// fp32. Fewer lanes per row would save DPP steps but hold twice the query
+// registers, which costs more occupancy than it saves (measured).
+template <int DT, int D>
+constexpr int score_lpr() {
+  return (D * (DT ? 2 : 4)) / 32;
+}
+
+template <int DT, int D, bool PAGED, int TILE>
 static hipError_t launch_pass1_gs(const ScoreParams& p, hipStream_t s) {
   dim3 grid(p.ntiles, p.B * p.nslices);
-  const size_t shmem = (size_t)p.Hkv * p.GS * kScoreTile * sizeof(float);
+  const size_t shmem = (size_t)p.Hkv * p.GS * (TILE + 1) * sizeof(float);
+#ifdef TS_SCORE_LPR
+  constexpr int LPR = TS_SCORE_LPR;
+#else
+  constexpr int LPR = score_lpr<DT, D>();
+#endif
   switch (p.GS) {
-#define TS_GS(n) case n: hipLaunchKernelGGL((score_pass1_kernel<DT, D, n, PAGED>), grid, dim3(256), shmem, s, p); break;
+#define TS_GS(n) case n: hipLaunchKernelGGL((score_pass1_kernel<DT, D, n, PAGED, TILE, LPR>), grid, dim3(256), shmem, s, p); break;
     TS_GS(1) TS_GS(2) TS_GS(3) TS_GS(4) TS_GS(5) TS_GS(6) TS_GS(7) TS_GS(8)
 #undef TS_GS
     default: return hipErrorInvalidValue;
@@ -271,12 +329,24 @@ static hipError_t launch_pass1_gs(const ScoreParams& p, hipStream_t s) {
   return hipGetLastError();
 }
 
-hipError_t launch_score_pass1(int dtype, int d, bool paged, const ScoreParams& p, hipStream_t s) {
-  if (dtype == 1 && d == 128) return paged ? launch_pass1_gs<1, 128, true>(p, s) : launch_pass1_gs<1, 128, false>(p, s);
-  if (dtype == 1 && d == 64) return paged ? launch_pass1_gs<1, 64, true>(p, s) : launch_pass1_gs<1, 64, false>(p, s);
-  if (dtype == 0 && d == 128) return paged ? launch_pass1_gs<0, 128, true>(p, s) : launch_pass1_gs<0, 128, false>(p, s);
-  if (dtype == 0 && d == 64) return paged ? launch_pass1_gs<0, 64, true>(p, s) : launch_pass1_gs<0, 64, false>(p, s);
+template <int DT, int D, bool PAGED>
+static hipError_t launch_pass1_tile(const ScoreParams& p, hipStream_t s) {
+  if (p.tile == 128) return launch_pass1_gs<DT, D, PAGED, 128>(p, s);
+  if (p.tile == 256) return launch_pass1_gs<DT, D, PAGED, 256>(p, s);
   return hipErrorInvalidValue;
+}
+
+hipError_t launch_score_pass1(int dtype, int d, bool paged, const ScoreParams& p, hipStream_t s) {
+  if (dtype == 1 && d == 128) return paged ? launch_pass1_tile<1, 128, true>(p, s) : launch_pass1_tile<1, 128, false>(p, s);
+  if (dtype == 1 && d == 64) return paged ? launch_pass1_tile<1, 64, true>(p, s) : launch_pass1_tile<1, 64, false>(p, s);
+  if (dtype == 0 && d == 128) return paged ? launch_pass1_tile<0, 128, true>(p, s) : launch_pass1_tile<0, 128, false>(p, s);
+  if (dtype == 0 && d == 64) return paged ? launch_pass1_tile<0, 64, true>(p, s) : launch_pass1_tile<0, 64, false>(p, s);
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_lse(const LseParams& p, hipStream_t s) {
+  hipLaunchKernelGGL(lse_kernel, dim3(p.Hq, p.B), dim3(64), 0, s, p);
+  return hipGetLastError();
 }
 
 hipError_t launch_votes(const VoteParams& p, int grid_x, hipStream_t s) {

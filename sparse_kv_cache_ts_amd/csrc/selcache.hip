@@ -19,10 +19,6 @@ __global__ __launch_bounds__(256) void prologue_kernel(PrologueParams p) {
     uint32_t* c = p.ctrl + (size_t)r * kCtrlStride;
     for (int i = tid; i < kCtrlStride; i += 256) c[i] = 0u;
   }
-  if (p.flags && r < p.rows) {
-    unsigned long long* f = p.flags + (size_t)r * p.max_chunks;
-    for (int i = tid; i < p.max_chunks; i += 256) f[i] = 0ull;
-  }
   if (p.cache.prev_q == nullptr || r >= p.B) return;
 
   const SelCacheDev& c = p.cache;
@@ -31,15 +27,47 @@ __global__ __launch_bounds__(256) void prologue_kernel(PrologueParams p) {
   const int n = c.Hq * c.d;
   double dot = 0.0, nq = 0.0, np = 0.0;
   if (can) {
+    // 8 consecutive elements per thread and step; every load of a step is
+    // issued before the fp64 accumulation (n = Hq*d is a multiple of 64)
     const float* pq = c.prev_q + (size_t)r * n;
-    for (int i = tid; i < n; i += 256) {
-      float qv;
-      if (p.dtype == 1) qv = __uint_as_float((uint32_t)((const uint16_t*)p.q)[(size_t)r * n + i] << 16);
-      else qv = ((const float*)p.q)[(size_t)r * n + i];
-      const double a = (double)qv, b = (double)pq[i];
-      dot += a * b;
-      nq += a * a;
-      np += b * b;
+    const int nch = n / 8;
+    for (int c0 = tid; c0 < nch; c0 += 256 * 4) {
+      float qv[4][8], pv[4][8];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int ch = c0 + u * 256;
+        if (ch < nch) {
+          if (p.dtype == 1) {
+            const uint4 w = ld16((const uint16_t*)p.q + (size_t)r * n + ch * 8);
+            const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              qv[u][2 * e] = bf16_lo(ws[e]);
+              qv[u][2 * e + 1] = bf16_hi(ws[e]);
+            }
+          } else {
+            const float4 a = ldf4((const float*)p.q + (size_t)r * n + ch * 8);
+            const float4 b = ldf4((const float*)p.q + (size_t)r * n + ch * 8 + 4);
+            qv[u][0] = a.x; qv[u][1] = a.y; qv[u][2] = a.z; qv[u][3] = a.w;
+            qv[u][4] = b.x; qv[u][5] = b.y; qv[u][6] = b.z; qv[u][7] = b.w;
+          }
+          const float4 a = ldf4(pq + ch * 8), b = ldf4(pq + ch * 8 + 4);
+          pv[u][0] = a.x; pv[u][1] = a.y; pv[u][2] = a.z; pv[u][3] = a.w;
+          pv[u][4] = b.x; pv[u][5] = b.y; pv[u][6] = b.z; pv[u][7] = b.w;
+        } else {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) { qv[u][e] = 0.f; pv[u][e] = 0.f; }
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const double a = (double)qv[u][e], b = (double)pv[u][e];
+          dot += a * b;
+          nq += a * a;
+          np += b * b;
+        }
     }
   }
   dot = wave_sum_d(dot);

@@ -5,17 +5,20 @@
 // votes of a row; a tie at the k-th vote goes to the lower token index; the
 // indices come out ascending and are padded with -1 to k.
 //
-// Radix select on the order-preserving 32-bit image of each float, in three
-// digit passes over the row: bits 31..21, 20..10 and 9..0. Each pass is a
-// multi-work-group histogram (LDS, then device atomics) whose last
-// work-group (device-scope counter) finds the bin that holds the k-th
-// largest key, so after the third pass the threshold key T and the number of
-// ties at T still to take are exact. The first histogram is built inside the
-// vote kernel. Compaction then keeps every key above T and the first `need`
-// keys equal to T in index order: work-groups take chunk tickets in dispatch
-// order, publish (above, equal) counts and look back over their predecessors
-// (a decoupled look-back scan), then write their picks at ordered positions,
-// so the output is already ascending and no sort is needed.
+// Keys are the order-preserving 32-bit images of the floats. Three steps,
+// none of which waits on another work-group inside a kernel (device-scope
+// fences cost far more than a kernel boundary on this multi-XCD part):
+//   1. histogram of the top 12 key bits over the row (built by the vote
+//      kernel on the decode path, by topk_hist0_kernel otherwise);
+//   2. partition: every work-group finds the bin b0 that holds the k-th
+//      largest key from the finished histogram, sets the selection bits of
+//      its keys above b0 in a bitmap (one ballot per 64 keys), and appends the
+//      keys inside b0 to a short candidate list;
+//   3. finalize, one work-group per row: an exact radix select among the
+//      candidates (in LDS; a rescan of the row if the list overflowed) on the
+//      remaining 20 key bits, then on the index among exact ties so the lower
+//      indices win, sets their bits, and turns the bitmap into ascending
+//      indices with popcounts and a block scan.
 #include "ts_device.h"
 
 namespace ts {
@@ -24,183 +27,343 @@ __device__ __forceinline__ int row_length(const TopkParams& p, int r) {
   return p.row_lens ? p.row_lens[r] : p.row_len_base + r;
 }
 
-// PASS 0: histogram of bits 31..21 over the whole row (standalone top-k; the
-// decode path builds it in the vote kernel). PASS 1: bits 20..10 of keys whose
-// top 11 bits equal the pass-0 bin. PASS 2: bits 9..0 of keys whose top 22
-// bits equal the pass-1 prefix.
-template <int PASS>
-__global__ __launch_bounds__(256) void topk_hist_kernel(TopkParams p) {
-  constexpr int NB = (PASS == 2) ? 1024 : 2048;
-  constexpr int CNT = (PASS == 0) ? kCtlCntVote : (PASS == 1) ? kCtlCntHist1 : kCtlCntHist2;
-  constexpr int HOFF = (PASS == 0) ? kCtlHist0 : (PASS == 1) ? kCtlHist1 : kCtlHist2;
-  __shared__ uint32_t s_hist[2048];
-  __shared__ uint32_t s_sh[260];
-  __shared__ int s_last;
+// Exclusive prefix sum of one uint32 per thread over an NT-thread block;
+// `sh` holds NT/64 words. Returns the prefix; *total gets the block sum.
+template <int NT>
+__device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, uint32_t* sh, uint32_t* total) {
+  constexpr int NWAVE = NT / 64;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  uint32_t x = v;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const uint32_t y = __shfl_up(x, o);
+    if (lane >= o) x += y;
+  }
+  if (lane == 63) sh[w] = x;
+  __syncthreads();
+  uint32_t base = 0, tot = 0;
+#pragma unroll
+  for (int i = 0; i < NWAVE; ++i) {
+    const uint32_t s = sh[i];
+    if (i < w) base += s;
+    tot += s;
+  }
+  __syncthreads();
+  *total = tot;
+  return base + x - v;
+}
 
+// ---- step 1 (standalone top-k): histogram of the top 12 key bits ------------
+__global__ __launch_bounds__(256) void topk_hist0_kernel(TopkParams p) {
+  constexpr int PER = kTopkChunk / 256;
+  __shared__ uint32_t s_hist[1 << kHist0Bits];
   const int r = blockIdx.y;
   if (p.hit && p.hit[r]) return;
   const int len = row_length(p, r);
   const int start = blockIdx.x * kTopkChunk;
   if (start >= len) return;
   const int tid = threadIdx.x;
-  uint32_t* ctrl = p.ctrl + (size_t)r * kCtrlStride;
-  const uint32_t prefix = (PASS == 0) ? 0u : ctrl[kCtlPrefix];
-  const uint32_t need = (PASS == 0) ? (uint32_t)min(p.k, len) : ctrl[kCtlNeed];
-
-  for (int i = tid; i < NB; i += 256) s_hist[i] = 0u;
-  __syncthreads();
+  for (int i = tid; i < (1 << kHist0Bits); i += 256) s_hist[i] = 0u;
   const float* row = p.votes + (size_t)r * p.row_stride;
-#pragma unroll 4
-  for (int i = 0; i < kTopkChunk / 256; ++i) {
+  float v[PER];
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
     const int e = start + i * 256 + tid;
-    if (e < len) {
-      const uint32_t key = float_key(row[e]);
-      if (PASS == 0) {
-        atomicAdd(&s_hist[key >> 21], 1u);
-      } else if (PASS == 1) {
-        if ((key >> 21) == prefix) atomicAdd(&s_hist[(key >> 10) & 2047u], 1u);
-      } else {
-        if ((key >> 10) == prefix) atomicAdd(&s_hist[key & 1023u], 1u);
-      }
+    v[i] = (e < len) ? row[e] : 0.f;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < PER; ++i)
+    if (start + i * 256 + tid < len) atomicAdd(&s_hist[float_key(v[i]) >> (32 - kHist0Bits)], 1u);
+  __syncthreads();
+  uint32_t* gh = p.ctrl + (size_t)r * kCtrlStride + kCtlHist0;
+  for (int i = tid; i < (1 << kHist0Bits); i += 256)
+    if (s_hist[i]) atomicAdd(gh + i, s_hist[i]);
+}
+
+// ---- step 2: partition into selected bits / threshold-bin candidates --------
+__global__ __launch_bounds__(256) void topk_partition_kernel(TopkParams p) {
+  constexpr int PER = kTopkChunk / 256;           // 16 keys per thread
+  constexpr int SHIFT = 32 - kHist0Bits;
+  __shared__ uint32_t s_sh[8];
+  __shared__ uint32_t s_base;
+  const int r = blockIdx.y;
+  if (p.hit && p.hit[r]) return;
+  const int len = row_length(p, r);
+  const int start = blockIdx.x * kTopkChunk;
+  if (start >= len) return;
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const uint32_t k_eff = (uint32_t)min(p.k, len);
+  uint32_t* ctrl = p.ctrl + (size_t)r * kCtrlStride;
+
+  // the row's keys of this chunk, coalesced: key i of thread t is start + i*256 + t
+  const float* row = p.votes + (size_t)r * p.row_stride;
+  float v[PER];
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    const int e = start + i * 256 + tid;
+    v[i] = (e < len) ? row[e] : 0.f;
+  }
+  // the bin b0 that holds the k-th largest key (16 of the 4096 bins per thread)
+  uint32_t c[16];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const uint4 a = ld16(ctrl + kCtlHist0 + tid * 16 + 4 * q);
+    c[4 * q] = a.x; c[4 * q + 1] = a.y; c[4 * q + 2] = a.z; c[4 * q + 3] = a.w;
+  }
+  const uint2 rb = resolve_counts<16>(c, k_eff, s_sh);
+  const uint32_t b0 = rb.x, need = rb.y;
+  const uint32_t cnt_b0 = ctrl[kCtlHist0 + b0];
+  const bool whole = (need == cnt_b0);     // the whole bin is selected: no candidates
+  if (blockIdx.x == 0 && tid == 0) {
+    ctrl[kCtlPrefix] = b0;
+    ctrl[kCtlNeed] = whole ? 0u : need;
+  }
+
+  uint32_t* bm = p.bitmap + (size_t)r * p.bm_stride + start / 32;
+  uint32_t ncand = 0;
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    const int e = start + i * 256 + tid;
+    const uint32_t key = float_key(v[i]);
+    const uint32_t bin = key >> SHIFT;
+    const bool in = e < len;
+    const bool sel = in && (whole ? bin >= b0 : bin > b0);
+    ncand += (in && !whole && bin == b0) ? 1u : 0u;
+    const unsigned long long m = __ballot(sel);
+    if (lane == 0)
+      *reinterpret_cast<uint2*>(bm + i * 8 + wv * 2) = make_uint2((uint32_t)m, (uint32_t)(m >> 32));
+  }
+  if (whole) return;
+  uint32_t total;
+  const uint32_t off = block_excl_scan<256>(ncand, s_sh, &total);
+  if (tid == 0) s_base = total ? atomicAdd(ctrl + kCtlCandCount, total) : 0u;
+  __syncthreads();
+  if (ncand == 0) return;
+  uint2* cand = p.cand + (size_t)r * kCandCap;
+  uint32_t pos = s_base + off;
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    const int e = start + i * 256 + tid;
+    const uint32_t key = float_key(v[i]);
+    if (e < len && (key >> SHIFT) == b0) {
+      if (pos < (uint32_t)kCandCap) cand[pos] = make_uint2(key, (uint32_t)e);
+      ++pos;
     }
   }
+}
+
+// ---- step 3: exact select among the candidates, then bitmap -> indices ------
+
+// (key, index) lists the finalize work-group walks: the candidates staged in
+// LDS, or the whole row (keys recomputed) after a candidate overflow.
+struct LdsList {
+  const uint32_t* key;
+  const uint32_t* idx;
+  int n;
+  __device__ int size() const { return n; }
+  __device__ uint2 get(int i) const { return make_uint2(key[i], idx[i]); }
+};
+struct GlobalList {
+  const uint2* c;
+  int n;
+  __device__ int size() const { return n; }
+  __device__ uint2 get(int i) const { return c[i]; }
+};
+struct RowList {
+  const float* row;
+  int n;
+  __device__ int size() const { return n; }
+  __device__ uint2 get(int i) const { return make_uint2(float_key(row[i]), (uint32_t)i); }
+};
+
+// Among the list elements whose top 12 key bits equal b0, choose the `need`
+// largest keys (lower index first among equal keys) and set their bits in
+// `bm` (LDS or global).
+template <class List>
+__device__ void select_in_bin(const List& L, uint32_t b0, uint32_t need, uint32_t* bm,
+                              uint32_t* s_hist, uint32_t* s_sh) {
+  constexpr int NT = kFinalThreads;
+  const int tid = threadIdx.x;
+  const int n = L.size();
+  const uint32_t pre20 = b0;                       // key >> 20
+  // pass A: key bits 19..10
+  for (int i = tid; i < 1024; i += NT) s_hist[i] = 0u;
   __syncthreads();
-  uint32_t* gh = ctrl + HOFF;
-  for (int i = tid; i < NB; i += 256)
-    if (s_hist[i]) atomicAdd(gh + i, s_hist[i]);
-  __threadfence();
-  __syncthreads();
-  if (tid == 0) {
-    const int nchunks = (len + kTopkChunk - 1) / kTopkChunk;
-    const uint32_t prev = atomicAdd(ctrl + CNT, 1u);
-    s_last = (prev == (uint32_t)(nchunks - 1));
+  for (int i = tid; i < n; i += NT) {
+    const uint2 e = L.get(i);
+    if ((e.x >> 20) == pre20) atomicAdd(&s_hist[(e.x >> 10) & 1023u], 1u);
   }
   __syncthreads();
-  if (!s_last) return;
-  __threadfence();
-  resolve_bin(gh, NB, need, s_sh);
-  if (tid == 0) {
-    ctrl[kCtlPrefix] = (PASS == 0) ? s_sh[256] : ((prefix << (PASS == 1 ? 11 : 10)) | s_sh[256]);
-    ctrl[kCtlNeed] = s_sh[257];
+  const uint2 ra = resolve_lds<1024 / NT, NT>(s_hist, need, s_sh);
+  const uint32_t pre10 = (pre20 << 10) | ra.x;     // key >> 10
+  // pass B: key bits 9..0
+  for (int i = tid; i < 1024; i += NT) s_hist[i] = 0u;
+  __syncthreads();
+  for (int i = tid; i < n; i += NT) {
+    const uint2 e = L.get(i);
+    if ((e.x >> 10) == pre10) atomicAdd(&s_hist[e.x & 1023u], 1u);
+  }
+  __syncthreads();
+  const uint2 rbb = resolve_lds<1024 / NT, NT>(s_hist, ra.y, s_sh);
+  const uint32_t T = (pre10 << 10) | rbb.x;        // the k-th largest key
+  const uint32_t need_t = rbb.y;                   // ties at T to take
+  const uint32_t ntie = s_hist[rbb.x];
+  __syncthreads();
+  // among ties, the need_t smallest indices are the need_t largest values of
+  // ~index: three more digit passes (bits 31..21, 20..10, 9..0 of ~index)
+  uint32_t imax = 0xffffffffu;
+  if (ntie > need_t) {
+    uint32_t prefix = 0, nd = need_t;
+#pragma unroll
+    for (int ps = 0; ps < 3; ++ps) {
+      const int shift = (ps == 0) ? 21 : (ps == 1) ? 10 : 0;
+      const uint32_t mask = (ps == 2) ? 1023u : 2047u;
+      for (int i = tid; i < 2048; i += NT) s_hist[i] = 0u;
+      __syncthreads();
+      for (int i = tid; i < n; i += NT) {
+        const uint2 e = L.get(i);
+        const uint32_t ni = ~e.y;
+        const bool match = (e.x == T) && (ps == 0 || (ni >> (shift + (ps == 1 ? 11 : 10))) == prefix);
+        if (match) atomicAdd(&s_hist[(ni >> shift) & mask], 1u);
+      }
+      __syncthreads();
+      const uint2 rr = (ps < 2) ? resolve_lds<2048 / NT, NT>(s_hist, nd, s_sh)
+                                : resolve_lds<1024 / NT, NT>(s_hist, nd, s_sh);
+      prefix = (ps == 0) ? rr.x : ((prefix << (ps == 1 ? 11 : 10)) | rr.x);
+      nd = rr.y;
+    }
+    imax = ~prefix;                                 // ties with index <= imax are taken
+  }
+  for (int i = tid; i < n; i += NT) {
+    const uint2 e = L.get(i);
+    if ((e.x >> 20) == pre20 && (e.x > T || (e.x == T && e.y <= imax)))
+      atomicOr(bm + (e.y >> 5), 1u << (e.y & 31));
+  }
+  __syncthreads();
+}
+
+template <class List>
+__device__ __forceinline__ void select_any(const TopkParams& p, int r, int len, uint32_t C,
+                                           const List& lds_list, uint32_t b0, uint32_t need,
+                                           uint32_t* bm, uint32_t* s_hist, uint32_t* s_sh) {
+  if (C <= (uint32_t)kCandLds)
+    select_in_bin(lds_list, b0, need, bm, s_hist, s_sh);
+  else if (C <= (uint32_t)kCandCap)
+    select_in_bin(GlobalList{p.cand + (size_t)r * kCandCap, (int)C}, b0, need, bm, s_hist, s_sh);
+  else
+    select_in_bin(RowList{p.votes + (size_t)r * p.row_stride, len}, b0, need, bm, s_hist, s_sh);
+}
+
+// Ascending indices of the set bits of words [0, W), at most k_eff of them.
+template <bool LDS_BM>
+__device__ __forceinline__ void emit_bitmap(const uint32_t* bm, int W, int k_eff, int32_t* out,
+                                            uint32_t* s_sh) {
+  constexpr int NT = kFinalThreads;
+  constexpr int WPT = 16;                          // words per thread per round
+  const int tid = threadIdx.x;
+  uint32_t carry = 0;
+  for (int w0 = 0; w0 < W; w0 += NT * WPT) {
+    uint32_t words[WPT];
+    uint32_t cnt = 0;
+#pragma unroll
+    for (int i = 0; i < WPT; ++i) {
+      const int w = w0 + tid * WPT + i;
+      if (LDS_BM) words[i] = (w < W) ? bm[w] : 0u;
+      else words[i] = (w < W) ? __hip_atomic_load(bm + w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 0u;
+      cnt += __popc(words[i]);
+    }
+    uint32_t total;
+    uint32_t pos = carry + block_excl_scan<NT>(cnt, s_sh, &total);
+#pragma unroll
+    for (int i = 0; i < WPT; ++i) {
+      uint32_t m = words[i];
+      const int base = (w0 + tid * WPT + i) * 32;
+      while (m) {
+        const int bit = __ffs(m) - 1;
+        if (pos < (uint32_t)k_eff) out[pos] = base + bit;
+        ++pos;
+        m &= m - 1;
+      }
+    }
+    carry += total;
   }
 }
 
-// flag word: status (bits 63..62: 0 none, 1 aggregate, 2 inclusive prefix),
-// count above T (bits 61..31), count equal to T (bits 30..0)
-__device__ __forceinline__ unsigned long long pack_flag(uint32_t st, uint32_t gt, uint32_t eq) {
-  return ((unsigned long long)st << 62) | ((unsigned long long)gt << 31) | (unsigned long long)eq;
-}
-
-__global__ __launch_bounds__(256) void topk_compact_kernel(TopkParams p) {
-  constexpr int PER = kTopkChunk / 256;  // 16 consecutive elements per thread
-  __shared__ uint32_t s_sh[8];
-  __shared__ uint32_t s_x[4];
-
-  const int r = blockIdx.y;
+__global__ __launch_bounds__(kFinalThreads) void topk_finalize_kernel(TopkParams p) {
+  constexpr int NT = kFinalThreads;
+  constexpr int CPT = kCandLds / NT;               // staged candidates per thread
+  constexpr int BPT = kBitmapLds / NT;             // staged bitmap words per thread
+  __shared__ uint32_t s_hist[2048];
+  __shared__ uint32_t s_ck[kCandLds];
+  __shared__ uint32_t s_ci[kCandLds];
+  __shared__ uint32_t s_bm[kBitmapLds];
+  __shared__ uint32_t s_sh[16];
+  const int r = blockIdx.x;
   if (p.hit && p.hit[r]) return;
   const int len = row_length(p, r);
   const int k = p.k;
   const int k_eff = min(k, len);
   const int tid = threadIdx.x;
   int32_t* out = p.idx + (size_t)r * k;
-  int32_t* out2 = p.idx2 ? p.idx2 + (size_t)r * k : nullptr;
-  if (blockIdx.x == 0) {
-    for (int i = max(k_eff, 0) + tid; i < k; i += 256) {
-      out[i] = -1;
-      if (out2) out2[i] = -1;
-    }
-  }
-  const int nchunks = (len + kTopkChunk - 1) / kTopkChunk;
-  if ((int)blockIdx.x >= nchunks) return;
+  for (int i = max(k_eff, 0) + tid; i < k; i += NT) out[i] = -1;
+  if (k_eff <= 0) return;
 
-  uint32_t* ctrl = p.ctrl + (size_t)r * kCtrlStride;
-  const uint32_t T = ctrl[kCtlPrefix];
+  const uint32_t* ctrl = p.ctrl + (size_t)r * kCtrlStride;
+  uint32_t* bm = p.bitmap + (size_t)r * p.bm_stride;
+  const int W = (len + 31) / 32;
+  const bool lds_bm = W <= kBitmapLds;
+  // one round of loads: control words, the first candidates and the bitmap
+  const uint32_t b0 = ctrl[kCtlPrefix];
   const uint32_t need = ctrl[kCtlNeed];
-  if (tid == 0) s_x[0] = atomicAdd(ctrl + kCtlTicket, 1u);
-  __syncthreads();
-  const int c = (int)s_x[0];
-
-  const float* row = p.votes + (size_t)r * p.row_stride;
-  const int base = c * kTopkChunk + tid * PER;
-  uint32_t keys[PER];
-  uint32_t gt = 0, eq = 0;
+  const uint32_t C = ctrl[kCtlCandCount];
+  const uint2* cand = p.cand + (size_t)r * kCandCap;
+  uint2 cv[CPT];
 #pragma unroll
-  for (int i = 0; i < PER; ++i) {
-    const int e = base + i;
-    keys[i] = (e < len) ? float_key(row[e]) : 0u;
-    const bool in = e < len;
-    gt += (in && keys[i] > T) ? 1u : 0u;
-    eq += (in && keys[i] == T) ? 1u : 0u;
+  for (int i = 0; i < CPT; ++i) cv[i] = cand[i * NT + tid];   // stale entries are never used
+  uint32_t bw[BPT];
+  if (lds_bm) {
+#pragma unroll
+    for (int i = 0; i < BPT; ++i) bw[i] = (i * NT + tid < W) ? bm[i * NT + tid] : 0u;
   }
-  uint32_t gt_tot, eq_tot;
-  const uint32_t eq_before = block_excl_scan_256(eq, s_sh, &eq_tot);
-  (void)block_excl_scan_256(gt, s_sh, &gt_tot);
-
-  if (tid == 0) {
-    unsigned long long* fl = p.flags + (size_t)r * p.max_chunks;
-    __hip_atomic_store(fl + c, pack_flag(1u, gt_tot, eq_tot), __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
-    uint32_t gx = 0, ex = 0;
-    int pc = c - 1;
-    uint32_t spins = 0;
-    while (pc >= 0) {
-      const unsigned long long w = __hip_atomic_load(fl + pc, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT);
-      const uint32_t st = (uint32_t)(w >> 62);
-      if (st == 0u) {
-        // predecessors hold earlier tickets, so they are resident and publish
-        // without waiting; the bound only guards against a corrupted state.
-        if (++spins > (1u << 22)) {
-          atomicOr(ctrl + kCtlErr, 1u);
-          break;
-        }
-        __builtin_amdgcn_s_sleep(1);
-        continue;
-      }
-      gx += (uint32_t)((w >> 31) & 0x7fffffffull);
-      ex += (uint32_t)(w & 0x7fffffffull);
-      if (st == 2u) break;
-      --pc;
-    }
-    __hip_atomic_store(fl + c, pack_flag(2u, gx + gt_tot, ex + eq_tot), __ATOMIC_RELEASE,
-                       __HIP_MEMORY_SCOPE_AGENT);
-    s_x[1] = gx;
-    s_x[2] = ex;
+#pragma unroll
+  for (int i = 0; i < CPT; ++i) {
+    s_ck[i * NT + tid] = cv[i].x;
+    s_ci[i * NT + tid] = cv[i].y;
+  }
+  if (lds_bm) {
+#pragma unroll
+    for (int i = 0; i < BPT; ++i) s_bm[i * NT + tid] = bw[i];
   }
   __syncthreads();
-  const uint32_t gx = s_x[1], ex = s_x[2];
 
-  const uint32_t tie0 = ex + eq_before;    // global tie rank of this thread's first tie
-  const uint32_t taken = (need > tie0) ? min(eq, need - tie0) : 0u;
-  uint32_t sel_tot;
-  const uint32_t sel_before = block_excl_scan_256(gt + taken, s_sh, &sel_tot);
-  uint32_t pos = gx + min(ex, need) + sel_before;
-  uint32_t tie = tie0;
-#pragma unroll
-  for (int i = 0; i < PER; ++i) {
-    const int e = base + i;
-    if (e < len) {
-      const bool is_eq = keys[i] == T;
-      if ((keys[i] > T || (is_eq && tie < need)) && pos < (uint32_t)k) {
-        out[pos] = e;
-        if (out2) out2[pos] = e;
-        ++pos;
-      }
-      tie += is_eq ? 1u : 0u;
+  const LdsList lds_list{s_ck, s_ci, (int)min(C, (uint32_t)kCandLds)};
+  if (lds_bm) {
+    if (need > 0) select_any(p, r, len, C, lds_list, b0, need, s_bm, s_hist, s_sh);
+    emit_bitmap<true>(s_bm, W, k_eff, out, s_sh);
+  } else {
+    if (need > 0) {
+      select_any(p, r, len, C, lds_list, b0, need, bm, s_hist, s_sh);
+      // this work-group's bitmap updates must be visible to its own loads below
+      __threadfence();
+      __syncthreads();
     }
+    emit_bitmap<false>(bm, W, k_eff, out, s_sh);
   }
 }
 
-hipError_t launch_topk_hist(const TopkParams& p, int pass, int grid_x, hipStream_t s) {
-  if (pass == 0)
-    hipLaunchKernelGGL(topk_hist_kernel<0>, dim3(grid_x, p.rows), dim3(256), 0, s, p);
-  else if (pass == 1)
-    hipLaunchKernelGGL(topk_hist_kernel<1>, dim3(grid_x, p.rows), dim3(256), 0, s, p);
-  else
-    hipLaunchKernelGGL(topk_hist_kernel<2>, dim3(grid_x, p.rows), dim3(256), 0, s, p);
+hipError_t launch_topk_hist0(const TopkParams& p, int grid_x, hipStream_t s) {
+  hipLaunchKernelGGL(topk_hist0_kernel, dim3(grid_x, p.rows), dim3(256), 0, s, p);
   return hipGetLastError();
 }
 
-hipError_t launch_topk_compact(const TopkParams& p, int grid_x, hipStream_t s) {
-  hipLaunchKernelGGL(topk_compact_kernel, dim3(grid_x, p.rows), dim3(256), 0, s, p);
+hipError_t launch_topk_partition(const TopkParams& p, int grid_x, hipStream_t s) {
+  hipLaunchKernelGGL(topk_partition_kernel, dim3(grid_x, p.rows), dim3(256), 0, s, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_topk_finalize(const TopkParams& p, hipStream_t s) {
+  hipLaunchKernelGGL(topk_finalize_kernel, dim3(p.rows), dim3(kFinalThreads), 0, s, p);
   return hipGetLastError();
 }
 

@@ -48,12 +48,12 @@ ts_status hip_check(hipError_t e, const char* what) {
 
 // ---- kernel-level timing (ts_profile_*) ---------------------------------------
 enum KernelKind {
-  kKPrologue, kKScore, kKVotes, kKTopkHist, kKTopkCompact, kKAttend, kKCombine,
-  kKPrefillLse, kKPrefillVotes, kKFill, kKNum
+  kKPrologue, kKScore, kKLse, kKVotes, kKTopkHist, kKTopkPartition, kKTopkFinalize, kKAttend,
+  kKCombine, kKPrefillLse, kKPrefillVotes, kKFill, kKNum
 };
 const char* const kKernelNames[kKNum] = {
-  "prologue", "score_pass1", "votes", "topk_hist", "topk_compact", "attend", "combine",
-  "prefill_lse", "prefill_votes", "fill_zero"
+  "prologue", "score_pass1", "lse", "votes", "topk_hist", "topk_partition", "topk_finalize",
+  "attend", "combine", "prefill_lse", "prefill_votes", "fill_zero"
 };
 
 struct Prof {
@@ -170,6 +170,9 @@ ts_status check_layout(const ts_kv_layout* L, int batch, Geo* g) {
   if (L->page_size > 0) {
     if (!is_pow2(L->page_size)) return fail(TS_ERR_INVALID_ARG, "page_size must be a power of two");
     const long need = ((long)L->max_len + L->page_size - 1) / L->page_size;
+    const long esz = L->dtype == TS_BF16 ? 2 : 4;
+    if ((long)L->page_size * L->num_kv_heads * L->head_dim * esz > (1l << 31))
+      return fail(TS_ERR_UNSUPPORTED, "page too large (page_size * Hkv * d * elem > 2 GiB)");
     if (L->page_table_stride < need)
       return fail(TS_ERR_INVALID_ARG, "page_table_stride %d < pages of max_len (%ld)",
                   L->page_table_stride, need);
@@ -192,23 +195,31 @@ ts_status check_layout(const ts_kv_layout* L, int batch, Geo* g) {
   for (int s = 8; s >= 1; --s)
     if (g->G % s == 0 && g->Hkv * s <= kMaxHeadsPerWG) { g->GS = s; break; }
   g->nslices = g->G / g->GS;
-  // the scoring work-group keeps one KV head per row group
-  const int esz = g->dtype == TS_BF16 ? 2 : 4;
-  const int lpr = g->d * esz / 32;
-  if (g->Hkv > 256 / lpr)
+  // the scoring work-group keeps one KV head per row group: 64 row groups for
+  // bf16 rows, 32 for fp32 d=64, 16 for fp32 d=128
+  const int rgs = g->dtype == TS_BF16 ? 64 : (g->d == 64 ? 32 : 16);
+  if (g->Hkv > rgs)
     return fail(TS_ERR_UNSUPPORTED, "num_kv_heads %d too large for this head_dim/dtype (max %d)",
-                g->Hkv, 256 / lpr);
+                g->Hkv, rgs);
   return TS_OK;
 }
 
 // ---- workspace plans -----------------------------------------------------------
 
 struct ScorePlan {
-  int ntiles, Lpad;
+  int tile, ntiles, Lpad;
   size_t ctrl, lse, partials, logits;
 };
 void plan_score(const Geo& g, int B, Carve& c, ScorePlan& s) {
-  s.ntiles = cdiv(g.max_len, kScoreTile);
+  // 256-token tiles unless that leaves fewer than two work-groups per CU (and
+  // 128 whenever a 256-token logit tile would not fit in 64 KB of LDS)
+  const long wg256 = (long)B * g.nslices * cdiv(g.max_len, 256);
+  const bool fits256 = (long)g.Hkv * g.GS * (256 + 1) * 4 <= 65536;
+  s.tile = (wg256 >= 512 && fits256) ? 256 : 128;
+#ifdef TS_FORCE_SCORE_TILE
+  s.tile = TS_FORCE_SCORE_TILE;   // build-time override for tuning sweeps
+#endif
+  s.ntiles = cdiv(g.max_len, s.tile);
   s.Lpad = cdiv(g.max_len, kVoteTile) * kVoteTile;
   s.ctrl = c.take((size_t)B * kCtrlStride * 4);
   s.lse = c.take((size_t)B * g.Hq * 4);
@@ -221,10 +232,11 @@ struct AttendPlan {
   size_t pm, pl, pacc;
 };
 void plan_attend(const Geo& g, int B, int k, Carve& c, AttendPlan& a) {
-  // enough work-groups to cover the chip twice, without splits under 16 rows
+  // about two work-groups per CU, each gathering 32..256 selected rows
   const long cols = (long)B * g.Hkv * g.nslices;
   int split = 256;
-  while (split > 16 && cols * cdiv(k, split) < 512) split >>= 1;
+  while (split > 32 && cols * cdiv(k, split) < 512) split >>= 1;
+  while (cdiv(k, split) > kMaxSplits) split <<= 1;
   a.split = split;
   a.nsplit = cdiv(k, split);
   a.pm = c.take((size_t)B * g.Hq * a.nsplit * 4);
@@ -233,13 +245,33 @@ void plan_attend(const Geo& g, int B, int k, Carve& c, AttendPlan& a) {
 }
 
 struct TopkPlan {
-  int max_chunks;
-  size_t ctrl, flags;
+  int bm_stride;
+  size_t ctrl, bitmap, cand;
 };
 void plan_topk(int rows, int row_stride, Carve& c, TopkPlan& t, bool own_ctrl) {
-  t.max_chunks = cdiv(row_stride, kTopkChunk);
+  t.bm_stride = cdiv(row_stride, kTopkChunk) * (kTopkChunk / 32);
   if (own_ctrl) t.ctrl = c.take((size_t)rows * kCtrlStride * 4);
-  t.flags = c.take((size_t)rows * t.max_chunks * 8);
+  t.bitmap = c.take((size_t)rows * t.bm_stride * 4);
+  t.cand = c.take((size_t)rows * kCandCap * 8);
+}
+
+TopkParams topk_params(const TopkPlan& t, void* ws, int rows, int row_stride, int k,
+                       const float* votes, const int32_t* row_lens, int row_len_base,
+                       const int32_t* hit, int32_t* idx) {
+  TopkParams tp{};
+  tp.votes = votes;
+  tp.row_lens = row_lens;
+  tp.row_len_base = row_len_base;
+  tp.hit = hit;
+  tp.idx = idx;
+  tp.ctrl = at<uint32_t>(ws, t.ctrl);
+  tp.bitmap = at<uint32_t>(ws, t.bitmap);
+  tp.cand = at<uint2>(ws, t.cand);
+  tp.rows = rows;
+  tp.row_stride = row_stride;
+  tp.k = k;
+  tp.bm_stride = t.bm_stride;
+  return tp;
 }
 
 struct DecodePlan {
@@ -269,8 +301,7 @@ ScoreParams score_params(const Geo& g, const ScorePlan& s, int B, void* ws, cons
   p.hit = hit;
   p.logits = at<float>(ws, s.logits);
   p.partials = at<float2>(ws, s.partials);
-  p.lse = at<float>(ws, s.lse);
-  p.ctrl = at<uint32_t>(ws, s.ctrl);
+  p.tile = s.tile;
   p.B = B;
   p.Hq = g.Hq;
   p.Hkv = g.Hkv;
@@ -286,8 +317,22 @@ ScoreParams score_params(const Geo& g, const ScorePlan& s, int B, void* ws, cons
   return p;
 }
 
+LseParams lse_params(const Geo& g, const ScorePlan& s, int B, void* ws, const int32_t* lens,
+                     const int32_t* hit) {
+  LseParams l{};
+  l.partials = at<float2>(ws, s.partials);
+  l.seq_lens = lens;
+  l.hit = hit;
+  l.lse = at<float>(ws, s.lse);
+  l.B = B;
+  l.Hq = g.Hq;
+  l.ntiles = s.ntiles;
+  l.tile = s.tile;
+  return l;
+}
+
 VoteParams vote_params(const Geo& g, const ScorePlan& s, int B, void* ws, const int32_t* lens,
-                       const int32_t* hit, float* votes, int vote_stride, int k, int do_hist) {
+                       const int32_t* hit, float* votes, int vote_stride, int do_hist) {
   VoteParams v{};
   v.logits = at<float>(ws, s.logits);
   v.lse = at<float>(ws, s.lse);
@@ -299,7 +344,6 @@ VoteParams vote_params(const Geo& g, const ScorePlan& s, int B, void* ws, const 
   v.Hq = g.Hq;
   v.Lpad = s.Lpad;
   v.vote_stride = vote_stride;
-  v.k = k;
   v.do_hist = do_hist;
   return v;
 }
@@ -409,14 +453,12 @@ ts_status ts_score(const ts_kv_layout* L, int32_t batch, const void* q, const vo
   TS_TRY(check_ws(ws, ws_bytes, c.off));
   hipStream_t st = static_cast<hipStream_t>(stream);
 
-  PrologueParams pp{};
-  pp.ctrl = at<uint32_t>(ws, s.ctrl);
-  pp.rows = batch;
-  TS_LAUNCH_K(kKPrologue, launch_prologue(pp, batch, st), "prologue");
   ScoreParams sp = score_params(g, s, batch, ws, q, k_cache, g.paged ? page_table : nullptr,
                                 seq_lens, nullptr);
   TS_LAUNCH_K(kKScore, launch_score_pass1(g.dtype, g.d, g.paged, sp, st), "score pass 1");
-  VoteParams vp = vote_params(g, s, batch, ws, seq_lens, nullptr, votes, g.max_len, 1, 0);
+  LseParams lp = lse_params(g, s, batch, ws, seq_lens, nullptr);
+  TS_LAUNCH_K(kKLse, launch_lse(lp, st), "log-sum-exp");
+  VoteParams vp = vote_params(g, s, batch, ws, seq_lens, nullptr, votes, g.max_len, 0);
   TS_LAUNCH_K(kKVotes, launch_votes(vp, cdiv(g.max_len, kVoteTile), st), "votes");
   return ok();
 }
@@ -439,26 +481,13 @@ static ts_status run_topk(int rows, int row_stride, const float* votes, const in
                           int max_row_len, hipStream_t st) {
   PrologueParams pp{};
   pp.ctrl = at<uint32_t>(ws, t.ctrl);
-  pp.flags = at<unsigned long long>(ws, t.flags);
   pp.rows = rows;
-  pp.max_chunks = t.max_chunks;
   TS_LAUNCH_K(kKPrologue, launch_prologue(pp, rows, st), "prologue");
-  TopkParams tp{};
-  tp.votes = votes;
-  tp.row_lens = row_lens;
-  tp.row_len_base = row_len_base;
-  tp.idx = idx;
-  tp.ctrl = at<uint32_t>(ws, t.ctrl);
-  tp.flags = at<unsigned long long>(ws, t.flags);
-  tp.rows = rows;
-  tp.row_stride = row_stride;
-  tp.k = k;
-  tp.max_chunks = t.max_chunks;
+  TopkParams tp = topk_params(t, ws, rows, row_stride, k, votes, row_lens, row_len_base, nullptr, idx);
   const int gx = cdiv(max_row_len, kTopkChunk);
-  TS_LAUNCH_K(kKTopkHist, launch_topk_hist(tp, 0, gx, st), "top-k pass 0");
-  TS_LAUNCH_K(kKTopkHist, launch_topk_hist(tp, 1, gx, st), "top-k pass 1");
-  TS_LAUNCH_K(kKTopkHist, launch_topk_hist(tp, 2, gx, st), "top-k pass 2");
-  TS_LAUNCH_K(kKTopkCompact, launch_topk_compact(tp, gx, st), "top-k compaction");
+  TS_LAUNCH_K(kKTopkHist, launch_topk_hist0(tp, gx, st), "top-k histogram");
+  TS_LAUNCH_K(kKTopkPartition, launch_topk_partition(tp, gx, st), "top-k partition");
+  TS_LAUNCH_K(kKTopkFinalize, launch_topk_finalize(tp, st), "top-k finalize");
   return TS_OK;
 }
 
@@ -631,9 +660,7 @@ ts_status ts_decode_step(ts_sel_cache* cache, const ts_kv_layout* L, int32_t bat
   // 1. reset control blocks; Selection-Cache decision per sequence
   PrologueParams pp{};
   pp.ctrl = at<uint32_t>(ws, p.s.ctrl);
-  pp.flags = at<unsigned long long>(ws, p.t.flags);
   pp.rows = batch;
-  pp.max_chunks = p.t.max_chunks;
   pp.cache = cache->dev;
   pp.q = q;
   pp.dtype = g.dtype;
@@ -646,26 +673,18 @@ ts_status ts_decode_step(ts_sel_cache* cache, const ts_kv_layout* L, int32_t bat
   // 2. K-scan (misses only)
   ScoreParams sp = score_params(g, p.s, batch, ws, q, k_cache, pt, seq_lens, hit);
   TS_LAUNCH_K(kKScore, launch_score_pass1(g.dtype, g.d, g.paged, sp, st), "score pass 1");
+  LseParams lp = lse_params(g, p.s, batch, ws, seq_lens, hit);
+  TS_LAUNCH_K(kKLse, launch_lse(lp, st), "log-sum-exp");
   // 3. votes + first radix histogram
   float* votes = at<float>(ws, p.votes);
-  VoteParams vp = vote_params(g, p.s, batch, ws, seq_lens, hit, votes, g.max_len, k, 1);
+  VoteParams vp = vote_params(g, p.s, batch, ws, seq_lens, hit, votes, g.max_len, 1);
   TS_LAUNCH_K(kKVotes, launch_votes(vp, cdiv(g.max_len, kVoteTile), st), "votes");
   // 4. top-k into the cache's stored selection
-  TopkParams tp{};
-  tp.votes = votes;
-  tp.row_lens = seq_lens;
-  tp.hit = hit;
-  tp.idx = cache->dev.sel;
-  tp.ctrl = at<uint32_t>(ws, p.s.ctrl);
-  tp.flags = at<unsigned long long>(ws, p.t.flags);
-  tp.rows = batch;
-  tp.row_stride = g.max_len;
-  tp.k = k;
-  tp.max_chunks = p.t.max_chunks;
+  TopkParams tp = topk_params(p.t, ws, batch, g.max_len, k, votes, seq_lens, 0, hit,
+                              cache->dev.sel);
   const int gx = cdiv(g.max_len, kTopkChunk);
-  TS_LAUNCH_K(kKTopkHist, launch_topk_hist(tp, 1, gx, st), "top-k pass 1");
-  TS_LAUNCH_K(kKTopkHist, launch_topk_hist(tp, 2, gx, st), "top-k pass 2");
-  TS_LAUNCH_K(kKTopkCompact, launch_topk_compact(tp, gx, st), "top-k compaction");
+  TS_LAUNCH_K(kKTopkPartition, launch_topk_partition(tp, gx, st), "top-k partition");
+  TS_LAUNCH_K(kKTopkFinalize, launch_topk_finalize(tp, st), "top-k finalize");
   // 5. sparse attention over the current selection; 6. combine + state update
   AttendParams ap = attend_params(g, p.a, batch, ws, q, k_cache, v_cache, pt, seq_lens,
                                   cache->dev.sel, k);

@@ -22,6 +22,11 @@ __device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float acc) {
                                          __builtin_bit_cast(bf16x2_t, b), acc, false);
 }
 
+// 2^x with the hardware v_exp_f32 alone: results below 2^-126 flush to zero.
+// Used only on non-positive log-ratios whose exponentials are summed, where
+// such terms are negligible against the sum's 1-ulp rounding.
+__device__ __forceinline__ float ex2(float x) { return __builtin_amdgcn_exp2f(x); }
+
 template <int CTRL>
 __device__ __forceinline__ float dpp_f(float v) {
   return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL,
@@ -104,52 +109,60 @@ __device__ __forceinline__ uint32_t block_excl_scan_256(uint32_t v, uint32_t* sh
   return base + x - v;
 }
 
-// Find, in a histogram of `nbins` counts (256 | nbins, nbins <= 2048), the
-// highest bin whose suffix sum (bins >= it) reaches `need`, and the number of
-// elements still needed inside that bin. Block-wide over 256 threads; `sh`
-// needs 260 words. Result in sh[256] (bin) and sh[257] (still needed).
-__device__ __forceinline__ void resolve_bin(const uint32_t* hist, int nbins, uint32_t need,
-                                            uint32_t* sh) {
-  const int t = threadIdx.x;
-  const int per = nbins >> 8;
-  if (t == 0) { sh[256] = 0u; sh[257] = 0u; }
-  uint32_t c[8];
+// Given this thread's PER consecutive bins of an NT*PER-bin histogram (thread
+// t owns bins t*PER .. t*PER+PER-1), find the highest bin whose suffix sum
+// (bins >= it) reaches `need` (1 <= need <= total) and how many elements are
+// still needed inside it. Block-wide over NT threads (a multiple of 64); `sh`
+// needs NT/64 + 2 words. Returns (bin, still needed) in every thread.
+template <int PER, int NT = 256>
+__device__ __forceinline__ uint2 resolve_counts(const uint32_t (&c)[PER], uint32_t need, uint32_t* sh) {
+  constexpr int NWAVE = NT / 64;
+  const int t = threadIdx.x, lane = t & 63, w = t >> 6;
   uint32_t s = 0;
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    c[i] = (i < per) ? __hip_atomic_load(hist + t * per + i, __ATOMIC_RELAXED,
-                                         __HIP_MEMORY_SCOPE_AGENT)
-                     : 0u;
-    s += c[i];
+  for (int i = 0; i < PER; ++i) s += c[i];
+  // inclusive suffix sum over the lanes of this wave (lanes >= lane)
+  uint32_t x = s;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const uint32_t y = __shfl_down(x, o);
+    if (lane + o < 64) x += y;
   }
-  // suffix sums over threads: above_t = sum of s over threads > t
-  sh[t] = s;
+  if (lane == 0) sh[2 + w] = x;
+  if (t == 0) { sh[0] = 0u; sh[1] = 0u; }
   __syncthreads();
-  for (int o = 1; o < 256; o <<= 1) {
-    uint32_t y = (t + o < 256) ? sh[t + o] : 0u;
-    __syncthreads();
-    sh[t] += y;
-    __syncthreads();
-  }
-  uint32_t incl = sh[t];          // sum over threads >= t
-  uint32_t above = incl - s;
-  __syncthreads();
+  uint32_t above_w = 0;
+#pragma unroll
+  for (int i = 1; i < NWAVE; ++i)
+    if (w + i < NWAVE) above_w += sh[2 + w + i];
+  const uint32_t incl = x + above_w;     // sum over bins owned by threads >= t
+  const uint32_t above = incl - s;
   if (above < need && need <= incl) {
     uint32_t cum = above;
     bool done = false;
 #pragma unroll
-    for (int i = 7; i >= 0; --i) {
-      if (i < per && !done) {
-        if (cum + c[i] >= need) {
-          sh[256] = (uint32_t)(t * per + i);
-          sh[257] = need - cum;
-          done = true;
-        }
-        cum += c[i];
+    for (int i = PER - 1; i >= 0; --i) {
+      if (!done && cum + c[i] >= need) {
+        sh[0] = (uint32_t)(t * PER + i);
+        sh[1] = need - cum;
+        done = true;
       }
+      cum += c[i];
     }
   }
   __syncthreads();
+  const uint2 r = make_uint2(sh[0], sh[1]);
+  __syncthreads();
+  return r;
+}
+
+// Same over a histogram held in LDS (NT*PER bins).
+template <int PER, int NT>
+__device__ __forceinline__ uint2 resolve_lds(const uint32_t* hist, uint32_t need, uint32_t* sh) {
+  uint32_t c[PER];
+#pragma unroll
+  for (int i = 0; i < PER; ++i) c[i] = hist[threadIdx.x * PER + i];
+  return resolve_counts<PER, NT>(c, need, sh);
 }
 
 }  // namespace ts

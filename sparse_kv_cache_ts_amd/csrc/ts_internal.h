@@ -9,30 +9,30 @@
 namespace ts {
 
 // ---- tiling constants -------------------------------------------------------
-constexpr int kScoreTile = 256;    // tokens per scoring work-group (pass 1)
-constexpr int kVoteTile = 1024;    // tokens per vote work-group (pass 2)
+constexpr int kScoreTileMax = 256; // largest token tile of a scoring work-group (128 or 256)
+constexpr int kVoteTile = 512;     // tokens per vote work-group (pass 2)
 constexpr int kTopkChunk = 4096;   // elements per top-k work-group
 constexpr int kMaxHeadsPerWG = 64; // Hkv * heads-per-slice held by one scoring WG
 constexpr int kMaxQHeads = 256;
+constexpr int kMaxSplits = 1024;  // attention splits per (sequence, head)
 constexpr float kLog2eHost = 1.4426950408889634f;
 
 // ---- per-row control block (uint32 words) ----------------------------------
-// Zeroed by the prologue kernel at the start of every call that uses it.
+// Zeroed at the start of every call that uses it.
 enum CtrlWord : int {
-  kCtlCntScore = 0,   // scoring work-groups finished (per sequence)
-  kCtlCntVote = 1,    // vote work-groups finished
-  kCtlCntHist1 = 2,   // top-k pass-1 work-groups finished
-  kCtlCntHist2 = 3,   // top-k pass-2 work-groups finished
-  kCtlTicket = 4,     // compaction ticket
-  kCtlPrefix = 5,     // key bits fixed so far (after pass 2: the full threshold key)
-  kCtlNeed = 6,       // elements still to take among those matching the prefix
+  kCtlCandCount = 0,  // candidates appended to the row's candidate list
+  kCtlPrefix = 1,     // top-12-bit bin that holds the k-th largest key
+  kCtlNeed = 2,       // elements still to take inside that bin (0: the whole bin)
   kCtlErr = 7,        // non-zero if a bounded wait gave up
-  kCtlHist0 = 16,     // 2048 bins: key bits 31..21
-  kCtlHist1 = 16 + 2048,  // 2048 bins: key bits 20..10
-  kCtlHist2 = 16 + 4096,  // 1024 bins: key bits 9..0
-  kCtlWords = 16 + 4096 + 1024,
+  kCtlHist0 = 16,     // 4096 bins: key bits 31..20
+  kCtlWords = 16 + 4096,
 };
 constexpr int kCtrlStride = ((kCtlWords + 63) / 64) * 64;   // 256-byte rows
+constexpr int kHist0Bits = 12;
+constexpr int kCandCap = 8192;    // candidates kept per row; more falls back to a row rescan
+constexpr int kCandLds = 2048;    // candidates the finalize work-group stages in LDS
+constexpr int kBitmapLds = 8192;  // bitmap words (rows of up to 262144 tokens) staged in LDS
+constexpr int kFinalThreads = 512;
 
 inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 inline int cdiv(long a, long b) { return (int)((a + b - 1) / b); }
@@ -52,8 +52,7 @@ struct SelCacheDev {
 // ---- kernel parameter blocks -------------------------------------------------
 struct PrologueParams {
   uint32_t* ctrl;       // [rows][kCtrlStride] or null
-  unsigned long long* flags;  // [rows][max_chunks] or null
-  int rows, max_chunks;
+  int rows;
   // selection-cache check (cache.prev_q == null: none)
   SelCacheDev cache;
   const void* q;        // [B][Hq][d]
@@ -71,33 +70,40 @@ struct ScoreParams {
   const int32_t* hit;       // [B] or null: sequences with hit != 0 are skipped
   float* logits;            // [B][Hq][Lpad] base-2 logits (scale * log2 e * q.k)
   float2* partials;         // [B][Hq][ntiles] (tile max, tile sum of exp2)
-  float* lse;               // [B][Hq] base-2 log-sum-exp over all tokens
-  uint32_t* ctrl;           // [B][kCtrlStride]
   int B, Hq, Hkv, G, GS, nslices, max_len, Lpad, ntiles, ps_log2, pt_stride;
+  int tile;                 // tokens per work-group: 128 or 256
   float scale2;
+};
+
+struct LseParams {
+  const float2* partials;   // [B][Hq][ntiles]
+  const int32_t* seq_lens;
+  const int32_t* hit;
+  float* lse;               // [B][Hq] base-2 log-sum-exp over all tokens
+  int B, Hq, ntiles, tile;
 };
 
 struct VoteParams {
   const float* logits;
-  const float* lse;
+  const float* lse;         // [B][Hq]
   const int32_t* seq_lens;
   const int32_t* hit;
   float* votes;             // [B][vote_stride]
   uint32_t* ctrl;
-  int B, Hq, Lpad, vote_stride, k;
-  int do_hist;              // 1: build the first top-k histogram and resolve it
+  int B, Hq, Lpad, vote_stride;
+  int do_hist;              // 1: add the votes to the first top-k histogram
 };
 
 struct TopkParams {
   const float* votes;       // [rows][row_stride]
-  const int32_t* row_lens;  // [rows] (null: q_pos0 + r + 1, the causal prefill rows)
+  const int32_t* row_lens;  // [rows] (null: row_len_base + r, the causal prefill rows)
   int row_len_base;         // used when row_lens is null
-  const int32_t* hit;       // [rows] or null
+  const int32_t* hit;       // [rows] or null: rows with hit != 0 are skipped
   int32_t* idx;             // [rows][k]
-  int32_t* idx2;            // optional second copy of the result (or null)
-  uint32_t* ctrl;
-  unsigned long long* flags;  // [rows][max_chunks]
-  int rows, row_stride, k, max_chunks;
+  uint32_t* ctrl;           // [rows][kCtrlStride]
+  uint32_t* bitmap;         // [rows][bm_stride] selection bits
+  uint2* cand;              // [rows][kCandCap] (key, index) of threshold-bin candidates
+  int rows, row_stride, k, bm_stride;
 };
 
 struct AttendParams {
@@ -142,9 +148,11 @@ struct PrefillParams {
 hipError_t launch_prologue(const PrologueParams& p, int grid, hipStream_t s);
 hipError_t launch_fill_zero(void* ptr, size_t words, hipStream_t s);   // 32-bit words
 hipError_t launch_score_pass1(int dtype, int d, bool paged, const ScoreParams& p, hipStream_t s);
+hipError_t launch_lse(const LseParams& p, hipStream_t s);
 hipError_t launch_votes(const VoteParams& p, int grid_x, hipStream_t s);
-hipError_t launch_topk_hist(const TopkParams& p, int pass, int grid_x, hipStream_t s);
-hipError_t launch_topk_compact(const TopkParams& p, int grid_x, hipStream_t s);
+hipError_t launch_topk_hist0(const TopkParams& p, int grid_x, hipStream_t s);
+hipError_t launch_topk_partition(const TopkParams& p, int grid_x, hipStream_t s);
+hipError_t launch_topk_finalize(const TopkParams& p, hipStream_t s);
 hipError_t launch_attend(int dtype, int d, bool paged, const AttendParams& p, hipStream_t s);
 hipError_t launch_combine(const CombineParams& p, hipStream_t s);
 hipError_t launch_prefill_lse(const PrefillParams& p, hipStream_t s);
