@@ -28,6 +28,52 @@
 
 namespace ts {
 
+// ---- cross-lane reduce-scatter of per-head partial dot products ------------
+// A row's dot products are split over LPR lanes, each holding NS partial sums
+// (one per query-head slot, NS = GS padded to a power of two). The lanes of a
+// row are combined with DPP pairings, from the top lane bit down: row_mirror
+// (16 lanes), row_half_mirror (8), lane^2, lane^1. The first steps add a slot
+// to the partner's same slot (all-reduce); the last log2(NS) steps halve the
+// slot count: slot i adds the partner's slot i + n/2. For that to be correct
+// the partner's upper-half slot must carry the same head as this lane's slot
+// i, so lane j stores head (s ^ f(j)) in slot s, with f as below (the mirror
+// pairings flip all lower lane bits, which c(j) absorbs). Each lane ends with
+// NS >> min(log2 NS, log2 LPR) fully reduced heads: slot i is head i ^ f(j).
+constexpr int ilog2(int x) { return x <= 1 ? 0 : 1 + ilog2(x >> 1); }
+
+template <int LPR, int NS>
+__device__ __forceinline__ int slot_perm(int j) {
+  constexpr int RS = ilog2(NS) < ilog2(LPR) ? ilog2(NS) : ilog2(LPR);
+  constexpr int SH = ilog2(NS) - RS;
+  const int c = (((j >> 2) & 1) ? 3 : 0) ^ (((j >> 3) & 1) ? 4 : 0);
+  return ((j ^ c) << SH) & (NS - 1);
+}
+
+template <int CTRL, int NS, int N, bool SCATTER>
+__device__ __forceinline__ void rs_apply(float (&v)[NS]) {
+  if constexpr (SCATTER) {
+#pragma unroll
+    for (int i = 0; i < N / 2; ++i) v[i] += dpp_f<CTRL>(v[i + N / 2]);
+  } else {
+#pragma unroll
+    for (int i = 0; i < N; ++i) v[i] += dpp_f<CTRL>(v[i]);
+  }
+}
+
+template <int LPR, int NS, int K = 0>
+__device__ __forceinline__ void reduce_slots(float (&v)[NS]) {
+  constexpr int L2L = ilog2(LPR);
+  if constexpr (K < L2L) {
+    constexpr int RS = ilog2(NS) < L2L ? ilog2(NS) : L2L;
+    constexpr int AR = L2L - RS;
+    constexpr int lvl = L2L - K;   // 4: row_mirror, 3: row_half_mirror, 2: lane^2, 1: lane^1
+    constexpr int CTRL = lvl == 4 ? 0x140 : lvl == 3 ? 0x141 : lvl == 2 ? 0x4E : 0xB1;
+    if constexpr (K < AR) rs_apply<CTRL, NS, NS, false>(v);
+    else rs_apply<CTRL, NS, (NS >> (K - AR)), true>(v);
+    reduce_slots<LPR, NS, K + 1>(v);
+  }
+}
+
 // Row split: LPR lanes per (token, KV head) row, CPL 16-byte chunks per lane;
 // chunk c of lane j covers bytes c*16*LPR + 16*j of the row, so one load
 // instruction reads 16*LPR contiguous bytes of every row it touches.
@@ -46,11 +92,11 @@ __global__ __launch_bounds__(256) void score_pass1_kernel(ScoreParams p) {
   using RS = RowSplit<DT, D, LPR>;
   constexpr int ROWB = RS::ROWB, CPL = RS::CPL, WPL = RS::WPL, RG = RS::RG;
   constexpr int U = (8 / CPL) > 0 ? (8 / CPL) : 1;   // rows per lane per batch (8 loads)
-  constexpr int NW = (GS + LPR - 1) / LPR;           // logits each lane stores per row
-  constexpr int LS = TILE + 1;                       // padded LDS row: stores spread over banks
+  constexpr int NS = GS <= 1 ? 1 : GS <= 2 ? 2 : GS <= 4 ? 4 : 8;   // head slots
+  constexpr int NFIN = NS >> (ilog2(NS) < ilog2(LPR) ? ilog2(NS) : ilog2(LPR));  // heads per lane
   static_assert(TILE % 64 == 0 && TILE <= kScoreTileMax, "tile");
 
-  extern __shared__ float s_log[];   // [Hkv*GS][TILE+1]
+  __shared__ float2 s_ml[RG][GS];    // per (row group, head): running (max, sum of exp2)
   __shared__ long long s_page[PAGED ? TILE : 1];
 
   const int tile = blockIdx.x;
@@ -70,7 +116,6 @@ __global__ __launch_bounds__(256) void score_pass1_kernel(ScoreParams p) {
   const bool active = rg < TPI * Hkv;
   const int kvh = rg % Hkv;
   const int toff = rg / Hkv;
-  const int NH = Hkv * GS;                   // heads this work-group scores
 
   const char* kbase;
   if constexpr (PAGED) {
@@ -116,19 +161,31 @@ __global__ __launch_bounds__(256) void score_pass1_kernel(ScoreParams p) {
   uint4 bufA[U][CPL], bufB[U][CPL];
   if (n_iter > 0) load_batch(0, bufA, !full);
 
-  // query slice of this lane's KV-head group (bf16 pairs or fp32 words)
-  uint32_t qw[GS][WPL];
+  // query slice of this lane's KV-head group, slot s holding head s ^ f(j)
+  // (slots past GS hold zeros)
+  const int fj = slot_perm<LPR, NS>(j);
+  uint32_t qw[NS][WPL];
 #pragma unroll
-  for (int hh = 0; hh < GS; ++hh) {
-    const int head = kvh * p.G + slice * GS + hh;
-    const char* qb = (const char*)p.q + ((size_t)b * p.Hq + (active ? head : 0)) * ROWB + j * 16;
+  for (int sl = 0; sl < NS; ++sl) {
+    const int hh = sl ^ fj;
+    const bool real = active && hh < GS;
+    const int head = kvh * p.G + slice * GS + (real ? hh : 0);
+    const char* qb = (const char*)p.q + ((size_t)b * p.Hq + head) * ROWB + j * 16;
 #pragma unroll
     for (int c = 0; c < CPL; ++c) {
-      const uint4 v = ld16(qb + c * 16 * LPR);
-      qw[hh][4 * c + 0] = v.x; qw[hh][4 * c + 1] = v.y; qw[hh][4 * c + 2] = v.z; qw[hh][4 * c + 3] = v.w;
+      const uint4 v = real ? ld16(qb + c * 16 * LPR) : make_uint4(0, 0, 0, 0);
+      qw[sl][4 * c + 0] = v.x; qw[sl][4 * c + 1] = v.y; qw[sl][4 * c + 2] = v.z; qw[sl][4 * c + 3] = v.w;
     }
   }
   const float scale2 = p.scale2;
+  // token-major logits: all Hq heads of one token are contiguous
+  float* lrow = p.logits + ((size_t)b * p.Lpad + t0) * p.Hq + kvh * p.G + slice * GS;
+  float mx[NFIN], sm[NFIN];
+#pragma unroll
+  for (int i = 0; i < NFIN; ++i) {
+    mx[i] = -INFINITY;
+    sm[i] = 0.f;
+  }
 
   auto compute_batch = [&](int i0, const uint4 (&kc)[U][CPL], bool guard) {
 #pragma unroll
@@ -139,28 +196,35 @@ __global__ __launch_bounds__(256) void score_pass1_kernel(ScoreParams p) {
         kw[4 * c + 0] = kc[u][c].x; kw[4 * c + 1] = kc[u][c].y;
         kw[4 * c + 2] = kc[u][c].z; kw[4 * c + 3] = kc[u][c].w;
       }
-      float acc[GS];
+      float acc[NS];
 #pragma unroll
-      for (int hh = 0; hh < GS; ++hh) {
+      for (int sl = 0; sl < NS; ++sl) {
         float a = 0.f;
         if constexpr (DT == 1) {
 #pragma unroll
-          for (int w = 0; w < WPL; ++w) a = dot2_bf16(kw[w], qw[hh][w], a);
+          for (int w = 0; w < WPL; ++w) a = dot2_bf16(kw[w], qw[sl][w], a);
         } else {
 #pragma unroll
-          for (int w = 0; w < WPL; ++w) a = fmaf(__uint_as_float(kw[w]), __uint_as_float(qw[hh][w]), a);
+          for (int w = 0; w < WPL; ++w) a = fmaf(__uint_as_float(kw[w]), __uint_as_float(qw[sl][w]), a);
         }
-        acc[hh] = group_sum<LPR>(a);
+        acc[sl] = a;
       }
+      reduce_slots<LPR, NS>(acc);
       const int t = toff + (i0 + u) * TPI;
-      // lane j of the row group stores the logits of heads j, j+LPR, ...
+      if (!guard || i0 + u < n_iter) {
+        // this lane now holds heads i ^ f(j), i < NFIN (lanes paired by the
+        // all-reduce steps hold the same sums and store the same values)
 #pragma unroll
-      for (int r = 0; r < NW; ++r) {
-        float v = acc[0];
-#pragma unroll
-        for (int hh = 1; hh < GS; ++hh) v = (r * LPR + j == hh) ? acc[hh] : v;
-        const int hh = r * LPR + j;
-        if ((!guard || i0 + u < n_iter) && hh < GS) s_log[(kvh * GS + hh) * LS + t] = v * scale2;
+        for (int i = 0; i < NFIN; ++i) {
+          const int hh = i ^ fj;
+          const float sc = acc[i] * scale2;
+          if (hh < GS) lrow[(size_t)t * p.Hq + hh] = sc;
+          // running max and sum of exp2 with a single exp per logit
+          const float dlt = sc - mx[i];
+          const float e = ex2(-fabsf(dlt));
+          sm[i] = (dlt > 0.f) ? fmaf(sm[i], e, 1.f) : sm[i] + e;
+          mx[i] = fmaxf(mx[i], sc);
+        }
       }
     }
   };
@@ -180,41 +244,28 @@ __global__ __launch_bounds__(256) void score_pass1_kernel(ScoreParams p) {
       compute_batch(i0 + U, bufB, true);
     }
   }
-  __syncthreads();
 
-  // logits -> global, coalesced per head row (padding past tl is never read)
-  for (int i = tid; i < NH * (TILE / 4); i += 256) {
-    const int hl = i / (TILE / 4);
-    const int t = (i % (TILE / 4)) * 4;
-    if (t < tl) {
-      const int head = (hl / GS) * p.G + slice * GS + (hl % GS);
-      const float* sp = &s_log[hl * LS + t];
-      *reinterpret_cast<float4*>(p.logits + ((size_t)b * p.Hq + head) * p.Lpad + t0 + t) =
-          make_float4(sp[0], sp[1], sp[2], sp[3]);
+  // per (head, tile): fold the row groups' running (max, sum) into one pair
+  if (active) {
+#pragma unroll
+    for (int i = 0; i < NFIN; ++i) {
+      const int hh = i ^ fj;
+      if (hh < GS) s_ml[rg][hh] = make_float2(mx[i], sm[i]);
     }
   }
-
-  // per (head, tile): max and sum of exp2, consumed by the lse kernel
-  constexpr int EPT = TILE / 64;
-  const int lane = tid & 63, wv = tid >> 6;
-  for (int hl = wv; hl < NH; hl += 4) {
-    float x[EPT];
-    float m = -INFINITY;
-#pragma unroll
-    for (int e = 0; e < EPT; ++e) {
-      const int t = e * 64 + lane;
-      x[e] = (t < tl) ? s_log[hl * LS + t] : -INFINITY;
-      m = fmaxf(m, x[e]);
+  __syncthreads();
+  const int NH = Hkv * GS;
+  for (int hl = tid; hl < NH; hl += 256) {
+    const int kv = hl / GS, hh = hl - kv * GS;
+    float M = -INFINITY;
+    for (int to = 0; to < TPI; ++to) M = fmaxf(M, s_ml[to * Hkv + kv][hh].x);
+    float L = 0.f;
+    for (int to = 0; to < TPI; ++to) {
+      const float2 e = s_ml[to * Hkv + kv][hh];
+      if (e.x != -INFINITY) L += e.y * ex2(e.x - M);
     }
-    m = wave_max(m);
-    float l = 0.f;
-#pragma unroll
-    for (int e = 0; e < EPT; ++e) l += (e * 64 + lane < tl) ? ex2(x[e] - m) : 0.f;
-    l = wave_sum(l);
-    if (lane == 0) {
-      const int head = (hl / GS) * p.G + slice * GS + (hl % GS);
-      p.partials[((size_t)b * p.Hq + head) * p.ntiles + tile] = make_float2(m, l);
-    }
+    const int head = kv * p.G + slice * GS + hh;
+    p.partials[((size_t)b * p.Hq + head) * p.ntiles + tile] = make_float2(M, L);
   }
 }
 
@@ -249,8 +300,8 @@ __global__ __launch_bounds__(64) void lse_kernel(LseParams p) {
   if (lane == 0) p.lse[(size_t)b * p.Hq + h] = Mw + log2f(Lw);
 }
 
-// votes: kVoteTile tokens per work-group, two per thread; all logit loads of a
-// thread are issued before any exp2.
+// votes: kVoteTile tokens per work-group, one per thread; a token's logits
+// for all heads are contiguous and loaded at once before any exp2.
 __global__ __launch_bounds__(256) void votes_kernel(VoteParams p) {
   __shared__ float s_lse[kMaxQHeads];
   __shared__ uint32_t s_hist[1 << kHist0Bits];
@@ -261,38 +312,39 @@ __global__ __launch_bounds__(256) void votes_kernel(VoteParams p) {
   const int start = blockIdx.x * kVoteTile;
   if (start >= len) return;
   const int tid = threadIdx.x;
-  for (int h = tid; h < p.Hq; h += 256) s_lse[h] = p.lse[(size_t)b * p.Hq + h];
+  const int Hq = p.Hq;
+  for (int h = tid; h < Hq; h += 256) s_lse[h] = p.lse[(size_t)b * Hq + h];
   if (p.do_hist)
     for (int i = tid; i < (1 << kHist0Bits); i += 256) s_hist[i] = 0u;
   __syncthreads();
 
-  const int j0 = start + tid * 2;
-  if (j0 < len) {
-    const float* lg = p.logits + (size_t)b * p.Hq * p.Lpad + j0;
-    float v0 = 0.f, v1 = 0.f;
-    constexpr int HB = 16;
-    for (int h0 = 0; h0 < p.Hq; h0 += HB) {
-      float2 sv[HB];
+  const int j = start + tid;
+  if (j < len) {
+    const float* lg = p.logits + ((size_t)b * p.Lpad + j) * Hq;
+    float v = 0.f;
+    if ((Hq & 3) == 0) {
+      constexpr int HB = 8;                      // float4 groups in flight
+      for (int h0 = 0; h0 < Hq; h0 += 4 * HB) {
+        float4 sv[HB];
 #pragma unroll
-      for (int u = 0; u < HB; ++u)
-        sv[u] = (h0 + u < p.Hq) ? *reinterpret_cast<const float2*>(lg + (size_t)(h0 + u) * p.Lpad)
-                                : make_float2(-INFINITY, -INFINITY);
+        for (int u = 0; u < HB; ++u)
+          sv[u] = (h0 + 4 * u < Hq) ? ldf4(lg + h0 + 4 * u) : make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
-      for (int u = 0; u < HB; ++u) {
-        if (h0 + u < p.Hq) {
-          const float c = s_lse[h0 + u];
-          v0 += ex2(sv[u].x - c);
-          v1 += ex2(sv[u].y - c);
+        for (int u = 0; u < HB; ++u) {
+          const int h = h0 + 4 * u;
+          if (h < Hq) {
+            v += ex2(sv[u].x - s_lse[h]);
+            v += ex2(sv[u].y - s_lse[h + 1]);
+            v += ex2(sv[u].z - s_lse[h + 2]);
+            v += ex2(sv[u].w - s_lse[h + 3]);
+          }
         }
       }
+    } else {
+      for (int h = 0; h < Hq; ++h) v += ex2(lg[h] - s_lse[h]);
     }
-    float* vo = p.votes + (size_t)b * p.vote_stride + j0;
-    vo[0] = v0;
-    if (p.do_hist) atomicAdd(&s_hist[float_key(v0) >> (32 - kHist0Bits)], 1u);
-    if (j0 + 1 < len) {
-      vo[1] = v1;
-      if (p.do_hist) atomicAdd(&s_hist[float_key(v1) >> (32 - kHist0Bits)], 1u);
-    }
+    p.votes[(size_t)b * p.vote_stride + j] = v;
+    if (p.do_hist) atomicAdd(&s_hist[float_key(v) >> (32 - kHist0Bits)], 1u);
   }
   if (!p.do_hist) return;
   __syncthreads();
@@ -314,7 +366,7 @@ constexpr int score_lpr() {
 template <int DT, int D, bool PAGED, int TILE>
 static hipError_t launch_pass1_gs(const ScoreParams& p, hipStream_t s) {
   dim3 grid(p.ntiles, p.B * p.nslices);
-  const size_t shmem = (size_t)p.Hkv * p.GS * (TILE + 1) * sizeof(float);
+  const size_t shmem = 0;
 #ifdef TS_SCORE_LPR
   constexpr int LPR = TS_SCORE_LPR;
 #else

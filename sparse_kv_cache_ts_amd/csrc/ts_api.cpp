@@ -211,11 +211,9 @@ struct ScorePlan {
   size_t ctrl, lse, partials, logits;
 };
 void plan_score(const Geo& g, int B, Carve& c, ScorePlan& s) {
-  // 256-token tiles unless that leaves fewer than two work-groups per CU (and
-  // 128 whenever a 256-token logit tile would not fit in 64 KB of LDS)
+  // 256-token tiles unless that leaves fewer than two work-groups per CU
   const long wg256 = (long)B * g.nslices * cdiv(g.max_len, 256);
-  const bool fits256 = (long)g.Hkv * g.GS * (256 + 1) * 4 <= 65536;
-  s.tile = (wg256 >= 512 && fits256) ? 256 : 128;
+  s.tile = wg256 >= 512 ? 256 : 128;
 #ifdef TS_FORCE_SCORE_TILE
   s.tile = TS_FORCE_SCORE_TILE;   // build-time override for tuning sweeps
 #endif

@@ -10,7 +10,7 @@ namespace ts {
 
 // ---- tiling constants -------------------------------------------------------
 constexpr int kScoreTileMax = 256; // largest token tile of a scoring work-group (128 or 256)
-constexpr int kVoteTile = 512;     // tokens per vote work-group (pass 2)
+constexpr int kVoteTile = 256;     // tokens per vote work-group (pass 2)
 constexpr int kTopkChunk = 4096;   // elements per top-k work-group
 constexpr int kMaxHeadsPerWG = 64; // Hkv * heads-per-slice held by one scoring WG
 constexpr int kMaxQHeads = 256;
@@ -68,7 +68,7 @@ struct ScoreParams {
   const int32_t* page_table;
   const int32_t* seq_lens;
   const int32_t* hit;       // [B] or null: sequences with hit != 0 are skipped
-  float* logits;            // [B][Hq][Lpad] base-2 logits (scale * log2 e * q.k)
+  float* logits;            // [B][Lpad][Hq] base-2 logits (scale * log2 e * q.k), token-major
   float2* partials;         // [B][Hq][ntiles] (tile max, tile sum of exp2)
   int B, Hq, Hkv, G, GS, nslices, max_len, Lpad, ntiles, ps_log2, pt_stride;
   int tile;                 // tokens per work-group: 128 or 256
