@@ -34,7 +34,7 @@ HBM_PEAK_GBPS = 8000.0
 
 def _die_multi_gpu(n):
     print(f"bench.py measures one GPU; --gpus {n} is not supported (this path has no "
-          f"multi-GPU mode; see DESIGN.md for how it would shard)", file=sys.stderr)
+          f"multi-GPU mode: each GPU would score and select its own sequences)", file=sys.stderr)
     sys.exit(2)
 
 

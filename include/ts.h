@@ -176,6 +176,9 @@ ts_status ts_decode_step(ts_sel_cache* cache, const ts_kv_layout* layout /*[host
  *   votes    [chunk][n_ctx] fp32 out: row i holds the soft vote over keys
  *            0 .. q_pos0 + i; entries past that are written as 0.
  *   Requires q_pos0 >= 0 and q_pos0 + chunk <= n_ctx.
+ *   Built for bf16, head_dim 64 or 128, 4 query heads per KV head and at most
+ *   8 KV heads; other shapes return TS_ERR_UNSUPPORTED. The workspace size
+ *   does not depend on q_pos0.
  * ts_select_prefill additionally runs step 3 on every row:
  *   idx      [chunk][k] int32 out (row i selects from its q_pos0 + i + 1 keys).
  * ------------------------------------------------------------------------- */

@@ -1,0 +1,355 @@
+// prefill.hip — soft votes of a chunked-prefill query block with bf16 MFMA.
+//
+// The per-head criticality and soft voting of the TokenSelect README ("Key
+// Takeaways", first and second points) applied to every query of a prefill
+// chunk: query i sits at position q_pos0 + i and sees keys 0 .. q_pos0 + i
+// (causal), so its vote row is
+//   v_i[j] = sum_h exp(s_hij - lse_hi),  s_hij = scale * <q_ih, k_j,kv(h)>,
+// with lse_hi the log-sum-exp of head h over the keys query i sees. This is
+// a dense Q.K^T contraction (chunk x Hq rows against n_ctx keys), so it runs
+// on v_mfma_f32_16x16x32_bf16 tiles. Lane l of a wave holds A rows l%16
+// (8 consecutive d of k-step 8*(l/16)), B columns l%16 (one key) and C rows
+// 4*(l/16)..+3, column l%16. Rows are (query, head) pairs with the head
+// fastest, so for G = 4 a lane's four C rows are one query's four heads and
+// their softmax terms add up in registers.
+//
+// Pass 1 (prefill_lse_kernel): work-group = (KV head g, block of queries, key
+// split); 4 waves x 64 rows, each wave streams the same keys. Per tile of 16
+// keys a wave computes S with 16 MFMAs (4 row tiles x 4 k-steps for d=128),
+// then an online max/sum of exp2 per row with one exp per element. The 16
+// lanes that share a row are folded with DPP at the end; each (row, split)
+// leaves a partial.
+// Merge (prefill_merge_kernel): partials -> lse per (query, head).
+// Pass 2 (prefill_votes_kernel): work-group = (block of 32 queries, key
+// split), one wave per KV head; each wave recomputes S for its 128 rows per
+// key tile, adds exp2(s - lse) over its heads, and the KV-head partial votes
+// are summed in LDS and written (zeros past the causal limit).
+#include "ts_device.h"
+
+namespace ts {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ bf16x8_t as_bf8(uint4 v) { return __builtin_bit_cast(bf16x8_t, v); }
+
+__device__ __forceinline__ f32x4_t mfma16(bf16x8_t a, bf16x8_t b, f32x4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// Work-group b runs on XCD b % 8. Renumber so that each XCD gets a contiguous
+// range of flat ids; flat ids that share a KV head's key range are adjacent,
+// so the keys they all read are fetched into one XCD's L2 once.
+__device__ __forceinline__ int xcd_flat(int b, int total) {
+  if (total & 7) return b;
+  return (b & 7) * (total >> 3) + (b >> 3);
+}
+
+// Q fragment of row tile `rt` (16 rows) and k-step `ks` for this lane.
+// Row r of the group's row space is (query qbase + r / G, head g*G + r % G).
+template <int G, int D>
+__device__ __forceinline__ uint4 load_q_frag(const PrefillParams& p, int g, int qbase, int rt, int ks,
+                                             int lane) {
+  const int r = rt * 16 + (lane & 15);
+  const int qi = qbase + r / G;
+  const int head = g * G + r % G;
+  if (qi >= p.chunk) return make_uint4(0, 0, 0, 0);
+  const char* base = (const char*)p.q + (((size_t)qi * p.Hq + head) * D + ks * 32 + 8 * (lane >> 4)) * 2;
+  return ld16(base);
+}
+
+// K fragment (16 keys from kb) of k-step ks for KV head g. Ordinary (cached)
+// loads: every query block of the chunk reads the same keys.
+template <int D>
+__device__ __forceinline__ uint4 load_k_frag(const PrefillParams& p, int g, int kb, int ks, int lane) {
+  const int key = kb + (lane & 15);
+  if (key >= p.n_ctx) return make_uint4(0, 0, 0, 0);
+  const char* base = (const char*)p.k + (((size_t)key * p.Hkv + g) * D + ks * 32 + 8 * (lane >> 4)) * 2;
+  return ld16(base);
+}
+
+template <int RT, int KS>
+__device__ __forceinline__ void qk_tile(const bf16x8_t (&qf)[RT][KS], const uint4 (&kf)[KS], f32x4_t (&s)[RT]) {
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt) {
+    s[rt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) s[rt] = mfma16(qf[rt][ks], as_bf8(kf[ks]), s[rt]);
+  }
+}
+
+// ---- pass 1 -----------------------------------------------------------------
+// Keys go in groups of two 16-key tiles. Per (row, group) the running maximum
+// M (base-2 units, scale2 * s) is raised once and the sum rescaled once, then
+// each element adds exp2(scale2 * s - M): about four VALU operations and 1.5
+// exponentials per element. Masked elements are -inf and add 0. M starts at
+// a finite -1e30, so a row with nothing seen yet rescales by exp2(0) = 1 and
+// no inf - inf or 0 * inf arises.
+template <int G, int D>
+__global__ __launch_bounds__(256) void prefill_lse_kernel(PrefillParams p) {
+  constexpr int KS = D / 32;      // k-steps per tile
+  constexpr int RT = 4;           // row tiles per wave (64 rows)
+  constexpr int QB = 256 / G;     // queries per work-group (4 waves x 64 rows)
+  constexpr int QW = 64 / G;      // queries per wave
+  const int nqb = (p.chunk + QB - 1) / QB;
+  const int f = xcd_flat(blockIdx.x, gridDim.x);
+  const int qblk = f % nqb;
+  const int g = (f / nqb) % p.Hkv;
+  const int split = f / (nqb * p.Hkv);
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int qbase = qblk * QB + w * QW;   // first query of this wave
+  if (qbase >= p.chunk) return;           // no rows: this wave has nothing to write
+  const int qlast = min(qbase + QW, p.chunk) - 1;
+  const int k0 = split * p.key_split;
+  const int k1 = min(p.n_ctx, k0 + p.key_split);
+  const int kend = min(k1, p.q_pos0 + qlast + 1);     // keys no row of this wave sees start here
+  const int kall = p.q_pos0 + qbase + 1;              // keys below this every row sees
+
+  bf16x8_t qf[RT][KS];
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) qf[rt][ks] = as_bf8(load_q_frag<G, D>(p, g, qbase, rt, ks, lane));
+
+  float M[RT][4], S[RT][4];
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) { M[rt][i] = -1e30f; S[rt][i] = 0.f; }
+  const float sc2 = p.scale2;
+
+  uint4 ka[KS], kb2[KS], na[KS], nb[KS];
+  if (k0 < kend) {
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      ka[ks] = load_k_frag<D>(p, g, k0, ks, lane);
+      kb2[ks] = load_k_frag<D>(p, g, k0 + 16, ks, lane);
+    }
+  }
+  for (int kb = k0; kb < kend; kb += 32) {
+    if (kb + 32 < kend) {
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        na[ks] = load_k_frag<D>(p, g, kb + 32, ks, lane);
+        nb[ks] = load_k_frag<D>(p, g, kb + 48, ks, lane);
+      }
+    }
+    f32x4_t s0[RT], s1[RT];
+    qk_tile<RT, KS>(qf, ka, s0);
+    qk_tile<RT, KS>(qf, kb2, s1);
+    if (kb + 32 <= min(kall, kend)) {
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float a = s0[rt][i], b = s1[rt][i];
+          const float mn = fmaxf(M[rt][i], fmaxf(a, b) * sc2);
+          const float r = ex2(M[rt][i] - mn);
+          S[rt][i] = fmaf(S[rt][i], r, ex2(fmaf(a, sc2, -mn))) + ex2(fmaf(b, sc2, -mn));
+          M[rt][i] = mn;
+        }
+    } else {
+      // causal edge or end of the range: query qi sees keys <= q_pos0 + qi
+      const int key = kb + (lane & 15);
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int lim = min(kend - 1, p.q_pos0 + qbase + (rt * 16 + 4 * (lane >> 4) + i) / G);
+          const float a = key <= lim ? s0[rt][i] : -INFINITY;
+          const float b = key + 16 <= lim ? s1[rt][i] : -INFINITY;
+          const float mn = fmaxf(M[rt][i], fmaxf(a, b) * sc2);
+          const float r = ex2(M[rt][i] - mn);
+          S[rt][i] = fmaf(S[rt][i], r, ex2(fmaf(a, sc2, -mn))) + ex2(fmaf(b, sc2, -mn));
+          M[rt][i] = mn;
+        }
+    }
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      ka[ks] = na[ks];
+      kb2[ks] = nb[ks];
+    }
+  }
+
+  // fold the 16 lanes (key columns) that share each row
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      float m = M[rt][i], l = S[rt][i];
+#pragma unroll
+      for (int o = 1; o < 16; o <<= 1) {
+        const float mo = __shfl_xor(m, o), lo = __shfl_xor(l, o);
+        const float nm = fmaxf(m, mo);
+        l = l * ex2(m - nm) + lo * ex2(mo - nm);
+        m = nm;
+      }
+      M[rt][i] = m;
+      S[rt][i] = l;
+    }
+  if ((lane & 15) == 0) {
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = rt * 16 + 4 * (lane >> 4) + i;
+        const int qi = qbase + r / G;
+        const int head = g * G + r % G;
+        if (qi < p.chunk)
+          p.lse_part[((size_t)qi * p.Hq + head) * p.nsplit1 + split] = make_float2(M[rt][i], S[rt][i]);
+      }
+  }
+}
+
+// partials of each (query, head) over the key splits -> base-2 log-sum-exp.
+// A split that no key of the row reaches has sum 0 and adds nothing.
+__global__ __launch_bounds__(256) void prefill_merge_kernel(PrefillParams p) {
+  const int row = blockIdx.x * 256 + threadIdx.x;   // query * Hq + head
+  if (row >= p.chunk * p.Hq) return;
+  const int qi = row / p.Hq;
+  // splits at or past the row's causal limit were never written
+  const int ns = min(p.nsplit1, (p.q_pos0 + qi) / p.key_split + 1);
+  const float2* pp = p.lse_part + (size_t)row * p.nsplit1;
+  float M = -INFINITY;
+  for (int s = 0; s < ns; ++s) M = fmaxf(M, pp[s].x);
+  float L = 0.f;
+  for (int s = 0; s < ns; ++s) L += pp[s].y * ex2(pp[s].x - M);
+  p.lse[row] = M + log2f(L);
+}
+
+// ---- pass 2 -----------------------------------------------------------------
+template <int G, int D>
+__global__ __launch_bounds__(512) void prefill_votes_kernel(PrefillParams p) {
+  constexpr int KS = D / 32;
+  constexpr int RT = 8;           // row tiles per wave (128 rows of one KV head)
+  constexpr int QB = 128 / G;     // queries per work-group
+  static_assert(G == 4, "a lane's four C rows must be one query's four heads");
+  __shared__ float s_v[2][8][QB][16];           // [buffer][KV head][query][key]
+  const int nqb = (p.chunk + QB - 1) / QB;
+  const int f = xcd_flat(blockIdx.x, gridDim.x);
+  const int qblk = f % nqb;
+  const int split = f / nqb;
+  const int lane = threadIdx.x & 63, g = threadIdx.x >> 6;   // one wave per KV head
+  const int nw = blockDim.x >> 6;
+  const int qbase = qblk * QB;
+  const int qlast = min(qbase + QB, p.chunk) - 1;
+  const int k0 = split * p.key_split2;
+  const int k1 = min(p.n_ctx, k0 + p.key_split2);
+  const int kend = min(k1, p.q_pos0 + qlast + 1);   // keys from here on: zero votes
+  const int kall = p.q_pos0 + qbase + 1;            // keys below this: no mask
+
+  bf16x8_t qf[RT][KS];
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) qf[rt][ks] = as_bf8(load_q_frag<G, D>(p, g, qbase, rt, ks, lane));
+  float lse[RT][4];
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = rt * 16 + 4 * (lane >> 4) + i;
+      const int qi = qbase + r / G;
+      const int head = g * G + r % G;
+      lse[rt][i] = (qi < p.chunk) ? p.lse[(size_t)qi * p.Hq + head] : INFINITY;
+    }
+  const float sc2 = p.scale2;
+
+  uint4 kf[KS], kn[KS];
+  if (k0 < kend) {
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) kf[ks] = load_k_frag<D>(p, g, k0, ks, lane);
+  }
+  int buf = 0;
+  for (int kb = k0; kb < kend; kb += 16) {
+    if (kb + 16 < kend) {
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) kn[ks] = load_k_frag<D>(p, g, kb + 16, ks, lane);
+    }
+    f32x4_t s[RT];
+    qk_tile<RT, KS>(qf, kf, s);
+    // a lane's four C rows are one query's four heads: add their terms here
+    if (kb + 16 <= kall) {
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt) {
+        float v = 0.f;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) v += ex2(fmaf(s[rt][i], sc2, -lse[rt][i]));
+        s_v[buf][g][rt * 4 + (lane >> 4)][lane & 15] = v;
+      }
+    } else {
+      const int key = kb + (lane & 15);
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt) {
+        const int qi = qbase + rt * 4 + (lane >> 4);
+        const bool ok = key <= p.q_pos0 + qi;
+        float v = 0.f;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) v += ex2(fmaf(s[rt][i], sc2, -lse[rt][i]));
+        s_v[buf][g][rt * 4 + (lane >> 4)][lane & 15] = ok ? v : 0.f;
+      }
+    }
+    __syncthreads();
+    // sum over the KV heads and write the tile's votes
+    for (int e = threadIdx.x; e < QB * 16; e += blockDim.x) {
+      const int ql = e >> 4, c = e & 15;
+      float v = 0.f;
+      for (int gg = 0; gg < nw; ++gg) v += s_v[buf][gg][ql][c];
+      const int qi = qbase + ql, kk = kb + c;
+      if (qi < p.chunk && kk < k1) p.votes[(size_t)qi * p.n_ctx + kk] = v;
+    }
+    buf ^= 1;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) kf[ks] = kn[ks];
+  }
+  // keys that no query of this block sees
+  const int z0 = max(k0, kend);
+  for (int e = threadIdx.x; e < QB * (k1 - z0); e += blockDim.x) {
+    const int ql = e / (k1 - z0), kk = z0 + e % (k1 - z0);
+    if (qbase + ql < p.chunk) p.votes[(size_t)(qbase + ql) * p.n_ctx + kk] = 0.f;
+  }
+}
+
+template <int D>
+static hipError_t launch_lse_g(const PrefillParams& p, hipStream_t s) {
+  const int qb = 256 / p.G;
+  dim3 grid(((p.chunk + qb - 1) / qb) * p.Hkv * p.nsplit1);
+  switch (p.G) {
+    case 4: hipLaunchKernelGGL((prefill_lse_kernel<4, D>), grid, dim3(256), 0, s, p); break;
+    // other group sizes are not built (rejected on the host)
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_prefill_lse(const PrefillParams& p, hipStream_t s) {
+  if (p.D == 128) return launch_lse_g<128>(p, s);
+  if (p.D == 64) return launch_lse_g<64>(p, s);
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_prefill_merge(const PrefillParams& p, hipStream_t s) {
+  hipLaunchKernelGGL(prefill_merge_kernel, dim3((p.chunk * p.Hq + 255) / 256), dim3(256), 0, s, p);
+  return hipGetLastError();
+}
+
+template <int D>
+static hipError_t launch_votes_g(const PrefillParams& p, hipStream_t s) {
+  const int qb = 128 / p.G;
+  dim3 grid(((p.chunk + qb - 1) / qb) * p.nsplit2);
+  dim3 block(64 * p.Hkv);
+  switch (p.G) {
+    case 4: hipLaunchKernelGGL((prefill_votes_kernel<4, D>), grid, block, 0, s, p); break;
+    // other group sizes are not built (rejected on the host)
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_prefill_votes(const PrefillParams& p, hipStream_t s) {
+  if (p.D == 128) return launch_votes_g<128>(p, s);
+  if (p.D == 64) return launch_votes_g<64>(p, s);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace ts

@@ -698,28 +698,109 @@ ts_status ts_decode_step(ts_sel_cache* cache, const ts_kv_layout* L, int32_t bat
   return ok();
 }
 
+}  // extern "C"
+
 // ------------------------------------------------------------ prefill
+
+namespace {
+
+struct PrefillPlan {
+  PrefillParams pp;
+  size_t lse_part, lse, total_score;
+  TopkPlan t;
+  size_t total;
+};
+
+ts_status plan_prefill(const ts_kv_layout* L, int chunk, int q_pos0, int n_ctx, int k, bool select,
+                       PrefillPlan* P) {
+  Geo g;
+  TS_TRY(check_layout(L, 1, &g));
+  if (g.dtype != TS_BF16) return fail(TS_ERR_UNSUPPORTED, "prefill scoring needs bf16 q and K");
+  if (g.paged) return fail(TS_ERR_UNSUPPORTED, "prefill scoring needs a contiguous K");
+  if (g.G != 4) return fail(TS_ERR_UNSUPPORTED, "prefill scoring is built for 4 query heads per KV head");
+  if (g.Hkv > 8) return fail(TS_ERR_UNSUPPORTED, "prefill scoring supports at most 8 KV heads");
+  if (chunk < 1 || n_ctx < 1) return fail(TS_ERR_INVALID_ARG, "chunk and n_ctx must be >= 1");
+  if (q_pos0 < 0 || (long)q_pos0 + chunk > n_ctx)
+    return fail(TS_ERR_INVALID_ARG, "need 0 <= q_pos0 and q_pos0 + chunk <= n_ctx");
+  if (n_ctx > g.max_len) return fail(TS_ERR_INVALID_ARG, "n_ctx exceeds layout max_len");
+  if (select && k < 1) return fail(TS_ERR_INVALID_ARG, "k must be >= 1");
+  PrefillParams& p = P->pp;
+  p = PrefillParams{};
+  p.chunk = chunk;
+  p.q_pos0 = q_pos0;
+  p.n_ctx = n_ctx;
+  p.Hq = g.Hq;
+  p.Hkv = g.Hkv;
+  p.G = g.G;
+  p.D = g.d;
+  p.scale2 = g.scale * kLog2eHost;
+  // pass 1: two resident work-groups of 4 waves per CU; pass 2: one of 8 waves
+  const int qb1 = cdiv(chunk, 256 / g.G);
+  int ns1 = std::max(1, 512 / (qb1 * g.Hkv));
+  p.key_split = cdiv(cdiv(n_ctx, ns1), 32) * 32;
+  p.nsplit1 = cdiv(n_ctx, p.key_split);
+  const int qb2 = cdiv(chunk, 128 / g.G);
+  int ns2 = std::max(1, 256 / qb2);
+  p.key_split2 = cdiv(cdiv(n_ctx, ns2), 16) * 16;
+  p.nsplit2 = cdiv(n_ctx, p.key_split2);
+  Carve c;
+  P->lse_part = c.take((size_t)chunk * g.Hq * p.nsplit1 * 8);
+  P->lse = c.take((size_t)chunk * g.Hq * 4);
+  P->total_score = c.off;
+  if (select) plan_topk(chunk, n_ctx, c, P->t, true);
+  P->total = c.off;
+  return TS_OK;
+}
+
+ts_status run_prefill_score(PrefillPlan& P, const void* q, const void* k_cache, float* votes,
+                            void* ws, hipStream_t st) {
+  PrefillParams& p = P.pp;
+  p.q = q;
+  p.k = k_cache;
+  p.votes = votes;
+  p.lse_part = at<float2>(ws, P.lse_part);
+  p.lse = at<float>(ws, P.lse);
+  TS_LAUNCH_K(kKPrefillLse, launch_prefill_lse(p, st), "prefill log-sum-exp");
+  TS_LAUNCH_K(kKPrefillLse, launch_prefill_merge(p, st), "prefill merge");
+  TS_LAUNCH_K(kKPrefillVotes, launch_prefill_votes(p, st), "prefill votes");
+  return TS_OK;
+}
+
+}  // namespace
+
+extern "C" {
 
 ts_status ts_score_prefill_workspace_size(const ts_kv_layout* L, int32_t chunk, int32_t n_ctx,
                                           int32_t k, size_t* bytes) {
-  (void)L; (void)chunk; (void)n_ctx; (void)k; (void)bytes;
-  return fail(TS_ERR_UNSUPPORTED, "prefill scoring not built yet");
+  if (!bytes) return fail(TS_ERR_INVALID_ARG, "bytes is NULL");
+  PrefillPlan P;
+  TS_TRY(plan_prefill(L, chunk, n_ctx - chunk >= 0 ? n_ctx - chunk : 0, n_ctx, k, true, &P));
+  *bytes = P.total;
+  return ok();
 }
 
 ts_status ts_score_prefill(const ts_kv_layout* L, int32_t chunk, int32_t q_pos0, const void* q,
                            const void* k_cache, int32_t n_ctx, float* votes, void* ws,
                            size_t ws_bytes, void* stream) {
-  (void)L; (void)chunk; (void)q_pos0; (void)q; (void)k_cache; (void)n_ctx; (void)votes;
-  (void)ws; (void)ws_bytes; (void)stream;
-  return fail(TS_ERR_UNSUPPORTED, "prefill scoring not built yet");
+  PrefillPlan P;
+  TS_TRY(plan_prefill(L, chunk, q_pos0, n_ctx, 1, false, &P));
+  if (!q || !k_cache || !votes) return fail(TS_ERR_INVALID_ARG, "NULL tensor pointer");
+  TS_TRY(check_ws(ws, ws_bytes, P.total_score));
+  TS_TRY(run_prefill_score(P, q, k_cache, votes, ws, static_cast<hipStream_t>(stream)));
+  return ok();
 }
 
 ts_status ts_select_prefill(const ts_kv_layout* L, int32_t chunk, int32_t q_pos0, const void* q,
                             const void* k_cache, int32_t n_ctx, int32_t k, float* votes,
                             int32_t* idx, void* ws, size_t ws_bytes, void* stream) {
-  (void)L; (void)chunk; (void)q_pos0; (void)q; (void)k_cache; (void)n_ctx; (void)k; (void)votes;
-  (void)idx; (void)ws; (void)ws_bytes; (void)stream;
-  return fail(TS_ERR_UNSUPPORTED, "prefill scoring not built yet");
+  PrefillPlan P;
+  TS_TRY(plan_prefill(L, chunk, q_pos0, n_ctx, k, true, &P));
+  if (!q || !k_cache || !votes || !idx) return fail(TS_ERR_INVALID_ARG, "NULL tensor pointer");
+  TS_TRY(check_ws(ws, ws_bytes, P.total));
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  TS_TRY(run_prefill_score(P, q, k_cache, votes, ws, st));
+  TS_TRY(run_topk(chunk, n_ctx, votes, nullptr, q_pos0 + 1, k, idx, ws, P.t, n_ctx, st));
+  return ok();
 }
 
 // ------------------------------------------------------------ kernel timing

@@ -138,9 +138,12 @@ struct CombineParams {
 struct PrefillParams {
   const void* q;            // [chunk][Hq][d] bf16
   const void* k;            // [n_ctx][Hkv][d] bf16
+  float2* lse_part;         // [chunk][Hq][nsplit1] (max, sum of exp2) per key split
   float* lse;               // [chunk][Hq] base-2 log-sum-exp per query and head
   float* votes;             // [chunk][n_ctx]
-  int chunk, q_pos0, n_ctx, Hq, Hkv, G;
+  int chunk, q_pos0, n_ctx, Hq, Hkv, G, D;
+  int key_split, nsplit1;   // keys per work-group and splits of the log-sum-exp pass
+  int key_split2, nsplit2;  // the same for the vote pass
   float scale2;
 };
 
@@ -156,6 +159,7 @@ hipError_t launch_topk_finalize(const TopkParams& p, hipStream_t s);
 hipError_t launch_attend(int dtype, int d, bool paged, const AttendParams& p, hipStream_t s);
 hipError_t launch_combine(const CombineParams& p, hipStream_t s);
 hipError_t launch_prefill_lse(const PrefillParams& p, hipStream_t s);
+hipError_t launch_prefill_merge(const PrefillParams& p, hipStream_t s);
 hipError_t launch_prefill_votes(const PrefillParams& p, hipStream_t s);
 
 }  // namespace ts

@@ -12,7 +12,7 @@ from tests.parity import check_attention, check_selection, np32, np64
 
 pytestmark = pytest.mark.gpu
 
-# vote tolerance, derived in the design doc: fp32 logits carry an absolute error of
+# vote tolerance: fp32 logits carry an absolute error of
 # at most a few 1e-5 (base e) for logits of O(50); a vote is a sum of
 # exp(s - lse) terms, so its relative error is bounded by about twice that.
 VOTE_RTOL = 2e-4
