@@ -30,12 +30,96 @@ import sys
 import time
 
 HBM_PEAK_GBPS = 8000.0
+MFMA_BF16_PEAK_TFLOPS = 2500.0
+ROOT = os.path.dirname(os.path.abspath(__file__))
+# HBM bytes of the K-scan kernel from two rocprofv3 counter runs, scaled by a
+# plain copy kernel of known size; valid only for the kernel sources it names
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "score_pass1_qwen2-7b_n131072_traffic.txt")
+KSCAN_SOURCES = ["sparse_kv_cache_ts_amd/csrc/score.hip", "sparse_kv_cache_ts_amd/csrc/ts_device.h",
+                 "sparse_kv_cache_ts_amd/csrc/ts_internal.h"]
 
 
 def _die_multi_gpu(n):
     print(f"bench.py measures one GPU; --gpus {n} is not supported (this path has no "
           f"multi-GPU mode: each GPU would score and select its own sequences)", file=sys.stderr)
     sys.exit(2)
+
+
+def kscan_source_hash() -> str:
+    import hashlib
+    h = hashlib.sha256()
+    for f in KSCAN_SOURCES:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def stored_traffic():
+    """Measured HBM bytes per K-scan launch, or None when the kernel changed since."""
+    try:
+        kv = {}
+        with open(TRAFFIC_FILE) as fh:
+            for ln in fh:
+                if ":" in ln and not ln.startswith(" "):
+                    a, b = ln.split(":", 1)
+                    kv[a.strip()] = b.strip()
+        if kv.get("kernel_sources_sha256_16") != kscan_source_hash():
+            return None
+        return int(kv["hbm_bytes_per_launch"])
+    except (OSError, KeyError, ValueError):
+        return None
+
+
+def calibrate_copy(nbytes=512 << 20, reps=5):
+    """A plain elementwise copy of known size, for scaling HBM byte counters."""
+    import torch
+    src = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(reps):
+        torch.mul(src, 1.0, out=dst)
+    torch.cuda.synchronize()
+    print(json.dumps({"calibration": "copy", "bytes_read": nbytes, "bytes_written": nbytes,
+                      "launches": reps}), flush=True)
+
+
+def measure_prefill(ts, W, reps=10, warmup=3):
+    """512-query chunk over 65536 keys: soft votes (two MFMA passes) and per-row top-k."""
+    import torch
+    cfg = W.PREFILL_64K
+    x = W.gen_prefill(cfg, device="cuda")
+    q0 = x["q_pos0"]
+    votes = torch.empty(cfg.chunk, cfg.n_ctx, dtype=torch.float32, device="cuda")
+    idx = torch.empty(cfg.chunk, cfg.k, dtype=torch.int32, device="cuda")
+    for _ in range(warmup):
+        ts.select_prefill(x["q"], x["k_cache"], q0, cfg.k, votes=votes, idx=idx)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(reps):
+        ts.select_prefill(x["q"], x["k_cache"], q0, cfg.k, votes=votes, idx=idx)
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t0) / reps
+    ts.profile_reset()
+    ts.profile_enable(True)
+    for _ in range(reps):
+        ts.select_prefill(x["q"], x["k_cache"], q0, cfg.k, votes=votes, idx=idx)
+    torch.cuda.synchronize()
+    ts.profile_enable(False)
+    kern = {n: (c, ms) for n, (c, ms) in ts.profile_read().items() if c}
+    visible = sum(q0 + i + 1 for i in range(cfg.chunk))
+    flop = 2.0 * cfg.num_q_heads * cfg.head_dim * visible          # one Q.K^T product
+    t_lse = kern["prefill_lse"][1] / reps * 1e-3                   # pass 1 + merge
+    t_vote = kern["prefill_votes"][1] / reps * 1e-3
+    # pass 1 and pass 2 each evaluate every visible product once
+    mfma_tflops = 2 * flop / (t_lse + t_vote) / 1e12
+    del x, votes, idx
+    torch.cuda.empty_cache()
+    return {"workload": "512 queries x 65536 keys, 32/8 heads, d=128, bf16, top-k 4096",
+            "us_per_chunk": round(1e6 * wall, 1),
+            "scoring_us": round(1e6 * (t_lse + t_vote), 1),
+            "kernels_us": {n: round(1e3 * ms / reps, 1) for n, (c, ms) in kern.items()},
+            "qkt_gflop_per_pass": round(flop / 1e9, 1),
+            "mfma_tflops": round(mfma_tflops, 1),
+            "mfma_frac": round(mfma_tflops / MFMA_BF16_PEAK_TFLOPS, 4)}
 
 
 def kv_bytes_per_token(cfg) -> int:
@@ -133,6 +217,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-profile", action="store_true")
     ap.add_argument("--no-hit", action="store_true", help="skip the selection-reuse measurement")
+    ap.add_argument("--no-prefill", action="store_true", help="skip the prefill-chunk measurement")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="only run a plain 512 MiB copy kernel (for HBM byte counters)")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -142,7 +229,10 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
-    sys.path.insert(0, os.path.dirname(os.path.abspath(__file__)))
+    if args.calibrate_copy:
+        calibrate_copy()
+        return
+    sys.path.insert(0, ROOT)
     import sparse_kv_cache_ts_amd as ts
     import workloads as W
     ts.load()
@@ -165,7 +255,8 @@ def main():
         t_scan = ku["score_pass1"] * 1e-6
         achieved = kscan_bytes / t_scan / 1e9
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
-                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": None,
+                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
+                "traffic": stored_traffic(),
                 "kernel": "score_pass1 (K-scan)", "bytes_per_launch": kscan_bytes,
                 "avg_launch_us": round(ku["score_pass1"], 2)}
         t_att = ku["attend"] * 1e-6
@@ -180,6 +271,9 @@ def main():
     extra["step_algorithmic_bytes"] = kscan_bytes + gather_bytes
     extra["whole_step_hbm_frac"] = round(
         (kscan_bytes + gather_bytes) / (miss["ms_per_step"] * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4)
+
+    if not args.no_prefill:
+        extra["prefill_chunk"] = measure_prefill(ts, W)
 
     cpu = None
     if not args.no_cpu_baseline:

@@ -72,3 +72,65 @@ def rel_err(a: np.ndarray, b: np.ndarray) -> float:
     d = np.abs(a - b).max()
     s = np.abs(b).max()
     return float(d / s) if s > 0 else float(d)
+
+
+def oracle_votes(q64: np.ndarray, K32: np.ndarray, n: int) -> np.ndarray:
+    from oracle import ts_oracle as O
+    return O.soft_vote(O.head_softmax(O.logits(q64, K32[:n])))
+
+
+def check_run(ts, rc, mode: int, theta: float, sel_steps=None, att_steps=None, device="cuda"):
+    """Runs rc.steps decode steps of a paged selection-cache run through the C ABI
+    and checks them against the oracle. Every hit/miss decision is checked
+    (except cosines within 1e-9 of theta); a hit must repeat the previous
+    selection exactly. Selections of misses are checked at `sel_steps`, and
+    attention outputs at `att_steps` (None: every step). The oracle's cache
+    state follows the GPU's decisions and selections. Returns hits [T][B]."""
+    import math
+    import workloads as W
+    from oracle import ts_oracle as O
+    x = W.gen_run(rc, device=device)
+    lens = x["seq_lens"].tolist()
+    B = rc.batch
+    cache = ts.SelCache(B, rc.num_q_heads, rc.head_dim, rc.k, mode=mode)
+    pool_k, pool_v, pt = x["k_pool"], x["v_pool"], x["page_table"]
+    hits, sels, outs = [], [], []
+    for t in range(rc.steps):
+        out, idx, hit = cache.decode_step(x["queries"][t], pool_k, pool_v, x["seq_lens"], theta,
+                                          page_table=pt)
+        hits.append(hit.clone())
+        sels.append(idx.clone())
+        outs.append(out.clone())
+    torch.cuda.synchronize()
+    h, m = cache.stats(B)
+    cache.close()
+    hits = torch.stack(hits).cpu().numpy()
+    sels = torch.stack(sels).cpu().numpy()
+    outs = torch.stack(outs).cpu().numpy().astype(np.float64)
+    assert h == hits.sum(axis=0).tolist() and m == (rc.steps - hits.sum(axis=0)).tolist()
+    kp, vp, ptn = np32(pool_k), np32(pool_v), pt.cpu().numpy()
+    del pool_k, pool_v, x["k_pool"], x["v_pool"]
+    Q = np64(x["queries"])
+    sel_set = None if sel_steps is None else set(sel_steps)
+    att_set = None if att_steps is None else set(att_steps)
+    for b in range(B):
+        Kb = O.paged_to_contiguous(kp, ptn[b], lens[b])
+        Vb = O.paged_to_contiguous(vp, ptn[b], lens[b])
+        ref_cache = O.SelectionCache(mode)
+        for t in range(rc.steps):
+            hit_ref, c = ref_cache.decide(Q[t, b], theta)
+            if abs(c - theta) > 1e-9 or math.isnan(c):
+                assert bool(hits[t, b]) == hit_ref, f"seq {b} step {t}: cos {c}"
+            if hits[t, b]:
+                assert np.array_equal(sels[t, b], sels[t - 1, b])
+            elif sel_set is None or t in sel_set:
+                check_selection(sels[t, b], oracle_votes(Q[t, b], Kb, lens[b]), rc.k)
+            if att_set is None or t in att_set:
+                ref = O.sparse_attention(Q[t, b], Kb, Vb, sels[t, b])
+                check_attention(outs[t, b], ref, 1e-2)
+            # advance the oracle state with the GPU's decision and selection
+            if mode == 0 or not hits[t, b]:
+                ref_cache.prev_q = Q[t, b].copy()
+            ref_cache.prev_S = sels[t, b]
+            ref_cache.valid = True
+    return hits

@@ -1,6 +1,5 @@
 """GPU parity of the decode path (scoring, votes, top-k, sparse attention,
 Selection Cache, decode step) against the fp64 oracle, through the C ABI."""
-import math
 
 import numpy as np
 import pytest
@@ -8,7 +7,7 @@ import torch
 
 import workloads as W
 from oracle import ts_oracle as O
-from tests.parity import check_attention, check_selection, np32, np64
+from tests.parity import check_attention, check_run, check_selection, np32, np64
 
 pytestmark = pytest.mark.gpu
 
@@ -242,55 +241,10 @@ def test_decode_step_edge_cases(gpu_lib):
             check_attention(np64(out)[b], ref, 1e-2)
 
 
-def _run_case(ts, rc, mode, theta):
-    x = W.gen_run(rc, device="cuda")
-    lens = x["seq_lens"].tolist()
-    B = rc.batch
-    cache = ts.SelCache(B, rc.num_q_heads, rc.head_dim, rc.k, mode=mode)
-    pool_k, pool_v, pt = x["k_pool"], x["v_pool"], x["page_table"]
-    hits, sels, outs = [], [], []
-    for t in range(rc.steps):
-        out, idx, hit = cache.decode_step(x["queries"][t], pool_k, pool_v, x["seq_lens"], theta,
-                                          page_table=pt)
-        hits.append(hit.clone())
-        sels.append(idx.clone())
-        outs.append(out.clone())
-    torch.cuda.synchronize()
-    hits = torch.stack(hits).cpu().numpy()
-    sels = torch.stack(sels).cpu().numpy()
-    outs = torch.stack(outs).cpu().numpy().astype(np.float64)
-    kp, vp, ptn = np32(pool_k), np32(pool_v), pt.cpu().numpy()
-    Q = np64(x["queries"])
-    for b in range(B):
-        Kb = O.paged_to_contiguous(kp, ptn[b], lens[b])
-        Vb = O.paged_to_contiguous(vp, ptn[b], lens[b])
-        ref_cache = O.SelectionCache(mode)
-        for t in range(rc.steps):
-            hit_ref, c = ref_cache.decide(Q[t, b], theta)
-            if abs(c - theta) > 1e-9 or math.isnan(c):
-                assert bool(hits[t, b]) == hit_ref, f"seq {b} step {t}: cos {c}"
-            if not hits[t, b]:
-                v_ref = _oracle_votes(Q[t, b], Kb, lens[b])
-                check_selection(sels[t, b], v_ref, rc.k)
-            else:
-                assert np.array_equal(sels[t, b], sels[t - 1, b])
-            ref = O.sparse_attention(Q[t, b], Kb, Vb, sels[t, b])
-            check_attention(outs[t, b], ref, 1e-2)
-            # advance the oracle state with the GPU's decision and selection
-            if mode == 0 or not hits[t, b]:
-                ref_cache.prev_q = Q[t, b].copy()
-            ref_cache.prev_S = sels[t, b]
-            ref_cache.valid = True
-    h, m = cache.stats(B)
-    assert h == hits.sum(axis=0).tolist() and m == (rc.steps - hits.sum(axis=0)).tolist()
-    cache.close()
-    return hits
-
-
 def test_selcache_run_mode0(gpu_lib):
     rc = W.RunConfig("small-run", steps=70, batch=3, num_q_heads=8, num_kv_heads=2, head_dim=64,
                      min_len=300, max_len=3000, dtype="bf16", k=64, seed=41)
-    hits = _run_case(gpu_lib, rc, 0, 0.9)
+    hits = check_run(gpu_lib, rc, 0, 0.9)
     # drift (cos ~0.95) hits, the jumps at t % 32 == 0 miss
     for t in range(rc.steps):
         assert (hits[t] == (0 if t % 32 == 0 else 1)).all()
@@ -299,7 +253,7 @@ def test_selcache_run_mode0(gpu_lib):
 def test_selcache_run_mode1(gpu_lib):
     rc = W.RunConfig("small-run-anchor", steps=40, batch=2, num_q_heads=8, num_kv_heads=2,
                      head_dim=128, min_len=500, max_len=2000, dtype="bf16", k=100, seed=42)
-    hits = _run_case(gpu_lib, rc, 1, 0.9)
+    hits = check_run(gpu_lib, rc, 1, 0.9)
     assert 0 < hits.sum() < hits.size
 
 
