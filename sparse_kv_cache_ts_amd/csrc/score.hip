@@ -14,9 +14,12 @@
 // the row-group -> KV-head map is fixed, each lane keeps the query slice of
 // its KV head's query-head group in registers for the whole tile. bf16 rows
 // use v_dot2c_f32_bf16 (two bf16 products per instruction, fp32 accumulate);
-// the LPR partial sums are combined with DPP row operations. Logits (base 2:
-// scale*log2(e)*q.k) land in LDS, are written once, coalesced, to the logit
-// buffer, and each (head, tile) leaves its max and sum of exp2.
+// the LPR partial sums are combined with DPP row operations (a reduce-scatter
+// that leaves each lane a few fully summed heads). Logits (base 2:
+// scale*log2(e)*q.k) are stored token-major, [B][Lpad][Hq], straight from the
+// registers: a token's Hq logits are contiguous, so the lanes of a row group
+// write one short contiguous run. Each (head, tile) leaves its max and sum of
+// exp2, folded from per-lane online values through a small LDS table.
 //
 // Pass 2 (votes_kernel): every work-group first folds the tile partials into
 // each head's log-sum-exp (redundantly: a few KB from L2, and no cross-work-
