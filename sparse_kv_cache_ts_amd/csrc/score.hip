@@ -27,7 +27,7 @@
 // multi-XCD part), then turns its logits into votes v[j] = sum_h
 // exp2(s[h,j] - lse[h]) and, for the decode path, adds them to the first
 // radix histogram of the top-k.
-#include "ts_device.h"
+#include "selcache.h"
 
 namespace ts {
 
@@ -100,18 +100,30 @@ __global__ __launch_bounds__(256) void score_pass1_kernel(ScoreParams p) {
   static_assert(TILE % 64 == 0 && TILE <= kScoreTileMax, "tile");
 
   __shared__ float2 s_ml[RG][GS];    // per (row group, head): running (max, sum of exp2)
+  __shared__ double s_red[3][4];
+  __shared__ int s_hit;
   __shared__ long long s_page[PAGED ? TILE : 1];
+  extern __shared__ float s_logit[];  // [TILE][Hkv * GS] this tile's logits, token-major
 
   const int tile = blockIdx.x;
   const int b = blockIdx.y / p.nslices;
   const int slice = blockIdx.y - b * p.nslices;
-  if (p.hit && p.hit[b]) return;
+  const bool decide = p.cache.prev_q != nullptr;
+  if (!decide && p.hit && p.hit[b]) return;
   const int len = p.seq_lens[b];
   const int t0 = tile * TILE;
-  if (t0 >= len) return;
+  const int tid = threadIdx.x;
+  if (t0 >= len) {
+    // an empty sequence still gets its decision (a miss) from work-group 0
+    if (decide && tile == 0 && slice == 0) {
+      double cs;
+      const int h = cache_decision<1>(p.cache, p.q, DT, len, b, p.theta, s_red, &s_hit, &cs);
+      if (tid == 0) { p.cache.hit[b] = h; p.cache.cos[b] = cs; }
+    }
+    return;
+  }
   const int tl = min(TILE, len - t0);
 
-  const int tid = threadIdx.x;
   const int j = tid % LPR;
   const int rg = tid / LPR;
   const int Hkv = p.Hkv;
@@ -162,7 +174,8 @@ __global__ __launch_bounds__(256) void score_pass1_kernel(ScoreParams p) {
   };
 
   uint4 bufA[U][CPL], bufB[U][CPL];
-  if (n_iter > 0) load_batch(0, bufA, !full);
+  if (full) load_batch(0, bufA, false);
+  else if (n_iter > 0) load_batch(0, bufA, true);
 
   // query slice of this lane's KV-head group, slot s holding head s ^ f(j)
   // (slots past GS hold zeros)
@@ -180,9 +193,22 @@ __global__ __launch_bounds__(256) void score_pass1_kernel(ScoreParams p) {
       qw[sl][4 * c + 0] = v.x; qw[sl][4 * c + 1] = v.y; qw[sl][4 * c + 2] = v.z; qw[sl][4 * c + 3] = v.w;
     }
   }
+
+  // Selection-Cache decision while the first keys and the query slice are in
+  // flight: every work-group of the sequence takes the same decision (same
+  // data, same order); work-group 0 records it for the kernels that follow
+  if (decide) {
+    double cs;
+    const int h = cache_decision<1>(p.cache, p.q, DT, len, b, p.theta, s_red, &s_hit, &cs);
+    if (tile == 0 && slice == 0 && tid == 0) { p.cache.hit[b] = h; p.cache.cos[b] = cs; }
+    if (h) return;
+  }
   const float scale2 = p.scale2;
-  // token-major logits: all Hq heads of one token are contiguous
-  float* lrow = p.logits + ((size_t)b * p.Lpad + t0) * p.Hq + kvh * p.G + slice * GS;
+  // logits are staged in LDS and written to HBM once per tile, so the loop
+  // issues no global stores: every wait on the vector-memory counter is then a
+  // wait for the one batch of K it needs, never for earlier stores
+  const int NH = Hkv * GS;
+  float* lrow = s_logit + kvh * GS;
   float mx[NFIN], sm[NFIN];
 #pragma unroll
   for (int i = 0; i < NFIN; ++i) {
@@ -221,7 +247,7 @@ __global__ __launch_bounds__(256) void score_pass1_kernel(ScoreParams p) {
         for (int i = 0; i < NFIN; ++i) {
           const int hh = i ^ fj;
           const float sc = acc[i] * scale2;
-          if (hh < GS) lrow[(size_t)t * p.Hq + hh] = sc;
+          if (hh < GS) lrow[t * NH + hh] = sc;
           // running max and sum of exp2 with a single exp per logit
           const float dlt = sc - mx[i];
           const float e = ex2(-fabsf(dlt));
@@ -233,11 +259,22 @@ __global__ __launch_bounds__(256) void score_pass1_kernel(ScoreParams p) {
   };
 
   if (full) {
-    for (int i0 = 0; i0 < n_iter; i0 += 2 * U) {
-      if (i0 + U < n_iter) load_batch(i0 + U, bufB, false);
-      compute_batch(i0, bufA, false);
-      if (i0 + 2 * U < n_iter) load_batch(i0 + 2 * U, bufA, false);
-      if (i0 + U < n_iter) compute_batch(i0 + U, bufB, false);
+    // same batch count for every lane; loads are unconditional in the steady
+    // state, so the compiler can count the loads in flight exactly
+    const int nb = TILE / (TPI * U);
+    int bi = 0;
+    for (; bi + 2 < nb; bi += 2) {
+      load_batch((bi + 1) * U, bufB, false);
+      compute_batch(bi * U, bufA, false);
+      load_batch((bi + 2) * U, bufA, false);
+      compute_batch((bi + 1) * U, bufB, false);
+    }
+    if (bi + 1 < nb) {
+      load_batch((bi + 1) * U, bufB, false);
+      compute_batch(bi * U, bufA, false);
+      compute_batch((bi + 1) * U, bufB, false);
+    } else {
+      compute_batch(bi * U, bufA, false);
     }
   } else {
     for (int i0 = 0; i0 < n_iter; i0 += 2 * U) {
@@ -257,7 +294,20 @@ __global__ __launch_bounds__(256) void score_pass1_kernel(ScoreParams p) {
     }
   }
   __syncthreads();
-  const int NH = Hkv * GS;
+  // the tile's logits: with one head slice a token's Hq logits are contiguous,
+  // so the whole tile is one contiguous range
+  {
+    float* g = p.logits + ((size_t)b * p.Lpad + t0) * p.Hq + slice * GS;
+    const int n = tl * NH;
+    if (NH == p.Hq) {
+      for (int e = tid; e < n; e += 256) g[e] = s_logit[e];
+    } else {
+      for (int e = tid; e < n; e += 256) {
+        const int t = e / NH, c = e - t * NH, kv = c / GS;
+        g[(size_t)t * p.Hq + kv * p.G + (c - kv * GS)] = s_logit[e];
+      }
+    }
+  }
   for (int hl = tid; hl < NH; hl += 256) {
     const int kv = hl / GS, hh = hl - kv * GS;
     float M = -INFINITY;
@@ -269,6 +319,13 @@ __global__ __launch_bounds__(256) void score_pass1_kernel(ScoreParams p) {
     }
     const int head = kv * p.G + slice * GS + hh;
     p.partials[((size_t)b * p.Hq + head) * p.ntiles + tile] = make_float2(M, L);
+  }
+  // control-block reset for the top-k of this step, spread over the
+  // sequence's work-groups (all of them reach this point on a miss)
+  if (p.ctrl && slice == 0) {
+    const int ntl = (len + TILE - 1) / TILE;
+    uint4* c = reinterpret_cast<uint4*>(p.ctrl + (size_t)b * kCtrlStride);
+    for (int i = tile * 256 + tid; i < p.ctrl_words / 4; i += ntl * 256) c[i] = make_uint4(0u, 0u, 0u, 0u);
   }
 }
 
@@ -351,7 +408,8 @@ __global__ __launch_bounds__(256) void votes_kernel(VoteParams p) {
   }
   if (!p.do_hist) return;
   __syncthreads();
-  uint32_t* gh = p.ctrl + (size_t)b * kCtrlStride + kCtlHist0;
+  uint32_t* gh = p.ctrl + (size_t)b * kCtrlStride + kCtlHist0 +
+                 (blockIdx.x % p.hist_copies) * (1 << kHist0Bits);
   for (int i = tid; i < (1 << kHist0Bits); i += 256)
     if (s_hist[i]) atomicAdd(gh + i, s_hist[i]);
 }
@@ -369,7 +427,7 @@ constexpr int score_lpr() {
 template <int DT, int D, bool PAGED, int TILE>
 static hipError_t launch_pass1_gs(const ScoreParams& p, hipStream_t s) {
   dim3 grid(p.ntiles, p.B * p.nslices);
-  const size_t shmem = 0;
+  const size_t shmem = (size_t)TILE * p.Hkv * p.GS * sizeof(float);
 #ifdef TS_SCORE_LPR
   constexpr int LPR = TS_SCORE_LPR;
 #else

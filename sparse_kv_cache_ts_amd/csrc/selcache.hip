@@ -1,100 +1,23 @@
-// selcache.hip — per-call prologue: control-block reset and the Selection
-// Cache decision.
-//
-// TokenSelect README, "Key Takeaways", third point: when successive queries
-// are alike, the earlier token selection is reused, which cuts how often
-// selection runs. A step hits when the stored state is valid, the sequence is
-// not empty, and the cosine of the flattened (Hq*d) query with the stored
-// query exceeds theta (strictly). The cosine is accumulated in fp64 in a
-// fixed order, so the decision is reproducible and matches an fp64 reference
-// except within rounding distance of theta.
-#include "ts_device.h"
+// selcache.hip — per-call prologue: control-block reset and, for callers
+// that do not fuse it into scoring, the Selection-Cache decision (selcache.h).
+#include "selcache.h"
 
 namespace ts {
 
 __global__ __launch_bounds__(256) void prologue_kernel(PrologueParams p) {
   __shared__ double s_red[3][4];
+  __shared__ int s_hit;
   const int r = blockIdx.x, tid = threadIdx.x;
   if (p.ctrl && r < p.rows) {
-    uint32_t* c = p.ctrl + (size_t)r * kCtrlStride;
-    for (int i = tid; i < kCtrlStride; i += 256) c[i] = 0u;
+    uint4* c = reinterpret_cast<uint4*>(p.ctrl + (size_t)r * kCtrlStride);
+    for (int i = tid; i < p.ctrl_words / 4; i += 256) c[i] = make_uint4(0u, 0u, 0u, 0u);
   }
   if (p.cache.prev_q == nullptr || r >= p.B) return;
-
-  const SelCacheDev& c = p.cache;
-  const int len = p.seq_lens[r];
-  const bool can = c.valid[r] != 0 && len > 0;
-  const int n = c.Hq * c.d;
-  double dot = 0.0, nq = 0.0, np = 0.0;
-  if (can) {
-    // 8 consecutive elements per thread and step; every load of a step is
-    // issued before the fp64 accumulation (n = Hq*d is a multiple of 64)
-    const float* pq = c.prev_q + (size_t)r * n;
-    const int nch = n / 8;
-    for (int c0 = tid; c0 < nch; c0 += 256 * 4) {
-      float qv[4][8], pv[4][8];
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int ch = c0 + u * 256;
-        if (ch < nch) {
-          if (p.dtype == 1) {
-            const uint4 w = ld16((const uint16_t*)p.q + (size_t)r * n + ch * 8);
-            const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              qv[u][2 * e] = bf16_lo(ws[e]);
-              qv[u][2 * e + 1] = bf16_hi(ws[e]);
-            }
-          } else {
-            const float4 a = ldf4((const float*)p.q + (size_t)r * n + ch * 8);
-            const float4 b = ldf4((const float*)p.q + (size_t)r * n + ch * 8 + 4);
-            qv[u][0] = a.x; qv[u][1] = a.y; qv[u][2] = a.z; qv[u][3] = a.w;
-            qv[u][4] = b.x; qv[u][5] = b.y; qv[u][6] = b.z; qv[u][7] = b.w;
-          }
-          const float4 a = ldf4(pq + ch * 8), b = ldf4(pq + ch * 8 + 4);
-          pv[u][0] = a.x; pv[u][1] = a.y; pv[u][2] = a.z; pv[u][3] = a.w;
-          pv[u][4] = b.x; pv[u][5] = b.y; pv[u][6] = b.z; pv[u][7] = b.w;
-        } else {
-#pragma unroll
-          for (int e = 0; e < 8; ++e) { qv[u][e] = 0.f; pv[u][e] = 0.f; }
-        }
-      }
-#pragma unroll
-      for (int u = 0; u < 4; ++u)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const double a = (double)qv[u][e], b = (double)pv[u][e];
-          dot += a * b;
-          nq += a * a;
-          np += b * b;
-        }
-    }
-  }
-  dot = wave_sum_d(dot);
-  nq = wave_sum_d(nq);
-  np = wave_sum_d(np);
-  const int lane = tid & 63, w = tid >> 6;
-  if (lane == 0) {
-    s_red[0][w] = dot;
-    s_red[1][w] = nq;
-    s_red[2][w] = np;
-  }
-  __syncthreads();
+  double cs;
+  const int hit = cache_decision(p.cache, p.q, p.dtype, p.seq_lens[r], r, p.theta, s_red, &s_hit, &cs);
   if (tid == 0) {
-    double D = 0.0, Q = 0.0, P = 0.0;
-    for (int i = 0; i < 4; ++i) {
-      D += s_red[0][i];
-      Q += s_red[1][i];
-      P += s_red[2][i];
-    }
-    double cs = __builtin_nan("");
-    int hit = 0;
-    if (can && Q > 0.0 && P > 0.0) {
-      cs = D / sqrt(Q * P);
-      hit = cs > p.theta ? 1 : 0;
-    }
-    c.hit[r] = hit;
-    c.cos[r] = cs;
+    p.cache.hit[r] = hit;
+    p.cache.cos[r] = cs;
   }
 }
 

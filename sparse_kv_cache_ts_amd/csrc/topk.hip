@@ -33,12 +33,7 @@ template <int NT>
 __device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, uint32_t* sh, uint32_t* total) {
   constexpr int NWAVE = NT / 64;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  uint32_t x = v;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const uint32_t y = __shfl_up(x, o);
-    if (lane >= o) x += y;
-  }
+  const uint32_t x = wave_incl_scan_u(v);
   if (lane == 63) sh[w] = x;
   __syncthreads();
   uint32_t base = 0, tot = 0;
@@ -76,7 +71,8 @@ __global__ __launch_bounds__(256) void topk_hist0_kernel(TopkParams p) {
   for (int i = 0; i < PER; ++i)
     if (start + i * 256 + tid < len) atomicAdd(&s_hist[float_key(v[i]) >> (32 - kHist0Bits)], 1u);
   __syncthreads();
-  uint32_t* gh = p.ctrl + (size_t)r * kCtrlStride + kCtlHist0;
+  uint32_t* gh = p.ctrl + (size_t)r * kCtrlStride + kCtlHist0 +
+                 (blockIdx.x % p.hist_copies) * (1 << kHist0Bits);
   for (int i = tid; i < (1 << kHist0Bits); i += 256)
     if (s_hist[i]) atomicAdd(gh + i, s_hist[i]);
 }
@@ -105,15 +101,31 @@ __global__ __launch_bounds__(256) void topk_partition_kernel(TopkParams p) {
     v[i] = (e < len) ? row[e] : 0.f;
   }
   // the bin b0 that holds the k-th largest key (16 of the 4096 bins per thread)
+  // (the sum of the histogram copies; all copy loads are issued first)
   uint32_t c[16];
 #pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const uint4 a = ld16(ctrl + kCtlHist0 + tid * 16 + 4 * q);
-    c[4 * q] = a.x; c[4 * q + 1] = a.y; c[4 * q + 2] = a.z; c[4 * q + 3] = a.w;
+  for (int i = 0; i < 16; ++i) c[i] = 0u;
+  for (int cp0 = 0; cp0 < p.hist_copies; cp0 += 4) {
+    uint4 a[4][4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        a[u][q] = (cp0 + u < p.hist_copies)
+                      ? ld16(ctrl + kCtlHist0 + (cp0 + u) * (1 << kHist0Bits) + tid * 16 + 4 * q)
+                      : make_uint4(0u, 0u, 0u, 0u);
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        c[4 * q] += a[u][q].x; c[4 * q + 1] += a[u][q].y;
+        c[4 * q + 2] += a[u][q].z; c[4 * q + 3] += a[u][q].w;
+      }
   }
   const uint2 rb = resolve_counts<16>(c, k_eff, s_sh);
   const uint32_t b0 = rb.x, need = rb.y;
-  const uint32_t cnt_b0 = ctrl[kCtlHist0 + b0];
+  uint32_t cnt_b0 = 0;
+  for (int cp = 0; cp < p.hist_copies; ++cp) cnt_b0 += ctrl[kCtlHist0 + cp * (1 << kHist0Bits) + b0];
   const bool whole = (need == cnt_b0);     // the whole bin is selected: no candidates
   if (blockIdx.x == 0 && tid == 0) {
     ctrl[kCtlPrefix] = b0;
@@ -256,37 +268,55 @@ __device__ __forceinline__ void select_any(const TopkParams& p, int r, int len, 
 }
 
 // Ascending indices of the set bits of words [0, W), at most k_eff of them.
+// Wave w owns a contiguous segment of words and walks it 64 words at a time,
+// one word per lane: a DPP prefix sum of the popcounts places each lane's
+// indices, so a wave loops only as often as its fullest word of the chunk
+// has bits. A first pass counts each segment; a scan of the eight segment
+// totals gives the waves their output bases.
 template <bool LDS_BM>
 __device__ __forceinline__ void emit_bitmap(const uint32_t* bm, int W, int k_eff, int32_t* out,
                                             uint32_t* s_sh) {
-  constexpr int NT = kFinalThreads;
-  constexpr int WPT = 16;                          // words per thread per round
-  const int tid = threadIdx.x;
-  uint32_t carry = 0;
-  for (int w0 = 0; w0 < W; w0 += NT * WPT) {
-    uint32_t words[WPT];
-    uint32_t cnt = 0;
+  constexpr int NW = kFinalThreads / 64;
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int seg = (((W + NW - 1) / NW) + 63) & ~63;
+  const int w0 = wv * seg, w1 = min(W, w0 + seg);
+  auto word = [&](int w) -> uint32_t {
+    if (w >= w1) return 0u;
+    if (LDS_BM) return bm[w];
+    return __hip_atomic_load(bm + w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  };
+  uint32_t cnt = 0;
+  for (int w = w0 + lane; w < w1; w += 64) cnt += __popc(word(w));
+  cnt = wave_sum_u(cnt);
+  if (lane == 0) s_sh[wv] = cnt;
+  __syncthreads();
+  uint32_t pos = 0;
+  for (int i = 0; i < wv; ++i) pos += s_sh[i];
+  __syncthreads();                         // s_sh is reused by the caller
+  // eight chunks at a time: their loads and prefix sums are independent
+  constexpr int CB = 8;
+  for (int c0 = w0; c0 < w1 && pos < (uint32_t)k_eff; c0 += 64 * CB) {
+    uint32_t m[CB], pc[CB], incl[CB];
 #pragma unroll
-    for (int i = 0; i < WPT; ++i) {
-      const int w = w0 + tid * WPT + i;
-      if (LDS_BM) words[i] = (w < W) ? bm[w] : 0u;
-      else words[i] = (w < W) ? __hip_atomic_load(bm + w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 0u;
-      cnt += __popc(words[i]);
+    for (int b = 0; b < CB; ++b) m[b] = word(c0 + b * 64 + lane);
+#pragma unroll
+    for (int b = 0; b < CB; ++b) {
+      pc[b] = __popc(m[b]);
+      incl[b] = wave_incl_scan_u(pc[b]);
     }
-    uint32_t total;
-    uint32_t pos = carry + block_excl_scan<NT>(cnt, s_sh, &total);
 #pragma unroll
-    for (int i = 0; i < WPT; ++i) {
-      uint32_t m = words[i];
-      const int base = (w0 + tid * WPT + i) * 32;
-      while (m) {
-        const int bit = __ffs(m) - 1;
-        if (pos < (uint32_t)k_eff) out[pos] = base + bit;
-        ++pos;
-        m &= m - 1;
+    for (int b = 0; b < CB; ++b) {
+      const int w = c0 + b * 64 + lane;
+      uint32_t my = pos + incl[b] - pc[b];
+      uint32_t mb = m[b];
+      while (mb) {
+        const int bit = __ffs(mb) - 1;
+        if (my < (uint32_t)k_eff) out[my] = w * 32 + bit;
+        ++my;
+        mb &= mb - 1;
       }
+      pos += wave_last_u(incl[b]);
     }
-    carry += total;
   }
 }
 

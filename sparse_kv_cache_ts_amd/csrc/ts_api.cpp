@@ -214,6 +214,8 @@ void plan_score(const Geo& g, int B, Carve& c, ScorePlan& s) {
   // 256-token tiles unless that leaves fewer than two work-groups per CU
   const long wg256 = (long)B * g.nslices * cdiv(g.max_len, 256);
   s.tile = wg256 >= 512 ? 256 : 128;
+  // the tile's logits are staged in LDS: keep that within 48 KB
+  if ((long)s.tile * g.Hkv * g.GS * 4 > 48 * 1024) s.tile = 128;
 #ifdef TS_FORCE_SCORE_TILE
   s.tile = TS_FORCE_SCORE_TILE;   // build-time override for tuning sweeps
 #endif
@@ -253,6 +255,10 @@ void plan_topk(int rows, int row_stride, Carve& c, TopkPlan& t, bool own_ctrl) {
   t.cand = c.take((size_t)rows * kCandCap * 8);
 }
 
+// histogram copies for `wgs` work-groups adding into one row's first histogram
+int hist_copies_for(int wgs) { return std::max(1, std::min(kHistCopiesMax, wgs / 64)); }
+int ctrl_words_for(int copies) { return kCtlHist0 + copies * (1 << kHist0Bits); }
+
 TopkParams topk_params(const TopkPlan& t, void* ws, int rows, int row_stride, int k,
                        const float* votes, const int32_t* row_lens, int row_len_base,
                        const int32_t* hit, int32_t* idx) {
@@ -269,6 +275,7 @@ TopkParams topk_params(const TopkPlan& t, void* ws, int rows, int row_stride, in
   tp.row_stride = row_stride;
   tp.k = k;
   tp.bm_stride = t.bm_stride;
+  tp.hist_copies = 1;
   return tp;
 }
 
@@ -343,6 +350,7 @@ VoteParams vote_params(const Geo& g, const ScorePlan& s, int B, void* ws, const 
   v.Lpad = s.Lpad;
   v.vote_stride = vote_stride;
   v.do_hist = do_hist;
+  v.hist_copies = 1;
   return v;
 }
 
@@ -478,11 +486,14 @@ static ts_status run_topk(int rows, int row_stride, const float* votes, const in
                           int row_len_base, int k, int32_t* idx, void* ws, const TopkPlan& t,
                           int max_row_len, hipStream_t st) {
   PrologueParams pp{};
+  const int gx = cdiv(max_row_len, kTopkChunk);
+  const int copies = hist_copies_for(gx);
   pp.ctrl = at<uint32_t>(ws, t.ctrl);
   pp.rows = rows;
+  pp.ctrl_words = ctrl_words_for(copies);
   TS_LAUNCH_K(kKPrologue, launch_prologue(pp, rows, st), "prologue");
   TopkParams tp = topk_params(t, ws, rows, row_stride, k, votes, row_lens, row_len_base, nullptr, idx);
-  const int gx = cdiv(max_row_len, kTopkChunk);
+  tp.hist_copies = copies;
   TS_LAUNCH_K(kKTopkHist, launch_topk_hist0(tp, gx, st), "top-k histogram");
   TS_LAUNCH_K(kKTopkPartition, launch_topk_partition(tp, gx, st), "top-k partition");
   TS_LAUNCH_K(kKTopkFinalize, launch_topk_finalize(tp, st), "top-k finalize");
@@ -655,31 +666,29 @@ ts_status ts_decode_step(ts_sel_cache* cache, const ts_kv_layout* L, int32_t bat
   hipStream_t st = static_cast<hipStream_t>(stream);
   const int32_t* pt = g.paged ? page_table : nullptr;
 
-  // 1. reset control blocks; Selection-Cache decision per sequence
-  PrologueParams pp{};
-  pp.ctrl = at<uint32_t>(ws, p.s.ctrl);
-  pp.rows = batch;
-  pp.cache = cache->dev;
-  pp.q = q;
-  pp.dtype = g.dtype;
-  pp.seq_lens = seq_lens;
-  pp.B = batch;
-  pp.theta = theta;
-  TS_LAUNCH_K(kKPrologue, launch_prologue(pp, batch, st), "prologue");
+  // 1+2. Selection-Cache decision per sequence, then the K-scan on misses
+  // (one kernel: every scoring work-group evaluates its sequence's decision),
+  // and the reset of the top-k control blocks
+  const int vote_wgs = cdiv(g.max_len, kVoteTile);
+  const int copies = hist_copies_for(vote_wgs);
   const int32_t* hit = cache->dev.hit;
-
-  // 2. K-scan (misses only)
-  ScoreParams sp = score_params(g, p.s, batch, ws, q, k_cache, pt, seq_lens, hit);
+  ScoreParams sp = score_params(g, p.s, batch, ws, q, k_cache, pt, seq_lens, nullptr);
+  sp.cache = cache->dev;
+  sp.theta = theta;
+  sp.ctrl = at<uint32_t>(ws, p.s.ctrl);
+  sp.ctrl_words = ctrl_words_for(copies);
   TS_LAUNCH_K(kKScore, launch_score_pass1(g.dtype, g.d, g.paged, sp, st), "score pass 1");
   LseParams lp = lse_params(g, p.s, batch, ws, seq_lens, hit);
   TS_LAUNCH_K(kKLse, launch_lse(lp, st), "log-sum-exp");
   // 3. votes + first radix histogram
   float* votes = at<float>(ws, p.votes);
   VoteParams vp = vote_params(g, p.s, batch, ws, seq_lens, hit, votes, g.max_len, 1);
-  TS_LAUNCH_K(kKVotes, launch_votes(vp, cdiv(g.max_len, kVoteTile), st), "votes");
+  vp.hist_copies = copies;
+  TS_LAUNCH_K(kKVotes, launch_votes(vp, vote_wgs, st), "votes");
   // 4. top-k into the cache's stored selection
   TopkParams tp = topk_params(p.t, ws, batch, g.max_len, k, votes, seq_lens, 0, hit,
                               cache->dev.sel);
+  tp.hist_copies = copies;
   const int gx = cdiv(g.max_len, kTopkChunk);
   TS_LAUNCH_K(kKTopkPartition, launch_topk_partition(tp, gx, st), "top-k partition");
   TS_LAUNCH_K(kKTopkFinalize, launch_topk_finalize(tp, st), "top-k finalize");

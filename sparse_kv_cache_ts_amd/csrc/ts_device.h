@@ -45,25 +45,79 @@ __device__ __forceinline__ float group_sum(float v) {
   return v;
 }
 
+// Whole-wave reductions on DPP: the row operations of group_sum give every
+// lane of a 16-lane row its row's value, row_bcast:15 (rows 1, 3) and
+// row_bcast:31 (rows 2, 3) fold the rows into lane 63, and readlane returns
+// that to every lane. Fixed order: bitwise reproducible.
+template <int CTRL, int RM>
+__device__ __forceinline__ int dpp_i(int old, int v) {
+  return __builtin_amdgcn_update_dpp(old, v, CTRL, RM, 0xF, false);
+}
+template <int CTRL, int RM>
+__device__ __forceinline__ double dpp_d(double old, double v) {
+  const int2 o = __builtin_bit_cast(int2, old), x = __builtin_bit_cast(int2, v);
+  int2 r;
+  r.x = dpp_i<CTRL, RM>(o.x, x.x);
+  r.y = dpp_i<CTRL, RM>(o.y, x.y);
+  return __builtin_bit_cast(double, r);
+}
+
 __device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
-  return v;
+  v = fmaxf(v, dpp_f<0xB1>(v));
+  v = fmaxf(v, dpp_f<0x4E>(v));
+  v = fmaxf(v, dpp_f<0x141>(v));
+  v = fmaxf(v, dpp_f<0x140>(v));
+  const int ninf = __builtin_bit_cast(int, -INFINITY);
+  v = fmaxf(v, __builtin_bit_cast(float, dpp_i<0x142, 0xA>(ninf, __builtin_bit_cast(int, v))));
+  v = fmaxf(v, __builtin_bit_cast(float, dpp_i<0x143, 0xC>(ninf, __builtin_bit_cast(int, v))));
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 63));
 }
 __device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o);
-  return v;
+  v = group_sum<16>(v);
+  v += __builtin_bit_cast(float, dpp_i<0x142, 0xA>(0, __builtin_bit_cast(int, v)));
+  v += __builtin_bit_cast(float, dpp_i<0x143, 0xC>(0, __builtin_bit_cast(int, v)));
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 63));
 }
 __device__ __forceinline__ double wave_sum_d(double v) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o);
-  return v;
+  v += dpp_d<0xB1, 0xF>(0.0, v);
+  v += dpp_d<0x4E, 0xF>(0.0, v);
+  v += dpp_d<0x141, 0xF>(0.0, v);
+  v += dpp_d<0x140, 0xF>(0.0, v);
+  v += dpp_d<0x142, 0xA>(0.0, v);
+  v += dpp_d<0x143, 0xC>(0.0, v);
+  const int2 x = __builtin_bit_cast(int2, v);
+  int2 r;
+  r.x = __builtin_amdgcn_readlane(x.x, 63);
+  r.y = __builtin_amdgcn_readlane(x.y, 63);
+  return __builtin_bit_cast(double, r);
 }
 __device__ __forceinline__ uint32_t wave_sum_u(uint32_t v) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o);
-  return v;
+  v += (uint32_t)dpp_i<0xB1, 0xF>(0, (int)v);
+  v += (uint32_t)dpp_i<0x4E, 0xF>(0, (int)v);
+  v += (uint32_t)dpp_i<0x141, 0xF>(0, (int)v);
+  v += (uint32_t)dpp_i<0x140, 0xF>(0, (int)v);
+  v += (uint32_t)dpp_i<0x142, 0xA>(0, (int)v);
+  v += (uint32_t)dpp_i<0x143, 0xC>(0, (int)v);
+  return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
+}
+
+// Inclusive prefix sum over the 64 lanes of a wave, on DPP (no LDS round
+// trips): shifts by 1, 2, 4, 8 inside each 16-lane row (lanes without a source
+// add 0), then row_bcast:15 carries row r's last lane into row r+1 (rows 1, 3)
+// and row_bcast:31 carries lane 31 into rows 2 and 3.
+__device__ __forceinline__ uint32_t wave_incl_scan_u(uint32_t x) {
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x111, 0xf, 0xf, true);
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x112, 0xf, 0xf, true);
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x114, 0xf, 0xf, true);
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x118, 0xf, 0xf, true);
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x142, 0xa, 0xf, false);
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x143, 0xc, 0xf, false);
+  return x;
+}
+
+// Value of lane 63 (a wave-uniform scalar).
+__device__ __forceinline__ uint32_t wave_last_u(uint32_t x) {
+  return (uint32_t)__builtin_amdgcn_readlane((int)x, 63);
 }
 
 // Order-preserving map of a float onto uint32 (larger float -> larger key);
@@ -89,12 +143,7 @@ __device__ __forceinline__ uint4 ld16_nt(const void* p) {
 // block total is written to *total.
 __device__ __forceinline__ uint32_t block_excl_scan_256(uint32_t v, uint32_t* sh, uint32_t* total) {
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  uint32_t x = v;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    uint32_t y = __shfl_up(x, o);
-    if (lane >= o) x += y;
-  }
+  const uint32_t x = wave_incl_scan_u(v);
   if (lane == 63) sh[w] = x;
   __syncthreads();
   uint32_t base = 0, tot = 0;
@@ -121,13 +170,10 @@ __device__ __forceinline__ uint2 resolve_counts(const uint32_t (&c)[PER], uint32
   uint32_t s = 0;
 #pragma unroll
   for (int i = 0; i < PER; ++i) s += c[i];
-  // inclusive suffix sum over the lanes of this wave (lanes >= lane)
-  uint32_t x = s;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const uint32_t y = __shfl_down(x, o);
-    if (lane + o < 64) x += y;
-  }
+  // inclusive suffix sum over the lanes of this wave (lanes >= lane), from
+  // the inclusive prefix sum and the wave total
+  const uint32_t pre = wave_incl_scan_u(s);
+  const uint32_t x = wave_last_u(pre) - pre + s;
   if (lane == 0) sh[2 + w] = x;
   if (t == 0) { sh[0] = 0u; sh[1] = 0u; }
   __syncthreads();

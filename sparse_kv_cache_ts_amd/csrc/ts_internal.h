@@ -24,9 +24,14 @@ enum CtrlWord : int {
   kCtlPrefix = 1,     // top-12-bit bin that holds the k-th largest key
   kCtlNeed = 2,       // elements still to take inside that bin (0: the whole bin)
   kCtlErr = 7,        // non-zero if a bounded wait gave up
-  kCtlHist0 = 16,     // 4096 bins: key bits 31..20
-  kCtlWords = 16 + 4096,
+  kCtlHist0 = 16,     // kHistCopiesMax copies of 4096 bins (key bits 31..20), 16 KB apart
+  kCtlWords = 16 + 4 * 4096,
 };
+// The first histogram is spread over up to 4 copies: work-group x of a row adds
+// into copy x % hist_copies, so the few hot bins (votes of similar size share
+// their top 12 bits) see 1/hist_copies of the device-scope atomics; readers
+// sum the copies.
+constexpr int kHistCopiesMax = 4;
 constexpr int kCtrlStride = ((kCtlWords + 63) / 64) * 64;   // 256-byte rows
 constexpr int kHist0Bits = 12;
 constexpr int kCandCap = 8192;    // candidates kept per row; more falls back to a row rescan
@@ -53,6 +58,7 @@ struct SelCacheDev {
 struct PrologueParams {
   uint32_t* ctrl;       // [rows][kCtrlStride] or null
   int rows;
+  int ctrl_words;       // words zeroed at the start of each row (multiple of 4)
   // selection-cache check (cache.prev_q == null: none)
   SelCacheDev cache;
   const void* q;        // [B][Hq][d]
@@ -73,6 +79,12 @@ struct ScoreParams {
   int B, Hq, Hkv, G, GS, nslices, max_len, Lpad, ntiles, ps_log2, pt_stride;
   int tile;                 // tokens per work-group: 128 or 256
   float scale2;
+  // decode steps: the Selection-Cache decision and the control-block reset,
+  // fused into this kernel (cache.prev_q == null: neither; `hit` is used)
+  SelCacheDev cache;
+  double theta;
+  uint32_t* ctrl;           // [B][kCtrlStride]: the first ctrl_words words zeroed
+  int ctrl_words;
 };
 
 struct LseParams {
@@ -92,6 +104,7 @@ struct VoteParams {
   uint32_t* ctrl;
   int B, Hq, Lpad, vote_stride;
   int do_hist;              // 1: add the votes to the first top-k histogram
+  int hist_copies;          // 1 .. kHistCopiesMax
 };
 
 struct TopkParams {
@@ -104,6 +117,7 @@ struct TopkParams {
   uint32_t* bitmap;         // [rows][bm_stride] selection bits
   uint2* cand;              // [rows][kCandCap] (key, index) of threshold-bin candidates
   int rows, row_stride, k, bm_stride;
+  int hist_copies;          // copies of the first histogram (1 .. kHistCopiesMax)
 };
 
 struct AttendParams {
