@@ -154,12 +154,12 @@ __global__ __launch_bounds__(256) void attend_kernel(AttendParams p) {
   }
 
   // merge the row groups (fixed order: deterministic): the common max and the
-  // sums over a wave's row groups by lane shuffles, over the 4 waves in LDS
+  // sums over a wave's row groups by lane swaps, over the 4 waves in LDS
 #pragma unroll
   for (int hh = 0; hh < GS; ++hh) {
     float mw = m[hh];
-#pragma unroll
-    for (int o = LPR; o < 64; o <<= 1) mw = fmaxf(mw, __shfl_xor(mw, o));
+    if constexpr (LPR <= 8) mw = xor_max<8>(mw);
+    mw = xor_max<32>(xor_max<16>(mw));
     if (lane == 0) s_m[wv][hh] = mw;
   }
   __syncthreads();
@@ -168,14 +168,13 @@ __global__ __launch_bounds__(256) void attend_kernel(AttendParams p) {
     const float M = fmaxf(fmaxf(s_m[0][hh], s_m[1][hh]), fmaxf(s_m[2][hh], s_m[3][hh]));
     const float f = (l[hh] > 0.f) ? ex2(m[hh] - M) : 0.f;
     float lw = l[hh] * f;
-#pragma unroll
-    for (int o = LPR; o < 64; o <<= 1) lw += __shfl_xor(lw, o);
+    if constexpr (LPR <= 8) lw = xor_sum<8>(lw);
+    lw = xor_sum<32>(xor_sum<16>(lw));
 #pragma unroll
     for (int e = 0; e < EPL; ++e) {
       float v = acc[hh][e] * f;
-#pragma unroll
-      for (int o = LPR; o < 64; o <<= 1) v += __shfl_xor(v, o);
-      acc[hh][e] = v;
+      if constexpr (LPR <= 8) v = xor_sum<8>(v);
+      acc[hh][e] = xor_sum<32>(xor_sum<16>(v));
     }
     if (lane < LPR) {
 #pragma unroll
@@ -201,53 +200,65 @@ __global__ __launch_bounds__(256) void attend_kernel(AttendParams p) {
   }
 }
 
+// One work-group of 128 threads per (head, sequence); thread d owns output
+// element d. Everything that depends on nothing (the first SB splits' acc
+// values, this thread's (max, sum) pair, the query row for the cache update)
+// is loaded up front, so the kernel waits on memory about once.
 __global__ __launch_bounds__(128) void combine_kernel(CombineParams p) {
+  constexpr int SB = 64;                 // splits whose acc values are held in registers
   __shared__ float s_w[kMaxSplits];
   __shared__ float s_red[4];
   const int h = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
   const int lane = tid & 63, wv = tid >> 6;
-  const size_t base = ((size_t)b * p.Hq + h) * p.nsplit;
-  float m = -INFINITY;
-  for (int s = tid; s < p.nsplit; s += 128)
+  const int ns = p.nsplit;
+  const size_t base = ((size_t)b * p.Hq + h) * ns;
+  const bool own_d = tid < p.d;
+  const float* pa = p.pacc + base * p.d + tid;
+  float a[SB];
+#pragma unroll
+  for (int s = 0; s < SB; ++s) a[s] = (own_d && s < ns) ? pa[(size_t)s * p.d] : 0.f;
+  float pmv = -INFINITY, plv = 0.f;
+  if (tid < ns) {
+    pmv = p.pm[base + tid];
+    plv = p.pl[base + tid];
+  }
+  // splits past 128 (long selections): folded in a loop
+  float m = plv > 0.f ? pmv : -INFINITY;
+  for (int s = tid + 128; s < ns; s += 128)
     if (p.pl[base + s] > 0.f) m = fmaxf(m, p.pm[base + s]);
   m = wave_max(m);
   if (lane == 0) s_red[wv] = m;
   __syncthreads();
   const float M = fmaxf(s_red[0], s_red[1]);
   float lsum = 0.f;
-  for (int s = tid; s < p.nsplit; s += 128) {
+  if (tid < ns) {
+    const float w = plv > 0.f ? ex2(pmv - M) : 0.f;
+    s_w[tid] = w;
+    lsum = plv * w;
+  }
+  for (int s = tid + 128; s < ns; s += 128) {
     const float pl = p.pl[base + s];
     const float w = pl > 0.f ? ex2(p.pm[base + s] - M) : 0.f;
     s_w[s] = w;
     lsum += pl * w;
   }
   lsum = wave_sum(lsum);
-  __syncthreads();
   if (lane == 0) s_red[2 + wv] = lsum;
   __syncthreads();
   const float L = s_red[2] + s_red[3];
-  for (int d = tid; d < p.d; d += 128) {
-    // every split's acc was written (zeros for an empty split, whose weight is 0)
-    const float* pa = p.pacc + base * p.d + d;
-    float o0 = 0.f, o1 = 0.f, o2 = 0.f, o3 = 0.f;
-    int s = 0;
-    for (; s + 8 <= p.nsplit; s += 8) {
-      float a[8];
+  // every split's acc was written (zeros for an empty split, whose weight is 0)
+  float o0 = 0.f, o1 = 0.f, o2 = 0.f, o3 = 0.f;
 #pragma unroll
-      for (int u = 0; u < 8; ++u) a[u] = pa[(size_t)(s + u) * p.d];
-      o0 = fmaf(a[0], s_w[s], o0);
-      o1 = fmaf(a[1], s_w[s + 1], o1);
-      o2 = fmaf(a[2], s_w[s + 2], o2);
-      o3 = fmaf(a[3], s_w[s + 3], o3);
-      o0 = fmaf(a[4], s_w[s + 4], o0);
-      o1 = fmaf(a[5], s_w[s + 5], o1);
-      o2 = fmaf(a[6], s_w[s + 6], o2);
-      o3 = fmaf(a[7], s_w[s + 7], o3);
+  for (int s = 0; s < SB; s += 4) {
+    if (s < ns) {
+      o0 = fmaf(a[s], s_w[s], o0);
+      o1 = fmaf(a[s + 1], s < ns - 1 ? s_w[s + 1] : 0.f, o1);
+      o2 = fmaf(a[s + 2], s < ns - 2 ? s_w[s + 2] : 0.f, o2);
+      o3 = fmaf(a[s + 3], s < ns - 3 ? s_w[s + 3] : 0.f, o3);
     }
-    for (; s < p.nsplit; ++s) o0 = fmaf(pa[(size_t)s * p.d], s_w[s], o0);
-    const float o = (o0 + o1) + (o2 + o3);
-    p.out[((size_t)b * p.Hq + h) * p.d + d] = (L > 0.f) ? o / L : 0.f;
   }
+  for (int s = SB; s < ns; ++s) o0 = fmaf(own_d ? pa[(size_t)s * p.d] : 0.f, s_w[s], o0);
+  if (own_d) p.out[((size_t)b * p.Hq + h) * p.d + tid] = (L > 0.f) ? ((o0 + o1) + (o2 + o3)) / L : 0.f;
 
   // Selection-Cache state update, spread over the head blocks of a sequence
   if (p.cache.prev_q == nullptr) return;

@@ -101,6 +101,32 @@ __device__ __forceinline__ uint32_t wave_sum_u(uint32_t v) {
   return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
 }
 
+// Combine every lane with lane ^ O (O a power of two <= 32). O = 16 and
+// O = 32 use the gfx950 lane-swap instructions (VALU, no LDS round trip):
+// swapping a register with itself leaves lane l the pair {v[l], v[l ^ O]}
+// (in either order), which is all a commutative op needs.
+template <int O>
+__device__ __forceinline__ float2 xor_pair(float v) {
+  if constexpr (O == 16 || O == 32) {
+    const unsigned x = __builtin_bit_cast(unsigned, v);
+    unsigned lo, hi;
+    if constexpr (O == 16) {
+      const auto r = __builtin_amdgcn_permlane16_swap(x, x, false, false);
+      lo = r[0]; hi = r[1];
+    } else {
+      const auto r = __builtin_amdgcn_permlane32_swap(x, x, false, false);
+      lo = r[0]; hi = r[1];
+    }
+    return make_float2(__builtin_bit_cast(float, lo), __builtin_bit_cast(float, hi));
+  } else {
+    return make_float2(v, __shfl_xor(v, O));
+  }
+}
+template <int O>
+__device__ __forceinline__ float xor_sum(float v) { const float2 r = xor_pair<O>(v); return r.x + r.y; }
+template <int O>
+__device__ __forceinline__ float xor_max(float v) { const float2 r = xor_pair<O>(v); return fmaxf(r.x, r.y); }
+
 // Inclusive prefix sum over the 64 lanes of a wave, on DPP (no LDS round
 // trips): shifts by 1, 2, 4, 8 inside each 16-lane row (lanes without a source
 // add 0), then row_bcast:15 carries row r's last lane into row r+1 (rows 1, 3)
