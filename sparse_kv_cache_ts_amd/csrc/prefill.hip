@@ -58,39 +58,44 @@ __device__ __forceinline__ uint4 load_q_frag(const PrefillParams& p, int g, int 
   return ld16(base);
 }
 
-// K fragment (16 keys from kb) of k-step ks for KV head g. Ordinary (cached)
-// loads: every query block of the chunk reads the same keys.
+// K fragments (16 keys from kb, all k-steps) for KV head g. Ordinary (cached)
+// loads: every query block of the chunk reads the same keys. Keys past the
+// context are clamped to its last key (in bounds; their scores are masked), so
+// the loads are unconditional and the compiler can count the ones in flight.
 template <int D>
-__device__ __forceinline__ uint4 load_k_frag(const PrefillParams& p, int g, int kb, int ks, int lane) {
-  const int key = kb + (lane & 15);
-  if (key >= p.n_ctx) return make_uint4(0, 0, 0, 0);
-  const char* base = (const char*)p.k + (((size_t)key * p.Hkv + g) * D + ks * 32 + 8 * (lane >> 4)) * 2;
-  return ld16(base);
+__device__ __forceinline__ void load_k_tile(const PrefillParams& p, int g, int kb, int lane,
+                                            uint4 (&kf)[D / 32]) {
+  const int key = min(kb + (lane & 15), p.n_ctx - 1);
+  const char* base = (const char*)p.k + (((size_t)key * p.Hkv + g) * D + 8 * (lane >> 4)) * 2;
+#pragma unroll
+  for (int ks = 0; ks < D / 32; ++ks) kf[ks] = ld16(base + ks * 64);
 }
 
 template <int RT, int KS>
 __device__ __forceinline__ void qk_tile(const bf16x8_t (&qf)[RT][KS], const uint4 (&kf)[KS], f32x4_t (&s)[RT]) {
+  // k-steps outer, row tiles inner: consecutive MFMAs are independent, so
+  // none waits for the previous one's accumulator
 #pragma unroll
-  for (int rt = 0; rt < RT; ++rt) {
-    s[rt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  for (int rt = 0; rt < RT; ++rt) s[rt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) s[rt] = mfma16(qf[rt][ks], as_bf8(kf[ks]), s[rt]);
-  }
+  for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) s[rt] = mfma16(qf[rt][ks], as_bf8(kf[ks]), s[rt]);
 }
 
 // ---- pass 1 -----------------------------------------------------------------
-// Keys go in groups of two 16-key tiles. Per (row, group) the running maximum
-// M (base-2 units, scale2 * s) is raised once and the sum rescaled once, then
-// each element adds exp2(scale2 * s - M): about four VALU operations and 1.5
-// exponentials per element. Masked elements are -inf and add 0. M starts at
-// a finite -1e30, so a row with nothing seen yet rescales by exp2(0) = 1 and
-// no inf - inf or 0 * inf arises.
+// Keys go in groups of two 16-key tiles. Each row keeps a reference M (base-2
+// units, scale2 * s) and the sum S of exp2(scale2 * s - M); the reference only
+// moves when a score exceeds it by a margin (see update below), so most
+// elements cost one fma, one exponential and one add. Masked elements are
+// -inf and add 0. M starts at a finite -1e30, so a row with nothing seen yet
+// rescales by exp2(0) = 1 and no inf - inf or 0 * inf arises.
 template <int G, int D>
 __global__ __launch_bounds__(256) void prefill_lse_kernel(PrefillParams p) {
   constexpr int KS = D / 32;      // k-steps per tile
-  constexpr int RT = 4;           // row tiles per wave (64 rows)
-  constexpr int QB = 256 / G;     // queries per work-group (4 waves x 64 rows)
-  constexpr int QW = 64 / G;      // queries per wave
+  constexpr int RT = kPrefillRT1;  // row tiles per wave
+  constexpr int QW = 16 * RT / G;  // queries per wave
+  constexpr int QB = 4 * QW;       // queries per work-group (4 waves)
   const int nqb = (p.chunk + QB - 1) / QB;
   const int f = xcd_flat(blockIdx.x, gridDim.x);
   const int qblk = f % nqb;
@@ -118,57 +123,96 @@ __global__ __launch_bounds__(256) void prefill_lse_kernel(PrefillParams p) {
     for (int i = 0; i < 4; ++i) { M[rt][i] = -1e30f; S[rt][i] = 0.f; }
   const float sc2 = p.scale2;
 
-  uint4 ka[KS], kb2[KS], na[KS], nb[KS];
-  if (k0 < kend) {
+  // one group of two 16-key tiles: scores, then the running max/sum update.
+  // Scores are scaled first (a product is a canonical float, so the maxima
+  // need no NaN-quieting extra instructions).
+  // Lazy rescaling: M is a per-row reference, not necessarily the running
+  // max. A group adds exp2(scale2 * s - M) directly unless some score of the
+  // wave lies more than kLazy above its row's M (terms stay below 2^kLazy, so
+  // the sums cannot overflow); only then does the group take the exact
+  // online update, which raises M to the max and rescales S. The first group
+  // always does (M starts at a finite -1e30), and later ones rarely do.
+  constexpr float kLazy = 20.f;
+  auto update = [&](const f32x4_t (&s0)[RT], const f32x4_t (&s1)[RT], int kb, bool masked) {
+    const int key = kb + (lane & 15);
+    float d0[RT][4], d1[RT][4];
+    float lm = -INFINITY;
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      ka[ks] = load_k_frag<D>(p, g, k0, ks, lane);
-      kb2[ks] = load_k_frag<D>(p, g, k0 + 16, ks, lane);
-    }
-  }
-  for (int kb = k0; kb < kend; kb += 32) {
-    if (kb + 32 < kend) {
+    for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        na[ks] = load_k_frag<D>(p, g, kb + 32, ks, lane);
-        nb[ks] = load_k_frag<D>(p, g, kb + 48, ks, lane);
+      for (int i = 0; i < 4; ++i) {
+        float a = fmaf(s0[rt][i], sc2, -M[rt][i]), b = fmaf(s1[rt][i], sc2, -M[rt][i]);
+        if (masked) {
+          // causal edge or end of the range: query qi sees keys <= q_pos0 + qi
+          const int lim = min(kend - 1, p.q_pos0 + qbase + (rt * 16 + 4 * (lane >> 4) + i) / G);
+          a = key <= lim ? a : -INFINITY;
+          b = key + 16 <= lim ? b : -INFINITY;
+        }
+        d0[rt][i] = a;
+        d1[rt][i] = b;
+        lm = fmaxf(lm, fmaxf(a, b));
       }
+    if (__builtin_expect(__any(lm > kLazy), 0)) {
+      // exact update of this group: M <- max(M, group max), S rescaled
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float a2 = d0[rt][i] == -INFINITY ? -INFINITY : s0[rt][i] * sc2;
+          const float b2 = d1[rt][i] == -INFINITY ? -INFINITY : s1[rt][i] * sc2;
+          const float m2 = fmaxf(M[rt][i], fmaxf(a2, b2));
+          S[rt][i] *= ex2(M[rt][i] - m2);
+          M[rt][i] = m2;
+          d0[rt][i] = a2 - m2;
+          d1[rt][i] = b2 - m2;
+        }
     }
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) S[rt][i] += ex2(d0[rt][i]) + ex2(d1[rt][i]);
+  };
+  auto group = [&](int kb, const uint4 (&ka)[KS], const uint4 (&kb2)[KS]) {
     f32x4_t s0[RT], s1[RT];
     qk_tile<RT, KS>(qf, ka, s0);
     qk_tile<RT, KS>(qf, kb2, s1);
-    if (kb + 32 <= min(kall, kend)) {
-#pragma unroll
-      for (int rt = 0; rt < RT; ++rt)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const float a = s0[rt][i], b = s1[rt][i];
-          const float mn = fmaxf(M[rt][i], fmaxf(a, b) * sc2);
-          const float r = ex2(M[rt][i] - mn);
-          S[rt][i] = fmaf(S[rt][i], r, ex2(fmaf(a, sc2, -mn))) + ex2(fmaf(b, sc2, -mn));
-          M[rt][i] = mn;
-        }
-    } else {
-      // causal edge or end of the range: query qi sees keys <= q_pos0 + qi
-      const int key = kb + (lane & 15);
-#pragma unroll
-      for (int rt = 0; rt < RT; ++rt)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int lim = min(kend - 1, p.q_pos0 + qbase + (rt * 16 + 4 * (lane >> 4) + i) / G);
-          const float a = key <= lim ? s0[rt][i] : -INFINITY;
-          const float b = key + 16 <= lim ? s1[rt][i] : -INFINITY;
-          const float mn = fmaxf(M[rt][i], fmaxf(a, b) * sc2);
-          const float r = ex2(M[rt][i] - mn);
-          S[rt][i] = fmaf(S[rt][i], r, ex2(fmaf(a, sc2, -mn))) + ex2(fmaf(b, sc2, -mn));
-          M[rt][i] = mn;
-        }
-    }
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      ka[ks] = na[ks];
-      kb2[ks] = nb[ks];
-    }
+    // a separate copy of the update for the groups every row sees in full
+    if (kb + 32 <= min(kall, kend)) update(s0, s1, kb, false);
+    else update(s0, s1, kb, true);
+  };
+
+  // software pipeline over groups with two fragment sets (A, B) and
+  // unconditional prefetch one group ahead
+  const int ng = (kend > k0) ? (kend - k0 + 31) / 32 : 0;
+  uint4 a0[KS], a1[KS], b0[KS], b1[KS];
+  if (ng > 0) {
+    load_k_tile<D>(p, g, k0, lane, a0);
+    load_k_tile<D>(p, g, k0 + 16, lane, a1);
+  }
+  // (scheduling barriers keep the compiler from hoisting a group's MFMAs
+  // above the previous group's work, which would consume the prefetch at once)
+  int gi = 0;
+  for (; gi + 2 < ng; gi += 2) {
+    const int kb = k0 + gi * 32;
+    load_k_tile<D>(p, g, kb + 32, lane, b0);
+    load_k_tile<D>(p, g, kb + 48, lane, b1);
+    __builtin_amdgcn_sched_barrier(0);
+    group(kb, a0, a1);
+    __builtin_amdgcn_sched_barrier(0);
+    load_k_tile<D>(p, g, kb + 64, lane, a0);
+    load_k_tile<D>(p, g, kb + 80, lane, a1);
+    __builtin_amdgcn_sched_barrier(0);
+    group(kb + 32, b0, b1);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  if (gi + 1 < ng) {
+    const int kb = k0 + gi * 32;
+    load_k_tile<D>(p, g, kb + 32, lane, b0);
+    load_k_tile<D>(p, g, kb + 48, lane, b1);
+    group(kb, a0, a1);
+    group(kb + 32, b0, b1);
+  } else if (gi < ng) {
+    group(k0 + gi * 32, a0, a1);
   }
 
   // fold the 16 lanes (key columns) that share each row
@@ -218,25 +262,34 @@ __global__ __launch_bounds__(256) void prefill_merge_kernel(PrefillParams p) {
 }
 
 // ---- pass 2 -----------------------------------------------------------------
+// Work-group = (block of QB queries, kPrefillKeys2 keys), one wave per KV head.
+// Per 16-key tile each wave adds exp2(scale2 * s - lse) over its G query heads
+// (a lane's four C rows are one query's four heads); after a barrier the KV-
+// head partials are summed in a fixed order into an LDS vote tile, which is
+// written to HBM once at the end. The loop issues no global stores, so its
+// waits are for the one K tile they need (prefetched a tile ahead).
 template <int G, int D>
 __global__ __launch_bounds__(512) void prefill_votes_kernel(PrefillParams p) {
   constexpr int KS = D / 32;
-  constexpr int RT = 8;           // row tiles per wave (128 rows of one KV head)
-  constexpr int QB = 128 / G;     // queries per work-group
+  constexpr int RT = kPrefillRT2;  // row tiles per wave (rows of one KV head)
+  constexpr int QB = 16 * RT / G;  // queries per work-group
+  constexpr int KT = kPrefillKeys2;
   static_assert(G == 4, "a lane's four C rows must be one query's four heads");
   __shared__ float s_v[2][8][QB][16];           // [buffer][KV head][query][key]
+  __shared__ float s_out[QB][KT];               // the work-group's votes
   const int nqb = (p.chunk + QB - 1) / QB;
   const int f = xcd_flat(blockIdx.x, gridDim.x);
   const int qblk = f % nqb;
   const int split = f / nqb;
-  const int lane = threadIdx.x & 63, g = threadIdx.x >> 6;   // one wave per KV head
+  const int tid = threadIdx.x, lane = tid & 63, g = tid >> 6;   // one wave per KV head
   const int nw = blockDim.x >> 6;
   const int qbase = qblk * QB;
   const int qlast = min(qbase + QB, p.chunk) - 1;
-  const int k0 = split * p.key_split2;
-  const int k1 = min(p.n_ctx, k0 + p.key_split2);
+  const int k0 = split * KT;
+  const int k1 = min(p.n_ctx, k0 + KT);
   const int kend = min(k1, p.q_pos0 + qlast + 1);   // keys from here on: zero votes
   const int kall = p.q_pos0 + qbase + 1;            // keys below this: no mask
+  const int nt = kend > k0 ? (kend - k0 + 15) / 16 : 0;
 
   bf16x8_t qf[RT][KS];
 #pragma unroll
@@ -255,64 +308,71 @@ __global__ __launch_bounds__(512) void prefill_votes_kernel(PrefillParams p) {
     }
   const float sc2 = p.scale2;
 
-  uint4 kf[KS], kn[KS];
-  if (k0 < kend) {
+  // one tile: this wave's head-group terms into s_v[b], a barrier, then the
+  // fixed-order sum over the KV heads into the LDS vote tile
+  auto tile = [&](int t, const uint4 (&kf)[KS], int b) {
+    const int kb = k0 + t * 16;
+    f32x4_t sc[RT];
+    qk_tile<RT, KS>(qf, kf, sc);
+    const bool all = kb + 16 <= kall;
+    const int key = kb + (lane & 15);
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) kf[ks] = load_k_frag<D>(p, g, k0, ks, lane);
-  }
-  int buf = 0;
-  for (int kb = k0; kb < kend; kb += 16) {
-    if (kb + 16 < kend) {
+    for (int rt = 0; rt < RT; ++rt) {
+      float v = 0.f;
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) kn[ks] = load_k_frag<D>(p, g, kb + 16, ks, lane);
-    }
-    f32x4_t s[RT];
-    qk_tile<RT, KS>(qf, kf, s);
-    // a lane's four C rows are one query's four heads: add their terms here
-    if (kb + 16 <= kall) {
-#pragma unroll
-      for (int rt = 0; rt < RT; ++rt) {
-        float v = 0.f;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) v += ex2(fmaf(s[rt][i], sc2, -lse[rt][i]));
-        s_v[buf][g][rt * 4 + (lane >> 4)][lane & 15] = v;
-      }
-    } else {
-      const int key = kb + (lane & 15);
-#pragma unroll
-      for (int rt = 0; rt < RT; ++rt) {
-        const int qi = qbase + rt * 4 + (lane >> 4);
-        const bool ok = key <= p.q_pos0 + qi;
-        float v = 0.f;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) v += ex2(fmaf(s[rt][i], sc2, -lse[rt][i]));
-        s_v[buf][g][rt * 4 + (lane >> 4)][lane & 15] = ok ? v : 0.f;
-      }
+      for (int i = 0; i < 4; ++i) v += ex2(fmaf(sc[rt][i], sc2, -lse[rt][i]));
+      const int ql = rt * 4 + (lane >> 4);
+      if (!all && key > p.q_pos0 + qbase + ql) v = 0.f;
+      s_v[b][g][ql][lane & 15] = v;
     }
     __syncthreads();
-    // sum over the KV heads and write the tile's votes
-    for (int e = threadIdx.x; e < QB * 16; e += blockDim.x) {
+    for (int e = tid; e < QB * 16; e += blockDim.x) {
       const int ql = e >> 4, c = e & 15;
       float v = 0.f;
-      for (int gg = 0; gg < nw; ++gg) v += s_v[buf][gg][ql][c];
-      const int qi = qbase + ql, kk = kb + c;
-      if (qi < p.chunk && kk < k1) p.votes[(size_t)qi * p.n_ctx + kk] = v;
-    }
-    buf ^= 1;
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) kf[ks] = kn[ks];
+      for (int gg = 0; gg < 8; ++gg) v += (gg < nw) ? s_v[b][gg][ql][c] : 0.f;
+      s_out[ql][t * 16 + c] = v;
+    }
+  };
+
+  // K fragments one tile ahead; loads past the last tile are clamped in-bounds
+  // reads that nothing uses, so every load is unconditional. Scheduling
+  // barriers keep the compiler from consuming a prefetch as soon as it is
+  // issued.
+  uint4 ka[KS], kb_[KS];
+  if (nt > 0) load_k_tile<D>(p, g, k0, lane, ka);
+  int t = 0;
+  for (; t + 2 < nt; t += 2) {
+    load_k_tile<D>(p, g, k0 + (t + 1) * 16, lane, kb_);
+    __builtin_amdgcn_sched_barrier(0);
+    tile(t, ka, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    load_k_tile<D>(p, g, k0 + (t + 2) * 16, lane, ka);
+    __builtin_amdgcn_sched_barrier(0);
+    tile(t + 1, kb_, 1);
+    __builtin_amdgcn_sched_barrier(0);
   }
-  // keys that no query of this block sees
-  const int z0 = max(k0, kend);
-  for (int e = threadIdx.x; e < QB * (k1 - z0); e += blockDim.x) {
-    const int ql = e / (k1 - z0), kk = z0 + e % (k1 - z0);
-    if (qbase + ql < p.chunk) p.votes[(size_t)(qbase + ql) * p.n_ctx + kk] = 0.f;
+  if (t + 1 < nt) {
+    load_k_tile<D>(p, g, k0 + (t + 1) * 16, lane, kb_);
+    tile(t, ka, 0);
+    tile(t + 1, kb_, 1);
+  } else if (t < nt) {
+    tile(t, ka, 0);
+  }
+  __syncthreads();
+  // the vote tile, coalesced along each query's row; keys no query of the
+  // block sees are zero
+  const int nk = k1 - k0;
+  for (int e = tid; e < QB * nk; e += blockDim.x) {
+    const int ql = e / nk, c = e - ql * nk;
+    if (qbase + ql < p.chunk)
+      p.votes[(size_t)(qbase + ql) * p.n_ctx + k0 + c] = (k0 + c < kend) ? s_out[ql][c] : 0.f;
   }
 }
 
 template <int D>
 static hipError_t launch_lse_g(const PrefillParams& p, hipStream_t s) {
-  const int qb = 256 / p.G;
+  const int qb = 64 * kPrefillRT1 / p.G;
   dim3 grid(((p.chunk + qb - 1) / qb) * p.Hkv * p.nsplit1);
   switch (p.G) {
     case 4: hipLaunchKernelGGL((prefill_lse_kernel<4, D>), grid, dim3(256), 0, s, p); break;
@@ -335,7 +395,7 @@ hipError_t launch_prefill_merge(const PrefillParams& p, hipStream_t s) {
 
 template <int D>
 static hipError_t launch_votes_g(const PrefillParams& p, hipStream_t s) {
-  const int qb = 128 / p.G;
+  const int qb = 16 * kPrefillRT2 / p.G;
   dim3 grid(((p.chunk + qb - 1) / qb) * p.nsplit2);
   dim3 block(64 * p.Hkv);
   switch (p.G) {

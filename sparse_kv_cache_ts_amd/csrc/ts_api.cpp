@@ -743,14 +743,12 @@ ts_status plan_prefill(const ts_kv_layout* L, int chunk, int q_pos0, int n_ctx, 
   p.G = g.G;
   p.D = g.d;
   p.scale2 = g.scale * kLog2eHost;
-  // pass 1: two resident work-groups of 4 waves per CU; pass 2: one of 8 waves
-  const int qb1 = cdiv(chunk, 256 / g.G);
-  int ns1 = std::max(1, 512 / (qb1 * g.Hkv));
+  // pass 1: about one work-group of 4 waves per CU
+  const int qb1 = cdiv(chunk, 64 * kPrefillRT1 / g.G);
+  int ns1 = std::max(1, 256 / (qb1 * g.Hkv));
   p.key_split = cdiv(cdiv(n_ctx, ns1), 32) * 32;
   p.nsplit1 = cdiv(n_ctx, p.key_split);
-  const int qb2 = cdiv(chunk, 128 / g.G);
-  int ns2 = std::max(1, 256 / qb2);
-  p.key_split2 = cdiv(cdiv(n_ctx, ns2), 16) * 16;
+  p.key_split2 = kPrefillKeys2;
   p.nsplit2 = cdiv(n_ctx, p.key_split2);
   Carve c;
   P->lse_part = c.take((size_t)chunk * g.Hq * p.nsplit1 * 8);

@@ -16,6 +16,14 @@ constexpr int kMaxHeadsPerWG = 64; // Hkv * heads-per-slice held by one scoring 
 constexpr int kMaxQHeads = 256;
 constexpr int kMaxSplits = 1024;  // attention splits per (sequence, head)
 constexpr float kLog2eHost = 1.4426950408889634f;
+// prefill log-sum-exp pass: 16-row MFMA tiles per wave (4 waves per work-group,
+// one KV head); every wave reads the same keys, so more rows per wave means
+// fewer key fragments through each CU's L1
+constexpr int kPrefillRT1 = 8;
+// prefill vote pass: 16-row MFMA tiles per wave (one KV head); a work-group
+// covers 16 * kPrefillRT2 / G queries
+constexpr int kPrefillRT2 = 8;
+constexpr int kPrefillKeys2 = 512; // keys per vote-pass work-group (its LDS vote tile)
 
 // ---- per-row control block (uint32 words) ----------------------------------
 // Zeroed at the start of every call that uses it.
