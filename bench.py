@@ -122,6 +122,29 @@ def measure_prefill(ts, W, reps=10, warmup=3):
             "mfma_frac": round(mfma_tflops / MFMA_BF16_PEAK_TFLOPS, 4)}
 
 
+def measure_dense(ts, W, cfg, steps, warmup, copies):
+    """Full softmax attention over every cached token (the method's comparison arm)."""
+    import torch
+    x = W.gen_decode(cfg, device="cuda")
+    Ks = [x["k_cache"]] + [x["k_cache"].clone() for _ in range(copies - 1)]
+    Vs = [x["v_cache"]] + [x["v_cache"].clone() for _ in range(copies - 1)]
+    out = torch.empty(cfg.batch, cfg.num_q_heads, cfg.head_dim, dtype=torch.float32, device="cuda")
+    ws = ts.Workspace()
+    for i in range(warmup):
+        ts.dense_attend(x["q"], Ks[i % copies], Vs[i % copies], x["seq_lens"], out=out, ws=ws)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        ts.dense_attend(x["q"], Ks[i % copies], Vs[i % copies], x["seq_lens"], out=out, ws=ws)
+    torch.cuda.synchronize()
+    us = 1e6 * (time.perf_counter() - t0) / steps
+    kv = 2 * cfg.batch * cfg.seq_len * kv_bytes_per_token(cfg)
+    del Ks, Vs, x
+    torch.cuda.empty_cache()
+    return {"us_per_call": round(us, 2), "kv_bytes": kv, "GBps": round(kv / (us * 1e-6) / 1e9, 1),
+            "us_at_hbm_peak": round(kv / (HBM_PEAK_GBPS * 1e3), 2)}
+
+
 def kv_bytes_per_token(cfg) -> int:
     return cfg.num_kv_heads * cfg.head_dim * (2 if cfg.dtype == "bf16" else 4)
 
@@ -218,6 +241,7 @@ def main():
     ap.add_argument("--no-profile", action="store_true")
     ap.add_argument("--no-hit", action="store_true", help="skip the selection-reuse measurement")
     ap.add_argument("--no-prefill", action="store_true", help="skip the prefill-chunk measurement")
+    ap.add_argument("--no-dense", action="store_true", help="skip the full-attention baseline")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 512 MiB copy kernel (for HBM byte counters)")
     args = ap.parse_args()
@@ -274,6 +298,17 @@ def main():
 
     if not args.no_prefill:
         extra["prefill_chunk"] = measure_prefill(ts, W)
+    if not args.no_dense:
+        dense = measure_dense(ts, W, cfg, args.steps, args.warmup, args.kv_copies)
+        step_us = 1e3 * miss["ms_per_step"]
+        dense["speedup_vs_miss_step"] = round(dense["us_per_call"] / step_us, 3)
+        if "hit_step" in extra:
+            dense["speedup_vs_hit_step"] = round(dense["us_per_call"] / (1e3 * extra["hit_step"]["ms_per_step"]), 3)
+        if "kernels_us" in miss:
+            sparse_att = miss["kernels_us"]["attend"] + miss["kernels_us"]["combine"]
+            dense["sparse_attention_us"] = round(sparse_att, 2)
+            dense["attention_speedup"] = round(dense["us_per_call"] / sparse_att, 2)
+        extra["dense_attention"] = dense
 
     cpu = None
     if not args.no_cpu_baseline:

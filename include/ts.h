@@ -125,6 +125,21 @@ ts_status ts_sparse_attend(const ts_kv_layout* layout /*[host]*/, int32_t batch,
                            void* ws, size_t ws_bytes, void* stream);
 
 /* ---------------------------------------------------------------------------
+ * ts_dense_attend — the comparison arm of the method: ordinary softmax
+ * attention of every query head over all seq_lens[b] cached tokens (the
+ * TokenSelect README's "Result" quotes its speedups against full attention).
+ * Same split-K kernels as ts_sparse_attend with token j in position j, so the
+ * output equals ts_sparse_attend over idx = 0 .. seq_lens[b]-1.
+ *   out  [batch][Hq][d] fp32; an empty sequence gets zeros.
+ * ------------------------------------------------------------------------- */
+ts_status ts_dense_attend_workspace_size(const ts_kv_layout* layout /*[host]*/, int32_t batch,
+                                         size_t* bytes /*[host] out*/);
+ts_status ts_dense_attend(const ts_kv_layout* layout /*[host]*/, int32_t batch, const void* q,
+                          const void* k_cache, const void* v_cache, const int32_t* page_table,
+                          const int32_t* seq_lens, float* out, void* ws, size_t ws_bytes,
+                          void* stream);
+
+/* ---------------------------------------------------------------------------
  * Selection Cache state for up to max_batch sequences of one layer (step 5).
  *   compare_mode 0: compare with the previous step's query (stored every step);
  *   compare_mode 1: compare with the query of the last miss (the anchor).

@@ -22,6 +22,7 @@ import torch
 
 __all__ = [
     "load", "lib_path", "TsError", "KvLayout", "make_layout", "score", "topk", "sparse_attend",
+    "dense_attend",
     "SelCache", "score_prefill", "select_prefill", "Workspace", "EXPORTS",
     "profile_enable", "profile_reset", "profile_read",
 ]
@@ -38,6 +39,7 @@ EXPORTS = [
     "ts_score_workspace_size", "ts_score",
     "ts_topk_workspace_size", "ts_topk",
     "ts_sparse_attend_workspace_size", "ts_sparse_attend",
+    "ts_dense_attend_workspace_size", "ts_dense_attend",
     "ts_sel_cache_create", "ts_sel_cache_reset", "ts_sel_cache_destroy", "ts_sel_cache_stats",
     "ts_decode_step_workspace_size", "ts_decode_step",
     "ts_score_prefill_workspace_size", "ts_score_prefill", "ts_select_prefill",
@@ -88,6 +90,8 @@ def load():
         "ts_topk": ([I32, I32, P, P, I32, P, P, SZ, P], I32),
         "ts_sparse_attend_workspace_size": ([L, I32, I32, SZP], I32),
         "ts_sparse_attend": ([L, I32, P, P, P, P, P, P, I32, P, P, SZ, P], I32),
+        "ts_dense_attend_workspace_size": ([L, I32, SZP], I32),
+        "ts_dense_attend": ([L, I32, P, P, P, P, P, P, P, SZ, P], I32),
         "ts_sel_cache_create": ([I32, I32, I32, I32, I32, ctypes.POINTER(P)], I32),
         "ts_sel_cache_reset": ([P, P], I32),
         "ts_sel_cache_destroy": ([P], I32),
@@ -229,6 +233,25 @@ def sparse_attend(q, k_cache, v_cache, seq_lens, idx, page_table=None, scale=Non
     _check(lib.ts_sparse_attend(ctypes.byref(L), B, _ptr(q), _ptr(k_cache), _ptr(v_cache),
                                 _ptr(page_table), _ptr(seq_lens), _ptr(idx), k, _ptr(out), _ptr(w),
                                 w.numel(), _stream(stream)), "ts_sparse_attend")
+    return out
+
+
+def dense_attend(q, k_cache, v_cache, seq_lens, page_table=None, scale=None, out=None, ws=None,
+                 stream=None):
+    """Full softmax attention over every cached token: [B][Hq][d] fp32."""
+    lib = load()
+    _need_cuda(q, k_cache, v_cache, seq_lens, page_table)
+    L = make_layout(q, k_cache, page_table, scale)
+    B, Hq, d = q.shape
+    if out is None:
+        out = torch.empty(B, Hq, d, dtype=torch.float32, device=q.device)
+    n = ctypes.c_size_t()
+    _check(lib.ts_dense_attend_workspace_size(ctypes.byref(L), B, ctypes.byref(n)),
+           "ts_dense_attend_workspace_size")
+    w = _ws(n.value, q.device, ws)
+    _check(lib.ts_dense_attend(ctypes.byref(L), B, _ptr(q), _ptr(k_cache), _ptr(v_cache),
+                               _ptr(page_table), _ptr(seq_lens), _ptr(out), _ptr(w), w.numel(),
+                               _stream(stream)), "ts_dense_attend")
     return out
 
 

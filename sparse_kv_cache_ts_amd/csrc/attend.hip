@@ -17,7 +17,7 @@
 
 namespace ts {
 
-template <int DT, int D, int GS, bool PAGED>
+template <int DT, int D, int GS, bool PAGED, bool DENSE>
 __global__ __launch_bounds__(256) void attend_kernel(AttendParams p) {
   constexpr int ESZ = DT ? 2 : 4;
   constexpr int ROWB = D * ESZ;
@@ -26,7 +26,7 @@ __global__ __launch_bounds__(256) void attend_kernel(AttendParams p) {
   constexpr int EPC = 16 / ESZ;                            // elements per chunk
   constexpr int EPL = EPC * CPL;                           // elements per lane
   constexpr int W = 4 * CPL;                               // 32-bit words per lane
-  constexpr int UA = 4;                                    // gathered rows in flight per row group
+  constexpr int UA = 4;                                    // rows in flight per row group
   constexpr int RG = 256 / LPR;
 
   __shared__ float s_m[4][GS];
@@ -44,59 +44,24 @@ __global__ __launch_bounds__(256) void attend_kernel(AttendParams p) {
   const int len = p.seq_lens[b];
   const int pbeg = split * p.split;
   const int pend = min(pbeg + p.split, p.nidx);
-  const int32_t* idx = p.idx + (size_t)b * p.nidx;
+  const int32_t* idx = DENSE ? nullptr : p.idx + (size_t)b * p.nidx;
   const int Hkv = p.Hkv;
 
-  // first batch of indices together with the query slice
-  int tok[UA];
-#pragma unroll
-  for (int u = 0; u < UA; ++u) {
-    const int pos = pbeg + rg + u * RG;
-    const int t = pos < pend ? idx[pos] : -1;
-    tok[u] = (t >= 0 && t < len) ? t : -1;
-  }
-  uint32_t qw[GS][W];
-#pragma unroll
-  for (int hh = 0; hh < GS; ++hh) {
-    const int head = kvh * p.G + slice * GS + hh;
-    const char* qb = (const char*)p.q + ((size_t)b * p.Hq + head) * ROWB;
-#pragma unroll
-    for (int c = 0; c < CPL; ++c) {
-      const uint4 v = ld16(qb + (c * LPR + j) * 16);
-      qw[hh][4 * c + 0] = v.x; qw[hh][4 * c + 1] = v.y;
-      qw[hh][4 * c + 2] = v.z; qw[hh][4 * c + 3] = v.w;
+  auto row_of = [&](int t) -> size_t {
+    if constexpr (PAGED) {
+      const int pg = p.page_table[(size_t)b * p.pt_stride + (t >> p.ps_log2)];
+      return ((((size_t)pg << p.ps_log2) + (t & ((1 << p.ps_log2) - 1))) * Hkv + kvh);
+    } else {
+      return (((size_t)b * p.max_len + t) * Hkv + kvh);
     }
-  }
-
-  float m[GS], l[GS], acc[GS][EPL];
-#pragma unroll
-  for (int hh = 0; hh < GS; ++hh) {
-    m[hh] = -INFINITY;
-    l[hh] = 0.f;
-#pragma unroll
-    for (int e = 0; e < EPL; ++e) acc[hh][e] = 0.f;
-  }
-
-  for (int pos0 = pbeg + rg; pos0 < pend; pos0 += RG * UA) {
-    if (pos0 != pbeg + rg) {
-#pragma unroll
-      for (int u = 0; u < UA; ++u) {
-        const int pos = pos0 + u * RG;
-        const int t = pos < pend ? idx[pos] : -1;
-        tok[u] = (t >= 0 && t < len) ? t : -1;
-      }
-    }
-    uint32_t kw[UA][W], vw[UA][W];
+  };
+  // UA rows (tokens tok[u]; -1 = none) into registers
+  auto load_rows = [&](const int (&tok)[UA], uint32_t (&kw)[UA][W], uint32_t (&vw)[UA][W]) {
 #pragma unroll
     for (int u = 0; u < UA; ++u) {
-      if (tok[u] >= 0) {
-        size_t row;
-        if constexpr (PAGED) {
-          const int pg = p.page_table[(size_t)b * p.pt_stride + (tok[u] >> p.ps_log2)];
-          row = ((((size_t)pg << p.ps_log2) + (tok[u] & ((1 << p.ps_log2) - 1))) * Hkv + kvh);
-        } else {
-          row = (((size_t)b * p.max_len + tok[u]) * Hkv + kvh);
-        }
+      if (DENSE || tok[u] >= 0) {
+        // (dense: tok is clamped into the sequence, validity is tracked apart)
+        const size_t row = row_of(DENSE ? tok[u] : tok[u]);
         const char* kp = (const char*)p.k + row * ROWB;
         const char* vp = (const char*)p.v + row * ROWB;
 #pragma unroll
@@ -111,7 +76,12 @@ __global__ __launch_bounds__(256) void attend_kernel(AttendParams p) {
         for (int w = 0; w < W; ++w) { kw[u][w] = 0u; vw[u][w] = 0u; }
       }
     }
-    // scores of the batch, one rescale of the running sums per batch
+  };
+
+  uint32_t qw[GS][W];
+  float m[GS], l[GS], acc[GS][EPL];
+  // scores of a batch, one rescale of the running sums per batch
+  auto consume = [&](const bool (&ok)[UA], const uint32_t (&kw)[UA][W], const uint32_t (&vw)[UA][W]) {
 #pragma unroll
     for (int hh = 0; hh < GS; ++hh) {
       float sc[UA];
@@ -124,7 +94,7 @@ __global__ __launch_bounds__(256) void attend_kernel(AttendParams p) {
           if constexpr (DT == 1) a = dot2_bf16(kw[u][w], qw[hh][w], a);
           else a = fmaf(__uint_as_float(kw[u][w]), __uint_as_float(qw[hh][w]), a);
         }
-        sc[u] = (tok[u] >= 0) ? group_sum<LPR>(a) * p.scale2 : -INFINITY;
+        sc[u] = ok[u] ? group_sum<LPR>(a) * p.scale2 : -INFINITY;
         bm = fmaxf(bm, sc[u]);
       }
       if (bm == -INFINITY) continue;           // nothing valid yet for this row group
@@ -150,6 +120,97 @@ __global__ __launch_bounds__(256) void attend_kernel(AttendParams p) {
         }
         acc[hh][e] = a;
       }
+    }
+  };
+
+  // indices of the first batch (sparse) together with the query slice
+  int tok[UA];
+  if constexpr (!DENSE) {
+#pragma unroll
+    for (int u = 0; u < UA; ++u) {
+      const int pos = pbeg + rg + u * RG;
+      const int t = pos < pend ? idx[pos] : -1;
+      tok[u] = (t >= 0 && t < len) ? t : -1;
+    }
+  }
+#pragma unroll
+  for (int hh = 0; hh < GS; ++hh) {
+    const int head = kvh * p.G + slice * GS + hh;
+    const char* qb = (const char*)p.q + ((size_t)b * p.Hq + head) * ROWB;
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) {
+      const uint4 v = ld16(qb + (c * LPR + j) * 16);
+      qw[hh][4 * c + 0] = v.x; qw[hh][4 * c + 1] = v.y;
+      qw[hh][4 * c + 2] = v.z; qw[hh][4 * c + 3] = v.w;
+    }
+  }
+#pragma unroll
+  for (int hh = 0; hh < GS; ++hh) {
+    m[hh] = -INFINITY;
+    l[hh] = 0.f;
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) acc[hh][e] = 0.f;
+  }
+
+  if constexpr (DENSE) {
+    // contiguous token range [pbeg, pe): batches of RG*UA rows, the next
+    // batch in flight while one is consumed; rows past the end are clamped
+    // to the last token (in bounds) and masked, so every load is
+    // unconditional and the compiler can count them
+    const int pe = min(pend, len);
+    const int nb = pe > pbeg ? (pe - pbeg + RG * UA - 1) / (RG * UA) : 0;
+    uint32_t kA[UA][W], vA[UA][W], kB[UA][W], vB[UA][W];
+    auto batch = [&](int bi, int (&t)[UA], bool (&ok)[UA]) {
+#pragma unroll
+      for (int u = 0; u < UA; ++u) {
+        const int pos = pbeg + bi * RG * UA + u * RG + rg;
+        ok[u] = pos < pe;
+        t[u] = min(pos, pe - 1);
+      }
+    };
+    int tA[UA], tB[UA];
+    bool oA[UA], oB[UA];
+    if (nb > 0) {
+      batch(0, tA, oA);
+      load_rows(tA, kA, vA);
+    }
+    int bi = 0;
+    for (; bi + 2 < nb; bi += 2) {
+      batch(bi + 1, tB, oB);
+      load_rows(tB, kB, vB);
+      __builtin_amdgcn_sched_barrier(0);
+      consume(oA, kA, vA);
+      __builtin_amdgcn_sched_barrier(0);
+      batch(bi + 2, tA, oA);
+      load_rows(tA, kA, vA);
+      __builtin_amdgcn_sched_barrier(0);
+      consume(oB, kB, vB);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    if (bi + 1 < nb) {
+      batch(bi + 1, tB, oB);
+      load_rows(tB, kB, vB);
+      consume(oA, kA, vA);
+      consume(oB, kB, vB);
+    } else if (bi < nb) {
+      consume(oA, kA, vA);
+    }
+  } else {
+    for (int pos0 = pbeg + rg; pos0 < pend; pos0 += RG * UA) {
+      if (pos0 != pbeg + rg) {
+#pragma unroll
+        for (int u = 0; u < UA; ++u) {
+          const int pos = pos0 + u * RG;
+          const int t = pos < pend ? idx[pos] : -1;
+          tok[u] = (t >= 0 && t < len) ? t : -1;
+        }
+      }
+      uint32_t kw[UA][W], vw[UA][W];
+      load_rows(tok, kw, vw);
+      bool ok[UA];
+#pragma unroll
+      for (int u = 0; u < UA; ++u) ok[u] = tok[u] >= 0;
+      consume(ok, kw, vw);
     }
   }
 
@@ -257,7 +318,20 @@ __global__ __launch_bounds__(128) void combine_kernel(CombineParams p) {
       o3 = fmaf(a[s + 3], s < ns - 3 ? s_w[s + 3] : 0.f, o3);
     }
   }
-  for (int s = SB; s < ns; ++s) o0 = fmaf(own_d ? pa[(size_t)s * p.d] : 0.f, s_w[s], o0);
+  // more splits (dense attention): further register blocks of SB loads each
+  for (int s0 = SB; s0 < ns; s0 += SB) {
+#pragma unroll
+    for (int s = 0; s < SB; ++s) a[s] = (own_d && s0 + s < ns) ? pa[(size_t)(s0 + s) * p.d] : 0.f;
+#pragma unroll
+    for (int s = 0; s < SB; s += 4) {
+      if (s0 + s < ns) {
+        o0 = fmaf(a[s], s_w[s0 + s], o0);
+        o1 = fmaf(a[s + 1], s0 + s + 1 < ns ? s_w[s0 + s + 1] : 0.f, o1);
+        o2 = fmaf(a[s + 2], s0 + s + 2 < ns ? s_w[s0 + s + 2] : 0.f, o2);
+        o3 = fmaf(a[s + 3], s0 + s + 3 < ns ? s_w[s0 + s + 3] : 0.f, o3);
+      }
+    }
+  }
   if (own_d) p.out[((size_t)b * p.Hq + h) * p.d + tid] = (L > 0.f) ? ((o0 + o1) + (o2 + o3)) / L : 0.f;
 
   // Selection-Cache state update, spread over the head blocks of a sequence
@@ -288,11 +362,11 @@ __global__ __launch_bounds__(128) void combine_kernel(CombineParams p) {
   }
 }
 
-template <int DT, int D, bool PAGED>
+template <int DT, int D, bool PAGED, bool DENSE>
 static hipError_t launch_attend_gs(const AttendParams& p, hipStream_t s) {
   dim3 grid(p.nsplit, p.Hkv * p.nslices, p.B);
   switch (p.GS) {
-#define TS_GS(n) case n: hipLaunchKernelGGL((attend_kernel<DT, D, n, PAGED>), grid, dim3(256), 0, s, p); break;
+#define TS_GS(n) case n: hipLaunchKernelGGL((attend_kernel<DT, D, n, PAGED, DENSE>), grid, dim3(256), 0, s, p); break;
     TS_GS(1) TS_GS(2) TS_GS(3) TS_GS(4) TS_GS(5) TS_GS(6) TS_GS(7) TS_GS(8)
 #undef TS_GS
     default: return hipErrorInvalidValue;
@@ -300,12 +374,18 @@ static hipError_t launch_attend_gs(const AttendParams& p, hipStream_t s) {
   return hipGetLastError();
 }
 
-hipError_t launch_attend(int dtype, int d, bool paged, const AttendParams& p, hipStream_t s) {
-  if (dtype == 1 && d == 128) return paged ? launch_attend_gs<1, 128, true>(p, s) : launch_attend_gs<1, 128, false>(p, s);
-  if (dtype == 1 && d == 64) return paged ? launch_attend_gs<1, 64, true>(p, s) : launch_attend_gs<1, 64, false>(p, s);
-  if (dtype == 0 && d == 128) return paged ? launch_attend_gs<0, 128, true>(p, s) : launch_attend_gs<0, 128, false>(p, s);
-  if (dtype == 0 && d == 64) return paged ? launch_attend_gs<0, 64, true>(p, s) : launch_attend_gs<0, 64, false>(p, s);
+template <bool DENSE>
+static hipError_t launch_attend_mode(int dtype, int d, bool paged, const AttendParams& p, hipStream_t s) {
+  if (dtype == 1 && d == 128) return paged ? launch_attend_gs<1, 128, true, DENSE>(p, s) : launch_attend_gs<1, 128, false, DENSE>(p, s);
+  if (dtype == 1 && d == 64) return paged ? launch_attend_gs<1, 64, true, DENSE>(p, s) : launch_attend_gs<1, 64, false, DENSE>(p, s);
+  if (dtype == 0 && d == 128) return paged ? launch_attend_gs<0, 128, true, DENSE>(p, s) : launch_attend_gs<0, 128, false, DENSE>(p, s);
+  if (dtype == 0 && d == 64) return paged ? launch_attend_gs<0, 64, true, DENSE>(p, s) : launch_attend_gs<0, 64, false, DENSE>(p, s);
   return hipErrorInvalidValue;
+}
+
+// idx null: dense attention over every cached token
+hipError_t launch_attend(int dtype, int d, bool paged, const AttendParams& p, hipStream_t s) {
+  return p.idx ? launch_attend_mode<false>(dtype, d, paged, p, s) : launch_attend_mode<true>(dtype, d, paged, p, s);
 }
 
 hipError_t launch_combine(const CombineParams& p, hipStream_t s) {

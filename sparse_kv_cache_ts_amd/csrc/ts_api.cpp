@@ -552,6 +552,57 @@ ts_status ts_sparse_attend(const ts_kv_layout* L, int32_t batch, const void* q, 
   return ok();
 }
 
+// ---------------------------------------------------------- ts_dense_attend
+
+}  // extern "C"
+
+namespace {
+// split-K over every cached token: 256-row multiples, at most 256 splits
+void plan_dense(const Geo& g, int B, Carve& c, AttendPlan& a) {
+  int split = 256;
+  while (cdiv(g.max_len, split) > 256) split += 256;
+  a.split = split;
+  a.nsplit = cdiv(g.max_len, split);
+  a.pm = c.take((size_t)B * g.Hq * a.nsplit * 4);
+  a.pl = c.take((size_t)B * g.Hq * a.nsplit * 4);
+  a.pacc = c.take((size_t)B * g.Hq * a.nsplit * g.d * 4);
+}
+}  // namespace
+
+extern "C" {
+
+ts_status ts_dense_attend_workspace_size(const ts_kv_layout* L, int32_t batch, size_t* bytes) {
+  Geo g;
+  TS_TRY(check_layout(L, batch, &g));
+  if (!bytes) return fail(TS_ERR_INVALID_ARG, "bytes is NULL");
+  Carve c;
+  AttendPlan a;
+  plan_dense(g, batch, c, a);
+  *bytes = c.off;
+  return ok();
+}
+
+ts_status ts_dense_attend(const ts_kv_layout* L, int32_t batch, const void* q, const void* k_cache,
+                          const void* v_cache, const int32_t* page_table, const int32_t* seq_lens,
+                          float* out, void* ws, size_t ws_bytes, void* stream) {
+  Geo g;
+  TS_TRY(check_layout(L, batch, &g));
+  if (!q || !k_cache || !v_cache || !seq_lens || !out)
+    return fail(TS_ERR_INVALID_ARG, "NULL tensor pointer");
+  if (g.paged && !page_table) return fail(TS_ERR_INVALID_ARG, "paged layout needs a page_table");
+  Carve c;
+  AttendPlan a;
+  plan_dense(g, batch, c, a);
+  TS_TRY(check_ws(ws, ws_bytes, c.off));
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  AttendParams ap = attend_params(g, a, batch, ws, q, k_cache, v_cache,
+                                  g.paged ? page_table : nullptr, seq_lens, nullptr, g.max_len);
+  TS_LAUNCH_K(kKAttend, launch_attend(g.dtype, g.d, g.paged, ap, st), "dense attention");
+  CombineParams cp = combine_params(g, a, batch, ws, out);
+  TS_LAUNCH_K(kKCombine, launch_combine(cp, st), "combine");
+  return ok();
+}
+
 // ------------------------------------------------------------ Selection Cache
 
 ts_status ts_sel_cache_create(int32_t max_batch, int32_t num_q_heads, int32_t head_dim, int32_t k,

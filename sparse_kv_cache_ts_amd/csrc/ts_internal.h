@@ -134,7 +134,7 @@ struct AttendParams {
   const void* v;
   const int32_t* page_table;
   const int32_t* seq_lens;
-  const int32_t* idx;       // [B][nidx]
+  const int32_t* idx;       // [B][nidx], or null: position j is token j (dense attention)
   float* pm;                // [B][Hq][nsplit] running max (base 2)
   float* pl;                // [B][Hq][nsplit] sum of exp2
   float* pacc;              // [B][Hq][nsplit][d] weighted value sums
