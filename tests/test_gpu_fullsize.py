@@ -87,3 +87,32 @@ def test_selection_cache_run_full_size(gpu_lib):
                      att_steps=[0, 1, 2, 31, 32, 33, 127, 255])
     for t in range(rc.steps):
         assert (hits[t] == (0 if t % rc.jump_every == 0 else 1)).all(), f"step {t}"
+
+
+def test_topk_rows_beyond_the_lds_bitmap(gpu_lib):
+    """Rows longer than 262144 tokens: the selection bitmap lives in HBM, and
+    ties/overflowing candidate lists fall back to rescanning the row."""
+    ts = gpu_lib
+    g = torch.Generator(device="cpu").manual_seed(77)
+    lens = [262145, 300000, 600000, 431111]
+    stride = 600000
+    rows = [torch.rand(stride, generator=g),
+            torch.randint(0, 4, (stride,), generator=g).float(),
+            torch.exp(torch.randn(stride, generator=g) * 8),
+            torch.randn(stride, generator=g)]
+    votes = torch.stack(rows)
+    for k in (1, 4096, 20000):
+        idx = ts.topk(votes.cuda(), torch.tensor(lens, dtype=torch.int32, device="cuda"), k)
+        torch.cuda.synchronize()
+        got = idx.cpu().numpy()
+        v = votes.numpy().astype(np.float64)
+        for r, n in enumerate(lens):
+            assert np.array_equal(got[r], O.top_k(v[r, :n], k)), f"row {r} (len {n}), k {k}"
+
+
+def test_decode_step_300k_tokens(gpu_lib):
+    """One sequence of 300000 tokens (beyond the LDS bitmap), 8/2 heads."""
+    cfg = W.DecodeConfig("g4-d128-bf16-300k", batch=1, num_q_heads=8, num_kv_heads=2,
+                         head_dim=128, seq_len=300000, dtype="bf16", k=4096, seed=78,
+                         heavy_frac=0.01)
+    _decode_full(gpu_lib, cfg)
