@@ -360,8 +360,12 @@ __global__ __launch_bounds__(64) void lse_kernel(LseParams p) {
   if (lane == 0) p.lse[(size_t)b * p.Hq + h] = Mw + log2f(Lw);
 }
 
-// votes: kVoteTile tokens per work-group, one per thread; a token's logits
-// for all heads are contiguous and loaded at once before any exp2.
+// votes: kVoteTile tokens per work-group. A token's logits for all heads are
+// contiguous (token-major), so when Hq is a multiple of 4 eight lanes share a
+// token: lane i of the group loads heads 4i..4i+3 (and 32 further on, for
+// Hq > 32) with one 16-byte load, a wave instruction reads eight consecutive
+// tokens' rows as one contiguous range, and the lanes' partial sums meet by
+// DPP. Each group takes 8 tokens, all loads issued before any exp2.
 __global__ __launch_bounds__(256) void votes_kernel(VoteParams p) {
   __shared__ float s_lse[kMaxQHeads];
   __shared__ uint32_t s_hist[1 << kHist0Bits];
@@ -378,33 +382,56 @@ __global__ __launch_bounds__(256) void votes_kernel(VoteParams p) {
     for (int i = tid; i < (1 << kHist0Bits); i += 256) s_hist[i] = 0u;
   __syncthreads();
 
-  const int j = start + tid;
-  if (j < len) {
-    const float* lg = p.logits + ((size_t)b * p.Lpad + j) * Hq;
-    float v = 0.f;
-    if ((Hq & 3) == 0) {
-      constexpr int HB = 8;                      // float4 groups in flight
-      for (int h0 = 0; h0 < Hq; h0 += 4 * HB) {
-        float4 sv[HB];
+  if ((Hq & 3) == 0 && Hq <= kMaxQHeads) {
+    constexpr int TPG = 8;                       // tokens per lane group and round
+    constexpr int WT = kVoteTile / 4;            // tokens per wave
+    const int li = tid & 7;                      // lane in the group
+    const int wv = tid >> 6, gi = (tid >> 3) & 7;
+    const int nr = (Hq + 31) / 32;               // 16-byte loads per lane and token
+    for (int c0 = 0; c0 < WT; c0 += 8 * TPG) {
+      float v[TPG];
 #pragma unroll
-        for (int u = 0; u < HB; ++u)
-          sv[u] = (h0 + 4 * u < Hq) ? ldf4(lg + h0 + 4 * u) : make_float4(0.f, 0.f, 0.f, 0.f);
+      for (int t = 0; t < TPG; ++t) v[t] = 0.f;
+      for (int r = 0; r < nr; ++r) {
+        const int h = 32 * r + 4 * li;
+        const bool has = h < Hq;
+        float4 x[TPG];
 #pragma unroll
-        for (int u = 0; u < HB; ++u) {
-          const int h = h0 + 4 * u;
-          if (h < Hq) {
-            v += ex2(sv[u].x - s_lse[h]);
-            v += ex2(sv[u].y - s_lse[h + 1]);
-            v += ex2(sv[u].z - s_lse[h + 2]);
-            v += ex2(sv[u].w - s_lse[h + 3]);
-          }
+        for (int t = 0; t < TPG; ++t) {
+          const int j = start + wv * WT + c0 + t * 8 + gi;
+          x[t] = (has && j < len) ? ldf4(p.logits + ((size_t)b * p.Lpad + j) * Hq + h)
+                                  : make_float4(-INFINITY, -INFINITY, -INFINITY, -INFINITY);
+        }
+        if (has) {
+          const float l0 = s_lse[h], l1 = s_lse[h + 1], l2 = s_lse[h + 2], l3 = s_lse[h + 3];
+#pragma unroll
+          for (int t = 0; t < TPG; ++t)
+            v[t] += (ex2(x[t].x - l0) + ex2(x[t].y - l1)) + (ex2(x[t].z - l2) + ex2(x[t].w - l3));
         }
       }
-    } else {
-      for (int h = 0; h < Hq; ++h) v += ex2(lg[h] - s_lse[h]);
+#pragma unroll
+      for (int t = 0; t < TPG; ++t) {
+        // sum over the 8 lanes of the group (every lane gets it)
+        float sum = v[t];
+        sum += dpp_f<0xB1>(sum);
+        sum += dpp_f<0x4E>(sum);
+        sum += dpp_f<0x141>(sum);
+        const int j = start + wv * WT + c0 + t * 8 + gi;
+        if (li == 0 && j < len) {
+          p.votes[(size_t)b * p.vote_stride + j] = sum;
+          if (p.do_hist) atomicAdd(&s_hist[float_key(sum) >> (32 - kHist0Bits)], 1u);
+        }
+      }
     }
-    p.votes[(size_t)b * p.vote_stride + j] = v;
-    if (p.do_hist) atomicAdd(&s_hist[float_key(v) >> (32 - kHist0Bits)], 1u);
+  } else {
+    // any head count: one token per thread
+    for (int j = start + tid; j < min(len, start + kVoteTile); j += 256) {
+      const float* lg = p.logits + ((size_t)b * p.Lpad + j) * Hq;
+      float v = 0.f;
+      for (int h = 0; h < Hq; ++h) v += ex2(lg[h] - s_lse[h]);
+      p.votes[(size_t)b * p.vote_stride + j] = v;
+      if (p.do_hist) atomicAdd(&s_hist[float_key(v) >> (32 - kHist0Bits)], 1u);
+    }
   }
   if (!p.do_hist) return;
   __syncthreads();
