@@ -105,18 +105,31 @@ def measure_prefill(ts, W, reps=10, warmup=3):
     torch.cuda.synchronize()
     ts.profile_enable(False)
     kern = {n: (c, ms) for n, (c, ms) in ts.profile_read().items() if c}
+    # each query then attends over its own selection
+    out = torch.empty(cfg.chunk, cfg.num_q_heads, cfg.head_dim, dtype=torch.float32, device="cuda")
+    aws = ts.Workspace()
+    for _ in range(warmup):
+        ts.sparse_attend_prefill(x["q"], x["k_cache"], x["v_cache"], q0, idx, out=out, ws=aws)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(reps):
+        ts.sparse_attend_prefill(x["q"], x["k_cache"], x["v_cache"], q0, idx, out=out, ws=aws)
+    torch.cuda.synchronize()
+    att_us = 1e6 * (time.perf_counter() - t0) / reps
     visible = sum(q0 + i + 1 for i in range(cfg.chunk))
     flop = 2.0 * cfg.num_q_heads * cfg.head_dim * visible          # one Q.K^T product
     t_lse = kern["prefill_lse"][1] / reps * 1e-3                   # pass 1 + merge
     t_vote = kern["prefill_votes"][1] / reps * 1e-3
     # pass 1 and pass 2 each evaluate every visible product once
     mfma_tflops = 2 * flop / (t_lse + t_vote) / 1e12
-    del x, votes, idx
+    del x, votes, idx, out
     torch.cuda.empty_cache()
     return {"workload": "512 queries x 65536 keys, 32/8 heads, d=128, bf16, top-k 4096",
             "us_per_chunk": round(1e6 * wall, 1),
             "scoring_us": round(1e6 * (t_lse + t_vote), 1),
             "kernels_us": {n: round(1e3 * ms / reps, 1) for n, (c, ms) in kern.items()},
+            "sparse_attention_us": round(att_us, 1),
+            "gathered_kv_bytes": cfg.chunk * cfg.k * 2 * cfg.num_kv_heads * cfg.head_dim * 2,
             "qkt_gflop_per_pass": round(flop / 1e9, 1),
             "mfma_tflops": round(mfma_tflops, 1),
             "mfma_frac": round(mfma_tflops / MFMA_BF16_PEAK_TFLOPS, 4)}

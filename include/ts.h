@@ -125,6 +125,25 @@ ts_status ts_sparse_attend(const ts_kv_layout* layout /*[host]*/, int32_t batch,
                            void* ws, size_t ws_bytes, void* stream);
 
 /* ---------------------------------------------------------------------------
+ * ts_sparse_attend_prefill — step 4 for a prefill chunk: query i (position
+ * q_pos0 + i) attends, with every head, over the rows its own selection names
+ * (TokenSelect README, "Key Takeaways": attention over the selected tokens).
+ *   q        [chunk][Hq][d], k_cache / v_cache [n_ctx][Hkv][d] contiguous
+ *            (layout.page_size 0, layout.max_len >= n_ctx), same dtype
+ *   idx      [chunk][k] int32: row i's indices, each < q_pos0 + i + 1 (others,
+ *            and negative entries, are skipped), e.g. from ts_select_prefill
+ *   out      [chunk][Hq][d] fp32; a row with no valid index gets zeros.
+ *   Requires q_pos0 >= 0 and q_pos0 + chunk <= n_ctx.
+ * ------------------------------------------------------------------------- */
+ts_status ts_sparse_attend_prefill_workspace_size(const ts_kv_layout* layout /*[host]*/,
+                                                  int32_t chunk, int32_t k,
+                                                  size_t* bytes /*[host] out*/);
+ts_status ts_sparse_attend_prefill(const ts_kv_layout* layout /*[host]*/, int32_t chunk,
+                                   int32_t q_pos0, const void* q, const void* k_cache,
+                                   const void* v_cache, int32_t n_ctx, const int32_t* idx,
+                                   int32_t k, float* out, void* ws, size_t ws_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------
  * ts_dense_attend — the comparison arm of the method: ordinary softmax
  * attention of every query head over all seq_lens[b] cached tokens (the
  * TokenSelect README's "Result" quotes its speedups against full attention).

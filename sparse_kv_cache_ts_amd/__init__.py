@@ -22,7 +22,7 @@ import torch
 
 __all__ = [
     "load", "lib_path", "TsError", "KvLayout", "make_layout", "score", "topk", "sparse_attend",
-    "dense_attend",
+    "dense_attend", "sparse_attend_prefill",
     "SelCache", "score_prefill", "select_prefill", "Workspace", "EXPORTS",
     "profile_enable", "profile_reset", "profile_read",
 ]
@@ -40,6 +40,7 @@ EXPORTS = [
     "ts_topk_workspace_size", "ts_topk",
     "ts_sparse_attend_workspace_size", "ts_sparse_attend",
     "ts_dense_attend_workspace_size", "ts_dense_attend",
+    "ts_sparse_attend_prefill_workspace_size", "ts_sparse_attend_prefill",
     "ts_sel_cache_create", "ts_sel_cache_reset", "ts_sel_cache_destroy", "ts_sel_cache_stats",
     "ts_decode_step_workspace_size", "ts_decode_step",
     "ts_score_prefill_workspace_size", "ts_score_prefill", "ts_select_prefill",
@@ -92,6 +93,8 @@ def load():
         "ts_sparse_attend": ([L, I32, P, P, P, P, P, P, I32, P, P, SZ, P], I32),
         "ts_dense_attend_workspace_size": ([L, I32, SZP], I32),
         "ts_dense_attend": ([L, I32, P, P, P, P, P, P, P, SZ, P], I32),
+        "ts_sparse_attend_prefill_workspace_size": ([L, I32, I32, SZP], I32),
+        "ts_sparse_attend_prefill": ([L, I32, I32, P, P, P, I32, P, I32, P, P, SZ, P], I32),
         "ts_sel_cache_create": ([I32, I32, I32, I32, I32, ctypes.POINTER(P)], I32),
         "ts_sel_cache_reset": ([P, P], I32),
         "ts_sel_cache_destroy": ([P], I32),
@@ -362,6 +365,30 @@ def select_prefill(q, k_ctx, q_pos0: int, k: int, scale=None, votes=None, idx=No
                                  _ptr(votes), _ptr(idx), _ptr(w), w.numel(), _stream(stream)),
            "ts_select_prefill")
     return votes, idx
+
+
+def sparse_attend_prefill(q, k_ctx, v_ctx, q_pos0: int, idx, scale=None, out=None, ws=None,
+                          stream=None):
+    """Query i of a prefill chunk attends over its own selection idx[i]: [C][Hq][d] fp32."""
+    lib = load()
+    _need_cuda(q, k_ctx, v_ctx, idx)
+    if idx.dtype != torch.int32:
+        raise TypeError("idx must be int32")
+    if v_ctx.shape != k_ctx.shape or v_ctx.dtype != k_ctx.dtype:
+        raise ValueError("K and V shapes/dtypes differ")
+    L = _prefill_layout(q, k_ctx, scale)
+    C, Hq, d = q.shape
+    n_ctx, k = k_ctx.shape[0], idx.shape[1]
+    if out is None:
+        out = torch.empty(C, Hq, d, dtype=torch.float32, device=q.device)
+    n = ctypes.c_size_t()
+    _check(lib.ts_sparse_attend_prefill_workspace_size(ctypes.byref(L), C, k, ctypes.byref(n)),
+           "ts_sparse_attend_prefill_workspace_size")
+    w = _ws(n.value, q.device, ws)
+    _check(lib.ts_sparse_attend_prefill(ctypes.byref(L), C, q_pos0, _ptr(q), _ptr(k_ctx), _ptr(v_ctx),
+                                        n_ctx, _ptr(idx), k, _ptr(out), _ptr(w), w.numel(),
+                                        _stream(stream)), "ts_sparse_attend_prefill")
+    return out
 
 
 def profile_enable(on: bool = True):

@@ -41,7 +41,8 @@ __global__ __launch_bounds__(256) void attend_kernel(AttendParams p) {
   const int j = tid % LPR;
   const int rg = tid / LPR;
   const int wv = tid >> 6, lane = tid & 63;
-  const int len = p.seq_lens[b];
+  const int len = p.seq_lens ? p.seq_lens[b] : p.len_base + b;
+  const int bkv = p.kv_shared ? 0 : b;
   const int pbeg = split * p.split;
   const int pend = min(pbeg + p.split, p.nidx);
   const int32_t* idx = DENSE ? nullptr : p.idx + (size_t)b * p.nidx;
@@ -52,7 +53,7 @@ __global__ __launch_bounds__(256) void attend_kernel(AttendParams p) {
       const int pg = p.page_table[(size_t)b * p.pt_stride + (t >> p.ps_log2)];
       return ((((size_t)pg << p.ps_log2) + (t & ((1 << p.ps_log2) - 1))) * Hkv + kvh);
     } else {
-      return (((size_t)b * p.max_len + t) * Hkv + kvh);
+      return (((size_t)bkv * p.max_len + t) * Hkv + kvh);
     }
   };
   // UA rows (tokens tok[u]; -1 = none) into registers

@@ -552,6 +552,57 @@ ts_status ts_sparse_attend(const ts_kv_layout* L, int32_t batch, const void* q, 
   return ok();
 }
 
+// ------------------------------------------------ ts_sparse_attend_prefill
+
+namespace {
+ts_status check_prefill_attend(const ts_kv_layout* L, int chunk, int q_pos0, int n_ctx, int k,
+                               Geo* g) {
+  TS_TRY(check_layout(L, 1, g));
+  if (g->paged) return fail(TS_ERR_UNSUPPORTED, "prefill attention needs a contiguous K/V");
+  if (chunk < 1 || n_ctx < 1 || k < 1) return fail(TS_ERR_INVALID_ARG, "chunk, n_ctx and k must be >= 1");
+  if (q_pos0 < 0 || (long)q_pos0 + chunk > n_ctx)
+    return fail(TS_ERR_INVALID_ARG, "need 0 <= q_pos0 and q_pos0 + chunk <= n_ctx");
+  if (n_ctx > g->max_len) return fail(TS_ERR_INVALID_ARG, "n_ctx exceeds layout max_len");
+  return TS_OK;
+}
+}  // namespace
+
+ts_status ts_sparse_attend_prefill_workspace_size(const ts_kv_layout* L, int32_t chunk, int32_t k,
+                                                  size_t* bytes) {
+  if (!bytes) return fail(TS_ERR_INVALID_ARG, "bytes is NULL");
+  Geo g;
+  TS_TRY(check_layout(L, 1, &g));
+  if (chunk < 1 || k < 1) return fail(TS_ERR_INVALID_ARG, "chunk and k must be >= 1");
+  Carve c;
+  AttendPlan a;
+  plan_attend(g, chunk, k, c, a);
+  *bytes = c.off;
+  return ok();
+}
+
+ts_status ts_sparse_attend_prefill(const ts_kv_layout* L, int32_t chunk, int32_t q_pos0,
+                                   const void* q, const void* k_cache, const void* v_cache,
+                                   int32_t n_ctx, const int32_t* idx, int32_t k, float* out,
+                                   void* ws, size_t ws_bytes, void* stream) {
+  Geo g;
+  TS_TRY(check_prefill_attend(L, chunk, q_pos0, n_ctx, k, &g));
+  if (!q || !k_cache || !v_cache || !idx || !out) return fail(TS_ERR_INVALID_ARG, "NULL tensor pointer");
+  Carve c;
+  AttendPlan a;
+  plan_attend(g, chunk, k, c, a);
+  TS_TRY(check_ws(ws, ws_bytes, c.off));
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  // the chunk's queries are the rows; row i sees q_pos0 + i + 1 tokens of
+  // the one shared context
+  AttendParams ap = attend_params(g, a, chunk, ws, q, k_cache, v_cache, nullptr, nullptr, idx, k);
+  ap.len_base = q_pos0 + 1;
+  ap.kv_shared = 1;
+  TS_LAUNCH_K(kKAttend, launch_attend(g.dtype, g.d, false, ap, st), "prefill sparse attention");
+  CombineParams cp = combine_params(g, a, chunk, ws, out);
+  TS_LAUNCH_K(kKCombine, launch_combine(cp, st), "combine");
+  return ok();
+}
+
 // ---------------------------------------------------------- ts_dense_attend
 
 }  // extern "C"

@@ -140,6 +140,9 @@ struct AttendParams {
   float* pacc;              // [B][Hq][nsplit][d] weighted value sums
   int B, Hq, Hkv, G, GS, nslices, max_len, ps_log2, pt_stride, nidx, nsplit, split;
   float scale2;
+  // prefill rows: seq_lens null gives row b the length len_base + b, and
+  // kv_shared != 0 makes every row read the one contiguous K/V of the context
+  int len_base, kv_shared;
 };
 
 struct CombineParams {

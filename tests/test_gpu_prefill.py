@@ -107,3 +107,63 @@ def test_prefill_rejects_unsupported(gpu_lib):
     with pytest.raises(ts.TsError) as e:
         ts.score_prefill(q.float(), k.float(), 96)                    # fp32
     assert e.value.status == ts.TS_ERR_UNSUPPORTED
+
+
+ATT_CASES = [SMALL[0], SMALL[1], SMALL[3], SMALL[4]]
+
+
+@pytest.mark.parametrize("case", ATT_CASES, ids=lambda c: c[0].name)
+def test_prefill_sparse_attention(gpu_lib, case):
+    """Each query attends over its own selection (from select_prefill)."""
+    from tests.parity import check_attention
+    ts = gpu_lib
+    cfg, q0 = case
+    x = W.gen_prefill(cfg, device="cuda")
+    _, idx = ts.select_prefill(x["q"], x["k_cache"], q0, cfg.k)
+    out = ts.sparse_attend_prefill(x["q"], x["k_cache"], x["v_cache"], q0, idx)
+    torch.cuda.synchronize()
+    Q, K, V = np64(x["q"]), np32(x["k_cache"]), np32(x["v_cache"])
+    gi, o = idx.cpu().numpy(), np64(out)
+    for i in range(cfg.chunk):
+        n = q0 + i + 1
+        ref = O.sparse_attention(Q[i], K[:n], V[:n], gi[i])
+        check_attention(o[i], ref, 1e-2)
+
+
+def test_prefill_sparse_attention_skips_invalid(gpu_lib):
+    """Indices at or past a row's causal limit, and negative ones, are skipped."""
+    from tests.parity import check_attention
+    ts = gpu_lib
+    cfg, q0 = SMALL[1]
+    x = W.gen_prefill(cfg, device="cuda")
+    C = cfg.chunk
+    g = torch.Generator(device="cpu").manual_seed(5)
+    idx = torch.randint(-3, cfg.n_ctx + 5, (C, 50), generator=g, dtype=torch.int32)
+    idx[0, :] = -1                                   # a row with nothing valid
+    out = ts.sparse_attend_prefill(x["q"], x["k_cache"], x["v_cache"], q0, idx.cuda())
+    torch.cuda.synchronize()
+    Q, K, V = np64(x["q"]), np32(x["k_cache"]), np32(x["v_cache"])
+    gi, o = idx.numpy(), np64(out)
+    assert (o[0] == 0).all()
+    for i in range(1, C):
+        n = q0 + i + 1
+        sel = gi[i][(gi[i] >= 0) & (gi[i] < n)]
+        ref = O.sparse_attention(Q[i], K[:n], V[:n], sel)
+        check_attention(o[i], ref, 1e-2)
+
+
+def test_prefill_sparse_attention_full_size(gpu_lib):
+    """512 x 65536, top-4096 per query: sampled rows against the oracle."""
+    from tests.parity import check_attention
+    ts = gpu_lib
+    cfg = W.PREFILL_64K
+    x = W.gen_prefill(cfg, device="cuda")
+    q0 = x["q_pos0"]
+    _, idx = ts.select_prefill(x["q"], x["k_cache"], q0, cfg.k)
+    out = ts.sparse_attend_prefill(x["q"], x["k_cache"], x["v_cache"], q0, idx)
+    torch.cuda.synchronize()
+    Q, K, V = np64(x["q"]), np32(x["k_cache"]), np32(x["v_cache"])
+    gi, o = idx.cpu().numpy(), np64(out)
+    for i in [0, 1, 200, 511]:
+        n = q0 + i + 1
+        check_attention(o[i], O.sparse_attention(Q[i], K[:n], V[:n], gi[i]), 1e-2)

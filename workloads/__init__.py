@@ -204,7 +204,8 @@ def rope_rotate_half(x: torch.Tensor, pos: torch.Tensor, base: float) -> torch.T
 
 
 def gen_prefill(cfg: PrefillConfig, device="cpu") -> dict:
-    """Q [chunk][Hq][d] and K [n_ctx][Hkv][d], N(0,1) then rotary at true positions."""
+    """Q [chunk][Hq][d] and K [n_ctx][Hkv][d], N(0,1) then rotary at true positions;
+    V [n_ctx][Hkv][d] N(0,1) for the chunk's attention."""
     g = _gen(cfg.seed, device)
     dt = torch_dtype(cfg.dtype)
     Q = torch.randn(cfg.chunk, cfg.num_q_heads, cfg.head_dim, generator=g, device=device)
@@ -213,8 +214,10 @@ def gen_prefill(cfg: PrefillConfig, device="cpu") -> dict:
     kpos = torch.arange(cfg.n_ctx, device=device)
     Q = rope_rotate_half(Q, qpos, cfg.rope_base)
     K = rope_rotate_half(K, kpos, cfg.rope_base)
+    # V ~ N(0,1), drawn after Q and K so those do not depend on it
+    V = torch.randn(cfg.n_ctx, cfg.num_kv_heads, cfg.head_dim, generator=g, device=device)
     return {"q": Q.to(dt).contiguous(), "k_cache": K.to(dt).contiguous(),
-            "q_pos0": cfg.q_pos0}
+            "v_cache": V.to(dt).contiguous(), "q_pos0": cfg.q_pos0}
 
 
 def gen_query_process(steps: int, batch: int, num_q_heads: int, head_dim: int, seed: int,
