@@ -125,6 +125,20 @@ ts_status ts_sparse_attend(const ts_kv_layout* layout /*[host]*/, int32_t batch,
                            void* ws, size_t ws_bytes, void* stream);
 
 /* ---------------------------------------------------------------------------
+ * ts_append_kv — the decode loop's cache growth: sequence b's new K and V rows
+ * (k_new, v_new [batch][Hkv][d], the cache's dtype) are written at position
+ * seq_lens[b], then seq_lens[b] is incremented on the device. Everything stays
+ * on the stream, so "append, then ts_decode_step" can be captured once in a
+ * HIP graph and replayed for every token.
+ *   Contiguous caches: a position >= layout.max_len is skipped (length kept).
+ *   Paged caches: the page holding the position must already be in
+ *   page_table (a negative entry is skipped likewise).
+ * ------------------------------------------------------------------------- */
+ts_status ts_append_kv(const ts_kv_layout* layout /*[host]*/, int32_t batch, const void* k_new,
+                       const void* v_new, void* k_cache, void* v_cache,
+                       const int32_t* page_table, int32_t* seq_lens, void* stream);
+
+/* ---------------------------------------------------------------------------
  * ts_sparse_attend_prefill — step 4 for a prefill chunk: query i (position
  * q_pos0 + i) attends, with every head, over the rows its own selection names
  * (TokenSelect README, "Key Takeaways": attention over the selected tokens).

@@ -22,7 +22,7 @@ import torch
 
 __all__ = [
     "load", "lib_path", "TsError", "KvLayout", "make_layout", "score", "topk", "sparse_attend",
-    "dense_attend", "sparse_attend_prefill",
+    "dense_attend", "sparse_attend_prefill", "append_kv",
     "SelCache", "score_prefill", "select_prefill", "Workspace", "EXPORTS",
     "profile_enable", "profile_reset", "profile_read",
 ]
@@ -41,6 +41,7 @@ EXPORTS = [
     "ts_sparse_attend_workspace_size", "ts_sparse_attend",
     "ts_dense_attend_workspace_size", "ts_dense_attend",
     "ts_sparse_attend_prefill_workspace_size", "ts_sparse_attend_prefill",
+    "ts_append_kv",
     "ts_sel_cache_create", "ts_sel_cache_reset", "ts_sel_cache_destroy", "ts_sel_cache_stats",
     "ts_decode_step_workspace_size", "ts_decode_step",
     "ts_score_prefill_workspace_size", "ts_score_prefill", "ts_select_prefill",
@@ -95,6 +96,7 @@ def load():
         "ts_dense_attend": ([L, I32, P, P, P, P, P, P, P, SZ, P], I32),
         "ts_sparse_attend_prefill_workspace_size": ([L, I32, I32, SZP], I32),
         "ts_sparse_attend_prefill": ([L, I32, I32, P, P, P, I32, P, I32, P, P, SZ, P], I32),
+        "ts_append_kv": ([L, I32, P, P, P, P, P, P, P], I32),
         "ts_sel_cache_create": ([I32, I32, I32, I32, I32, ctypes.POINTER(P)], I32),
         "ts_sel_cache_reset": ([P, P], I32),
         "ts_sel_cache_destroy": ([P], I32),
@@ -365,6 +367,28 @@ def select_prefill(q, k_ctx, q_pos0: int, k: int, scale=None, votes=None, idx=No
                                  _ptr(votes), _ptr(idx), _ptr(w), w.numel(), _stream(stream)),
            "ts_select_prefill")
     return votes, idx
+
+
+def append_kv(k_new, v_new, k_cache, v_cache, seq_lens, page_table=None, stream=None):
+    """Write each sequence's new K/V row at position seq_lens[b]; seq_lens += 1 (on device)."""
+    lib = load()
+    _need_cuda(k_new, v_new, k_cache, v_cache, seq_lens, page_table)
+    if seq_lens.dtype != torch.int32:
+        raise TypeError("seq_lens must be int32")
+    B, Hkv, d = k_new.shape
+    if v_new.shape != k_new.shape or k_new.dtype != k_cache.dtype or v_cache.shape != k_cache.shape:
+        raise ValueError("new rows and caches disagree in shape or dtype")
+    if page_table is None:
+        max_len, ps, stride = k_cache.shape[1], 0, 0
+    else:
+        ps, stride = k_cache.shape[1], page_table.shape[1]
+        max_len = ps * stride
+    if k_cache.shape[2:] != (Hkv, d):
+        raise ValueError("new rows and caches disagree in heads or head_dim")
+    L = KvLayout(Hkv, Hkv, d, _dtype_code(k_new), 0.0, ps, max_len, stride)
+    _check(lib.ts_append_kv(ctypes.byref(L), B, _ptr(k_new), _ptr(v_new), _ptr(k_cache),
+                            _ptr(v_cache), _ptr(page_table), _ptr(seq_lens), _stream(stream)),
+           "ts_append_kv")
 
 
 def sparse_attend_prefill(q, k_ctx, v_ctx, q_pos0: int, idx, scale=None, out=None, ws=None,

@@ -552,6 +552,33 @@ ts_status ts_sparse_attend(const ts_kv_layout* L, int32_t batch, const void* q, 
   return ok();
 }
 
+// ---------------------------------------------------------------- ts_append_kv
+
+ts_status ts_append_kv(const ts_kv_layout* L, int32_t batch, const void* k_new, const void* v_new,
+                       void* k_cache, void* v_cache, const int32_t* page_table, int32_t* seq_lens,
+                       void* stream) {
+  Geo g;
+  TS_TRY(check_layout(L, batch, &g));
+  if (!k_new || !v_new || !k_cache || !v_cache || !seq_lens)
+    return fail(TS_ERR_INVALID_ARG, "NULL tensor pointer");
+  if (g.paged && !page_table) return fail(TS_ERR_INVALID_ARG, "paged layout needs a page_table");
+  AppendParams p{};
+  p.k_new = k_new;
+  p.v_new = v_new;
+  p.k_cache = k_cache;
+  p.v_cache = v_cache;
+  p.page_table = g.paged ? page_table : nullptr;
+  p.seq_lens = seq_lens;
+  p.row_elems = g.Hkv * g.d;
+  p.esz = g.dtype == TS_BF16 ? 2 : 4;
+  p.max_len = g.max_len;
+  p.ps_log2 = g.ps_log2;
+  p.pt_stride = g.pt_stride;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  TS_LAUNCH_K(kKFill, launch_append_kv(p, batch, st), "append K/V");
+  return ok();
+}
+
 // ------------------------------------------------ ts_sparse_attend_prefill
 
 namespace {

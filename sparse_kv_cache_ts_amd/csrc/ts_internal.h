@@ -160,6 +160,16 @@ struct CombineParams {
   int32_t* hit_out;         // [B] or null
 };
 
+struct AppendParams {
+  const void* k_new;        // [B][Hkv][d]
+  const void* v_new;
+  void* k_cache;            // contiguous [B][max_len][Hkv][d] or pool [P][ps][Hkv][d]
+  void* v_cache;
+  const int32_t* page_table;
+  int32_t* seq_lens;        // [B], advanced by one per appended token
+  int row_elems, esz, max_len, ps_log2, pt_stride;
+};
+
 struct PrefillParams {
   const void* q;            // [chunk][Hq][d] bf16
   const void* k;            // [n_ctx][Hkv][d] bf16
@@ -183,6 +193,7 @@ hipError_t launch_topk_partition(const TopkParams& p, int grid_x, hipStream_t s)
 hipError_t launch_topk_finalize(const TopkParams& p, hipStream_t s);
 hipError_t launch_attend(int dtype, int d, bool paged, const AttendParams& p, hipStream_t s);
 hipError_t launch_combine(const CombineParams& p, hipStream_t s);
+hipError_t launch_append_kv(const AppendParams& p, int batch, hipStream_t s);
 hipError_t launch_prefill_lse(const PrefillParams& p, hipStream_t s);
 hipError_t launch_prefill_merge(const PrefillParams& p, hipStream_t s);
 hipError_t launch_prefill_votes(const PrefillParams& p, hipStream_t s);

@@ -117,6 +117,13 @@ def test_null_and_workspace_errors_enqueue_nothing():
     st = lib.ts_sparse_attend(ctypes.byref(L), 1, fake, fake, None, None, fake, fake, 8, fake,
                               fake, 1 << 30, None)
     assert st == ts.TS_ERR_INVALID_ARG
+    # append: NULL new rows, paged layout without page table
+    st = lib.ts_append_kv(ctypes.byref(L), 1, None, fake, fake, fake, None, fake, None)
+    assert st == ts.TS_ERR_INVALID_ARG
+    st = lib.ts_append_kv(ctypes.byref(Lp), 1, fake, fake, fake, fake, None, fake, None)
+    assert st == ts.TS_ERR_INVALID_ARG
+    st = lib.ts_append_kv(ctypes.byref(L), 0, fake, fake, fake, fake, None, fake, None)
+    assert st == ts.TS_ERR_INVALID_ARG
     # decode step without a cache
     st = lib.ts_decode_step(None, ctypes.byref(L), 1, fake, fake, fake, None, fake, 0.9, fake,
                             None, None, fake, 1 << 30, None)

@@ -1,5 +1,6 @@
 """The seeded generators build the inputs they claim to (CPU only)."""
 import math
+from dataclasses import replace
 
 import numpy as np
 import torch
@@ -92,3 +93,26 @@ def test_prefill_rope_positions():
     # position 0 is the identity
     z = W.rope_rotate_half(raw[:1], torch.zeros(1), 10000.0)
     assert torch.allclose(z, raw[:1])
+
+
+def test_gen_loop_layout():
+    """The growing-cache loop: room for every step, pages mapped, zeros past each length."""
+    cfg = replace(W.LOOP_RUN, batch=3, min_len=40, max_len=90, steps=7, page_size=16)
+    for paged in (False, True):
+        x = W.gen_loop(cfg, paged)
+        y = W.gen_loop(cfg, paged)
+        assert torch.equal(x["k_cache"], y["k_cache"]) and torch.equal(x["queries"], y["queries"])
+        lens = x["seq_lens"].tolist()
+        assert x["cap"] == max(lens) + cfg.steps
+        assert x["k_new"].shape == (cfg.steps, cfg.batch, cfg.num_kv_heads, cfg.head_dim)
+        if not paged:
+            for b, n in enumerate(lens):
+                assert (x["k_cache"][b, n:] == 0).all() and (x["k_cache"][b, n - 1] != 0).any()
+            continue
+        pt = x["page_table"]
+        used = []
+        for b, n in enumerate(lens):
+            need = (n + cfg.steps + cfg.page_size - 1) // cfg.page_size
+            assert (pt[b, :need] >= 0).all() and (pt[b, need:] == -1).all()
+            used += pt[b, :need].tolist()
+        assert sorted(used) == list(range(x["k_cache"].shape[0]))

@@ -297,3 +297,59 @@ def gen_run(cfg: RunConfig, device="cpu", lens: Optional[list] = None) -> dict:
         "seq_lens": torch.tensor(lens, dtype=torch.int32, device=device),
         "special": special,
     }
+
+
+LOOP_RUN = RunConfig("decode-loop-3x24-append", steps=24, batch=3, num_q_heads=16,
+                     num_kv_heads=4, head_dim=128, min_len=900, max_len=5000, dtype="bf16",
+                     k=256, seed=6, jump_every=8)
+
+
+def gen_loop(cfg: RunConfig, paged: bool, device="cpu") -> dict:
+    """A decode loop that grows the cache by one token per step.
+
+    Initial lengths are uniform in [min_len, max_len]; the cache has room for
+    steps more tokens per sequence. Contiguous: k_cache/v_cache
+    [B][cap][Hkv][d] with cap = max(lens) + steps. Paged: a pool holding
+    ceil((len_b + steps) / page) pages per sequence in a random order, and
+    page_table [B][ceil(cap / page)] (unused entries -1). Keys, values and the
+    per-step new rows k_new/v_new [steps][B][Hkv][d] are N(0,1); queries come
+    from gen_query_process. Cache slots past each length hold zeros.
+    """
+    g = _gen(cfg.seed, device)
+    B, Hq, Hkv, d, P, T = (cfg.batch, cfg.num_q_heads, cfg.num_kv_heads, cfg.head_dim,
+                           cfg.page_size, cfg.steps)
+    dt = torch_dtype(cfg.dtype)
+    lens = torch.randint(cfg.min_len, cfg.max_len + 1, (B,), generator=g, device=device).tolist()
+    cap = max(lens) + T
+    k_new = torch.randn(T, B, Hkv, d, generator=g, device=device).to(dt)
+    v_new = torch.randn(T, B, Hkv, d, generator=g, device=device).to(dt)
+    queries = gen_query_process(T, B, Hq, d, cfg.seed + 1000, cfg.keep, cfg.noise,
+                                cfg.jump_every, device=device).to(dt)
+    out = {"queries": queries.contiguous(), "k_new": k_new, "v_new": v_new,
+           "seq_lens": torch.tensor(lens, dtype=torch.int32, device=device), "cap": cap}
+    if not paged:
+        kc = torch.zeros(B, cap, Hkv, d, dtype=dt, device=device)
+        vc = torch.zeros(B, cap, Hkv, d, dtype=dt, device=device)
+        for b in range(B):
+            kc[b, :lens[b]] = torch.randn(lens[b], Hkv, d, generator=g, device=device).to(dt)
+            vc[b, :lens[b]] = torch.randn(lens[b], Hkv, d, generator=g, device=device).to(dt)
+        out.update(k_cache=kc, v_cache=vc, page_table=None)
+        return out
+    pages = [(n + T + P - 1) // P for n in lens]
+    total = sum(pages)
+    perm = torch.randperm(total, generator=g, device=device).to(torch.int32)
+    page_table = torch.full((B, (cap + P - 1) // P), -1, dtype=torch.int32, device=device)
+    off = 0
+    for b in range(B):
+        page_table[b, :pages[b]] = perm[off:off + pages[b]]
+        off += pages[b]
+    kp = torch.zeros(total, P, Hkv, d, dtype=dt, device=device)
+    vp = torch.zeros(total, P, Hkv, d, dtype=dt, device=device)
+    for b in range(B):
+        n = lens[b]
+        pos = torch.arange(n, device=device)
+        pg = page_table[b, pos // P].long()
+        kp[pg, pos % P] = torch.randn(n, Hkv, d, generator=g, device=device).to(dt)
+        vp[pg, pos % P] = torch.randn(n, Hkv, d, generator=g, device=device).to(dt)
+    out.update(k_cache=kp, v_cache=vp, page_table=page_table)
+    return out
