@@ -216,6 +216,71 @@ def measure_decode(ts, W, cfg, steps, warmup, copies, theta, profile, tag):
     return res, x
 
 
+def measure_loop(ts, W, cfg, layers, tokens, warmup):
+    """The decode loop of a model with `layers` attention layers: per token and
+    layer, append the new K/V row, then one decode step (selection every step)
+    with that layer's own selection-cache state. Eager launches vs the same
+    token captured once as a HIP graph and replayed."""
+    import torch
+    x = W.gen_decode(cfg, device="cuda")
+    B, Hq, Hkv, d, N, k = (cfg.batch, cfg.num_q_heads, cfg.num_kv_heads, cfg.head_dim,
+                           cfg.seq_len, cfg.k)
+    cap = N + 2 * (warmup + tokens) + 8
+    dt = x["k_cache"].dtype
+    L = []
+    for _ in range(layers):
+        kc = torch.empty(B, cap, Hkv, d, dtype=dt, device="cuda")
+        vc = torch.empty(B, cap, Hkv, d, dtype=dt, device="cuda")
+        kc[:, :N] = x["k_cache"]
+        vc[:, :N] = x["v_cache"]
+        L.append({"k": kc, "v": vc, "lens": x["seq_lens"].clone(),
+                  "kn": torch.randn(B, Hkv, d, device="cuda").to(dt),
+                  "vn": torch.randn(B, Hkv, d, device="cuda").to(dt),
+                  "cache": ts.SelCache(B, Hq, d, k),
+                  "out": torch.empty(B, Hq, d, dtype=torch.float32, device="cuda"),
+                  "idx": torch.empty(B, k, dtype=torch.int32, device="cuda"),
+                  "hit": torch.empty(B, dtype=torch.int32, device="cuda")})
+    q = x["q"]
+    lay = ts.make_layout(q, L[0]["k"])
+    for l in L:
+        l["cache"].ws.get(l["cache"].workspace_size(lay, B), q.device)
+
+    def token():
+        for l in L:
+            ts.append_kv(l["kn"], l["vn"], l["k"], l["v"], l["lens"])
+            l["cache"].decode_step(q, l["k"], l["v"], l["lens"], 1.0, out=l["out"],
+                                   idx_out=l["idx"], hit_out=l["hit"])
+
+    def timed(fn, n):
+        for _ in range(warmup):
+            fn()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(n):
+            fn()
+        torch.cuda.synchronize()
+        return 1e3 * (time.perf_counter() - t0) / n
+
+    eager_ms = timed(token, tokens)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        token()
+    graph_ms = timed(graph.replay, tokens)
+    final = [int(l["lens"][0].item()) for l in L]
+    for l in L:
+        l["cache"].close()
+    del L, graph
+    torch.cuda.empty_cache()
+    return {"workload": f"{layers} layers x (append K/V + decode step), {cfg.name}, N={N} "
+                        f"growing by one per token, top-k {k}, selection every step",
+            "layers": layers, "tokens": tokens, "eager_ms_per_token": round(eager_ms, 4),
+            "graph_ms_per_token": round(graph_ms, 4),
+            "graph_tokens_per_s": round(1e3 / graph_ms, 2),
+            "graph_speedup": round(eager_ms / graph_ms, 3),
+            "us_per_layer_graph": round(1e3 * graph_ms / layers, 2),
+            "final_len": final[0]}
+
+
 def cpu_baseline(O, W, cfg, x, seconds):
     """The fp64 oracle (as written, untuned) on host copies of the same inputs."""
     import numpy as np
@@ -255,6 +320,8 @@ def main():
     ap.add_argument("--no-hit", action="store_true", help="skip the selection-reuse measurement")
     ap.add_argument("--no-prefill", action="store_true", help="skip the prefill-chunk measurement")
     ap.add_argument("--no-dense", action="store_true", help="skip the full-attention baseline")
+    ap.add_argument("--no-loop", action="store_true", help="skip the multi-layer decode loop")
+    ap.add_argument("--loop-layers", type=int, default=28)
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 512 MiB copy kernel (for HBM byte counters)")
     args = ap.parse_args()
@@ -322,6 +389,10 @@ def main():
             dense["sparse_attention_us"] = round(sparse_att, 2)
             dense["attention_speedup"] = round(dense["us_per_call"] / sparse_att, 2)
         extra["dense_attention"] = dense
+
+    if not args.no_loop:
+        extra["decode_loop"] = measure_loop(ts, W, cfg, args.loop_layers,
+                                            max(1, args.steps // 4), max(1, args.warmup // 4))
 
     cpu = None
     if not args.no_cpu_baseline:

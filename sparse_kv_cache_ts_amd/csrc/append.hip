@@ -41,7 +41,7 @@ __global__ __launch_bounds__(256) void append_kv_kernel(AppendParams p) {
 }
 
 hipError_t launch_append_kv(const AppendParams& p, int batch, hipStream_t s) {
-  hipLaunchKernelGGL(append_kv_kernel, dim3(batch), dim3(256), 0, s, p);
+  TS_KLAUNCH(append_kv_kernel, dim3(batch), dim3(256), 0, s, p);
   return hipGetLastError();
 }
 

@@ -367,7 +367,7 @@ template <int DT, int D, bool PAGED, bool DENSE>
 static hipError_t launch_attend_gs(const AttendParams& p, hipStream_t s) {
   dim3 grid(p.nsplit, p.Hkv * p.nslices, p.B);
   switch (p.GS) {
-#define TS_GS(n) case n: hipLaunchKernelGGL((attend_kernel<DT, D, n, PAGED, DENSE>), grid, dim3(256), 0, s, p); break;
+#define TS_GS(n) case n: TS_KLAUNCH((attend_kernel<DT, D, n, PAGED, DENSE>), grid, dim3(256), 0, s, p); break;
     TS_GS(1) TS_GS(2) TS_GS(3) TS_GS(4) TS_GS(5) TS_GS(6) TS_GS(7) TS_GS(8)
 #undef TS_GS
     default: return hipErrorInvalidValue;
@@ -390,7 +390,7 @@ hipError_t launch_attend(int dtype, int d, bool paged, const AttendParams& p, hi
 }
 
 hipError_t launch_combine(const CombineParams& p, hipStream_t s) {
-  hipLaunchKernelGGL(combine_kernel, dim3(p.Hq, p.B), dim3(128), 0, s, p);
+  TS_KLAUNCH(combine_kernel, dim3(p.Hq, p.B), dim3(128), 0, s, p);
   return hipGetLastError();
 }
 

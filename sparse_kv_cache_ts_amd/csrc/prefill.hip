@@ -375,7 +375,7 @@ static hipError_t launch_lse_g(const PrefillParams& p, hipStream_t s) {
   const int qb = 64 * kPrefillRT1 / p.G;
   dim3 grid(((p.chunk + qb - 1) / qb) * p.Hkv * p.nsplit1);
   switch (p.G) {
-    case 4: hipLaunchKernelGGL((prefill_lse_kernel<4, D>), grid, dim3(256), 0, s, p); break;
+    case 4: TS_KLAUNCH((prefill_lse_kernel<4, D>), grid, dim3(256), 0, s, p); break;
     // other group sizes are not built (rejected on the host)
     default: return hipErrorInvalidValue;
   }
@@ -389,7 +389,7 @@ hipError_t launch_prefill_lse(const PrefillParams& p, hipStream_t s) {
 }
 
 hipError_t launch_prefill_merge(const PrefillParams& p, hipStream_t s) {
-  hipLaunchKernelGGL(prefill_merge_kernel, dim3((p.chunk * p.Hq + 255) / 256), dim3(256), 0, s, p);
+  TS_KLAUNCH(prefill_merge_kernel, dim3((p.chunk * p.Hq + 255) / 256), dim3(256), 0, s, p);
   return hipGetLastError();
 }
 
@@ -399,7 +399,7 @@ static hipError_t launch_votes_g(const PrefillParams& p, hipStream_t s) {
   dim3 grid(((p.chunk + qb - 1) / qb) * p.nsplit2);
   dim3 block(64 * p.Hkv);
   switch (p.G) {
-    case 4: hipLaunchKernelGGL((prefill_votes_kernel<4, D>), grid, block, 0, s, p); break;
+    case 4: TS_KLAUNCH((prefill_votes_kernel<4, D>), grid, block, 0, s, p); break;
     // other group sizes are not built (rejected on the host)
     default: return hipErrorInvalidValue;
   }

@@ -461,7 +461,7 @@ static hipError_t launch_pass1_gs(const ScoreParams& p, hipStream_t s) {
   constexpr int LPR = score_lpr<DT, D>();
 #endif
   switch (p.GS) {
-#define TS_GS(n) case n: hipLaunchKernelGGL((score_pass1_kernel<DT, D, n, PAGED, TILE, LPR>), grid, dim3(256), shmem, s, p); break;
+#define TS_GS(n) case n: TS_KLAUNCH((score_pass1_kernel<DT, D, n, PAGED, TILE, LPR>), grid, dim3(256), shmem, s, p); break;
     TS_GS(1) TS_GS(2) TS_GS(3) TS_GS(4) TS_GS(5) TS_GS(6) TS_GS(7) TS_GS(8)
 #undef TS_GS
     default: return hipErrorInvalidValue;
@@ -485,12 +485,12 @@ hipError_t launch_score_pass1(int dtype, int d, bool paged, const ScoreParams& p
 }
 
 hipError_t launch_lse(const LseParams& p, hipStream_t s) {
-  hipLaunchKernelGGL(lse_kernel, dim3(p.Hq, p.B), dim3(64), 0, s, p);
+  TS_KLAUNCH(lse_kernel, dim3(p.Hq, p.B), dim3(64), 0, s, p);
   return hipGetLastError();
 }
 
 hipError_t launch_votes(const VoteParams& p, int grid_x, hipStream_t s) {
-  hipLaunchKernelGGL(votes_kernel, dim3(grid_x, p.B), dim3(256), 0, s, p);
+  TS_KLAUNCH(votes_kernel, dim3(grid_x, p.B), dim3(256), 0, s, p);
   return hipGetLastError();
 }
 

@@ -28,12 +28,12 @@ __global__ __launch_bounds__(256) void fill_zero_kernel(uint32_t* p, size_t n) {
 hipError_t launch_fill_zero(void* ptr, size_t words, hipStream_t s) {
   if (words == 0) return hipSuccess;
   const int grid = (int)((words + 255) / 256 < 1024 ? (words + 255) / 256 : 1024);
-  hipLaunchKernelGGL(fill_zero_kernel, dim3(grid), dim3(256), 0, s, (uint32_t*)ptr, words);
+  TS_KLAUNCH(fill_zero_kernel, dim3(grid), dim3(256), 0, s, (uint32_t*)ptr, words);
   return hipGetLastError();
 }
 
 hipError_t launch_prologue(const PrologueParams& p, int grid, hipStream_t s) {
-  hipLaunchKernelGGL(prologue_kernel, dim3(grid), dim3(256), 0, s, p);
+  TS_KLAUNCH(prologue_kernel, dim3(grid), dim3(256), 0, s, p);
   return hipGetLastError();
 }
 

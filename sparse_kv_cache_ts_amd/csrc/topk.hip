@@ -383,17 +383,17 @@ __global__ __launch_bounds__(kFinalThreads) void topk_finalize_kernel(TopkParams
 }
 
 hipError_t launch_topk_hist0(const TopkParams& p, int grid_x, hipStream_t s) {
-  hipLaunchKernelGGL(topk_hist0_kernel, dim3(grid_x, p.rows), dim3(256), 0, s, p);
+  TS_KLAUNCH(topk_hist0_kernel, dim3(grid_x, p.rows), dim3(256), 0, s, p);
   return hipGetLastError();
 }
 
 hipError_t launch_topk_partition(const TopkParams& p, int grid_x, hipStream_t s) {
-  hipLaunchKernelGGL(topk_partition_kernel, dim3(grid_x, p.rows), dim3(256), 0, s, p);
+  TS_KLAUNCH(topk_partition_kernel, dim3(grid_x, p.rows), dim3(256), 0, s, p);
   return hipGetLastError();
 }
 
 hipError_t launch_topk_finalize(const TopkParams& p, hipStream_t s) {
-  hipLaunchKernelGGL(topk_finalize_kernel, dim3(p.rows), dim3(kFinalThreads), 0, s, p);
+  TS_KLAUNCH(topk_finalize_kernel, dim3(p.rows), dim3(kFinalThreads), 0, s, p);
   return hipGetLastError();
 }
 

@@ -70,6 +70,17 @@ Prof& prof() {
   return *p;
 }
 
+}  // namespace
+
+namespace ts {
+LaunchTiming& launch_timing() {
+  static thread_local LaunchTiming t;
+  return t;
+}
+}  // namespace ts
+
+namespace {
+
 hipEvent_t prof_event() {
   Prof& P = prof();
   std::lock_guard<std::mutex> g(P.mu);
@@ -85,15 +96,24 @@ hipEvent_t prof_event() {
 
 template <class F>
 ts_status launch_timed(int kind, hipStream_t st, F&& f, const char* what) {
+  (void)st;
   Prof& P = prof();
   if (!P.on.load(std::memory_order_relaxed)) return hip_check(f(), what);
   hipEvent_t a = prof_event(), b = prof_event();
-  if (a) (void)hipEventRecord(a, st);
+  if (!a || !b) return hip_check(f(), what);
+  LaunchTiming& t = launch_timing();
+  t.start = a;
+  t.stop = b;
+  t.used = false;
   hipError_t e = f();
-  if (b) (void)hipEventRecord(b, st);
-  if (a && b) {
-    std::lock_guard<std::mutex> g(P.mu);
+  const bool used = t.used;
+  t = LaunchTiming{};
+  std::lock_guard<std::mutex> g(P.mu);
+  if (used && e == hipSuccess) {
     P.pending.push_back({kind, a, b});
+  } else {
+    P.pool.push_back(a);
+    P.pool.push_back(b);
   }
   return hip_check(e, what);
 }

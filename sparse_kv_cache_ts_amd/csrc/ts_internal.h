@@ -3,6 +3,7 @@
 #pragma once
 
 #include <hip/hip_runtime.h>
+#include <hip/hip_ext.h>
 #include <stddef.h>
 #include <stdint.h>
 
@@ -198,4 +199,29 @@ hipError_t launch_prefill_lse(const PrefillParams& p, hipStream_t s);
 hipError_t launch_prefill_merge(const PrefillParams& p, hipStream_t s);
 hipError_t launch_prefill_votes(const PrefillParams& p, hipStream_t s);
 
+// Kernel-level timing. While the library's profiler is on, the launcher sets
+// these events before each launch function runs; the kernel launches then
+// carry them in their dispatch packets (hipExtLaunchKernelGGL), so the
+// interval is the kernels' own execution, first start to last end, with no
+// marker packets around it. Thread-local; stop == nullptr means "not timing".
+struct LaunchTiming {
+  hipEvent_t start = nullptr, stop = nullptr;
+  bool used = false;
+};
+LaunchTiming& launch_timing();
+
 }  // namespace ts
+
+// Every kernel launch of the library goes through this macro.
+#define TS_KLAUNCH(kernel, grid, block, shmem, stream, ...)                                   \
+  do {                                                                                        \
+    ::ts::LaunchTiming& ts_lt_ = ::ts::launch_timing();                                       \
+    if (ts_lt_.stop) {                                                                        \
+      hipExtLaunchKernelGGL(kernel, grid, block, shmem, stream, ts_lt_.start, ts_lt_.stop, 0, \
+                            __VA_ARGS__);                                                     \
+      ts_lt_.start = nullptr;                                                                 \
+      ts_lt_.used = true;                                                                     \
+    } else {                                                                                  \
+      hipLaunchKernelGGL(kernel, grid, block, shmem, stream, __VA_ARGS__);                    \
+    }                                                                                         \
+  } while (0)

@@ -179,3 +179,49 @@ def test_decode_loop_graph_replay(gpu_lib, paged):
     h, m = cache.stats(B)
     assert h == e_hit.sum(0).tolist()
     cache.close()
+
+
+def test_decode_loop_layers_graph(gpu_lib):
+    """Three layers, each with its own cache, lengths and selection-cache state:
+    one graph holding every layer's append + decode step, replayed per token,
+    equals each layer run alone eagerly (state stays per layer)."""
+    ts = gpu_lib
+    cfgs = [replace(W.LOOP_RUN, seed=W.LOOP_RUN.seed + 10 * l, steps=10) for l in range(3)]
+    xs = [W.gen_loop(c, True, device="cuda") for c in cfgs]
+    alone = [_run_eager(ts, x, c, 0, c.theta) for x, c in zip(xs, cfgs)]
+    B, Hq, d, k = cfgs[0].batch, cfgs[0].num_q_heads, cfgs[0].head_dim, cfgs[0].k
+    lay = []
+    for x in xs:
+        st = {"k": x["k_cache"].clone(), "v": x["v_cache"].clone(), "lens": x["seq_lens"].clone(),
+              "pt": x["page_table"], "cache": ts.SelCache(B, Hq, d, k, mode=0),
+              "q": torch.empty_like(x["queries"][0]), "kn": torch.empty_like(x["k_new"][0]),
+              "vn": torch.empty_like(x["v_new"][0]),
+              "out": torch.empty(B, Hq, d, dtype=torch.float32, device="cuda"),
+              "idx": torch.empty(B, k, dtype=torch.int32, device="cuda"),
+              "hit": torch.empty(B, dtype=torch.int32, device="cuda")}
+        L = ts.make_layout(st["q"], st["k"], st["pt"])
+        st["cache"].ws.get(st["cache"].workspace_size(L, B), st["q"].device)
+        lay.append(st)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for st in lay:
+            ts.append_kv(st["kn"], st["vn"], st["k"], st["v"], st["lens"], page_table=st["pt"])
+            st["cache"].decode_step(st["q"], st["k"], st["v"], st["lens"], cfgs[0].theta,
+                                    page_table=st["pt"], out=st["out"], idx_out=st["idx"],
+                                    hit_out=st["hit"])
+    for t in range(cfgs[0].steps):
+        for st, x in zip(lay, xs):
+            st["q"].copy_(x["queries"][t])
+            st["kn"].copy_(x["k_new"][t])
+            st["vn"].copy_(x["v_new"][t])
+        graph.replay()
+        torch.cuda.synchronize()
+        for l, st in enumerate(lay):
+            e_out, e_idx, e_hit, _ = alone[l]
+            assert torch.equal(st["hit"], e_hit[t]), f"layer {l} step {t}"
+            assert torch.equal(st["idx"], e_idx[t]), f"layer {l} step {t}"
+            assert torch.equal(st["out"], e_out[t]), f"layer {l} step {t}"
+    for l, st in enumerate(lay):
+        assert torch.equal(st["lens"], alone[l][3])
+        st["cache"].close()
