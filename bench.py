@@ -281,6 +281,75 @@ def measure_loop(ts, W, cfg, layers, tokens, warmup):
             "final_len": final[0]}
 
 
+def measure_quest(ts, W, steps, warmup):
+    """Quest-style page selection on the paged selection-cache workload (8
+    sequences of 16K..256K tokens, 32/8 heads, page 16): per step the last
+    page's extremes, page scores + top-256 pages per KV head, and attention
+    over those pages. Next to it, one TokenSelect step with selection on the
+    same KV (theta = 1), for scale."""
+    import torch
+    cfg = W.SELCACHE_RUN
+    x = W.gen_run(cfg, device="cuda")
+    q, lens, pt = x["queries"][0], x["seq_lens"], x["page_table"]
+    kp, vp = x["k_pool"], x["v_pool"]
+    B, Hq, Hkv, d, P = cfg.batch, cfg.num_q_heads, cfg.num_kv_heads, cfg.head_dim, cfg.page_size
+    k_pages = cfg.k // P
+    meta = ts.quest_meta(kp, pt, lens)
+    pidx = torch.empty(B, Hkv, k_pages, dtype=torch.int32, device="cuda")
+    out = torch.empty(B, Hq, d, dtype=torch.float32, device="cuda")
+    ws_s, ws_a = ts.Workspace(), ts.Workspace()
+
+    def step():
+        ts.quest_meta(kp, pt, lens, meta=meta, last_page_only=True)
+        ts.quest_select(q, kp, meta, pt, lens, k_pages, page_idx=pidx, ws=ws_s)
+        ts.quest_attend(q, kp, vp, pt, lens, pidx, out=out, ws=ws_a)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        step()
+    torch.cuda.synchronize()
+    us = 1e6 * (time.perf_counter() - t0) / steps
+    ts.profile_reset()
+    ts.profile_enable(True)
+    for _ in range(steps):
+        step()
+    torch.cuda.synchronize()
+    ts.profile_enable(False)
+    kern = {n: round(1e3 * ms / c, 2) for n, (c, ms) in ts.profile_read().items() if c}
+    n_list = lens.tolist()
+    pages = [-(-n // P) for n in n_list]
+    esz = 2
+    meta_bytes = sum(pages) * Hkv * 2 * d * esz
+    gathered = sum(min(k_pages, pg) * P for pg in pages) * Hkv * d * esz * 2
+    kscan_bytes = sum(n_list) * Hkv * d * esz
+    # TokenSelect on the same KV, selection every step
+    cache = ts.SelCache(B, Hq, d, cfg.k)
+    o2 = torch.empty(B, Hq, d, dtype=torch.float32, device="cuda")
+    for _ in range(warmup):
+        cache.decode_step(q, kp, vp, lens, 1.0, page_table=pt, out=o2, want_idx=False)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        cache.decode_step(q, kp, vp, lens, 1.0, page_table=pt, out=o2, want_idx=False)
+    torch.cuda.synchronize()
+    ts_us = 1e6 * (time.perf_counter() - t0) / steps
+    cache.close()
+    t_score = kern.get("quest_score", float("nan"))
+    del x, kp, vp, meta
+    torch.cuda.empty_cache()
+    return {"workload": f"{cfg.name}: {B} paged sequences, {sum(n_list)} tokens, {Hq}/{Hkv} heads, "
+                        f"d={d}, bf16, page {P}, top-{k_pages} pages per KV head",
+            "us_per_step": round(us, 2), "kernels_us": kern,
+            "meta_bytes": meta_bytes, "gathered_kv_bytes": gathered,
+            "page_score_GBps": round(meta_bytes / (t_score * 1e-6) / 1e9, 1),
+            "page_score_hbm_frac": round(meta_bytes / (t_score * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4),
+            "tokenselect_selection_step_us": round(ts_us, 2),
+            "tokenselect_kscan_bytes": kscan_bytes}
+
+
 def cpu_baseline(O, W, cfg, x, seconds):
     """The fp64 oracle (as written, untuned) on host copies of the same inputs."""
     import numpy as np
@@ -322,6 +391,7 @@ def main():
     ap.add_argument("--no-dense", action="store_true", help="skip the full-attention baseline")
     ap.add_argument("--no-loop", action="store_true", help="skip the multi-layer decode loop")
     ap.add_argument("--loop-layers", type=int, default=28)
+    ap.add_argument("--no-quest", action="store_true", help="skip the page-selection variant")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 512 MiB copy kernel (for HBM byte counters)")
     args = ap.parse_args()
@@ -393,6 +463,9 @@ def main():
     if not args.no_loop:
         extra["decode_loop"] = measure_loop(ts, W, cfg, args.loop_layers,
                                             max(1, args.steps // 4), max(1, args.warmup // 4))
+
+    if not args.no_quest:
+        extra["quest_pages"] = measure_quest(ts, W, max(1, args.steps // 4), max(1, args.warmup // 4))
 
     cpu = None
     if not args.no_cpu_baseline:

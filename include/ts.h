@@ -139,6 +139,56 @@ ts_status ts_append_kv(const ts_kv_layout* layout /*[host]*/, int32_t batch, con
                        const int32_t* page_table, int32_t* seq_lens, void* stream);
 
 /* ---------------------------------------------------------------------------
+ * Quest-style page selection, an alternative selector on paged KV ("Quest:
+ * Query-Aware Sparsity for Efficient Long-Context LLM Inference", arXiv
+ * 2406.10774: abstract and "Method Overview" point 4). Each KV page keeps the
+ * channel-wise min and max of its keys; a page's score for query head h is
+ * scale * sum_c max(q_hc * min_c, q_hc * max_c), an upper bound of its logits;
+ * a KV head scores a page by the largest bound over its group's query heads
+ * and keeps its own top k_pages pages; attention then runs per KV head over
+ * the tokens of its pages.
+ * Paged layouts only; G = Hq/Hkv <= 8 and Hkv <= 16 * 128 / d, otherwise
+ * TS_ERR_UNSUPPORTED.
+ *
+ * ts_quest_meta — per-page key extremes.
+ *   meta [P][Hkv][2][d] in the cache dtype, indexed by pool page: row 0 the
+ *        channel minima, row 1 the maxima, over the page's existing tokens
+ *        (< seq_lens[b]); exact (min/max of stored values).
+ *   last_page_only = 0: every page of every sequence; != 0: only the page
+ *        holding token seq_lens[b]-1 (call after ts_append_kv).
+ *   Pages outside a sequence and unmapped (negative) entries are left alone.
+ * ------------------------------------------------------------------------- */
+ts_status ts_quest_meta(const ts_kv_layout* layout /*[host]*/, int32_t batch, const void* k_cache,
+                        const int32_t* page_table, const int32_t* seq_lens,
+                        int32_t last_page_only, void* meta, void* stream);
+
+/* ts_quest_select — page scores, then the top k_pages pages per (sequence, KV head).
+ *   scores   optional out [batch][Hkv][n_pages] fp32, n_pages = ceil(max_len /
+ *            page_size); entries past a sequence's pages are unspecified.
+ *            NULL keeps them in the workspace.
+ *   page_idx [batch][Hkv][k_pages] int32 out: logical page numbers, ascending,
+ *            the min(k_pages, pages of b) best (ties to the lower page), -1 padded.
+ * ------------------------------------------------------------------------- */
+ts_status ts_quest_select_workspace_size(const ts_kv_layout* layout /*[host]*/, int32_t batch,
+                                         int32_t k_pages, size_t* bytes /*[host] out*/);
+ts_status ts_quest_select(const ts_kv_layout* layout /*[host]*/, int32_t batch, const void* q,
+                          const void* meta, const int32_t* page_table, const int32_t* seq_lens,
+                          int32_t k_pages, float* scores, int32_t* page_idx, void* ws,
+                          size_t ws_bytes, void* stream);
+
+/* ts_quest_attend — every query head attends over the existing tokens of its
+ * KV head's pages (softmax renormalised over them); negative page entries are
+ * skipped; a head with no token gets zeros.
+ *   page_idx [batch][Hkv][k_pages] as from ts_quest_select; out [batch][Hq][d] fp32.
+ * ------------------------------------------------------------------------- */
+ts_status ts_quest_attend_workspace_size(const ts_kv_layout* layout /*[host]*/, int32_t batch,
+                                         int32_t k_pages, size_t* bytes /*[host] out*/);
+ts_status ts_quest_attend(const ts_kv_layout* layout /*[host]*/, int32_t batch, const void* q,
+                          const void* k_cache, const void* v_cache, const int32_t* page_table,
+                          const int32_t* seq_lens, const int32_t* page_idx, int32_t k_pages,
+                          float* out, void* ws, size_t ws_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------
  * ts_sparse_attend_prefill — step 4 for a prefill chunk: query i (position
  * q_pos0 + i) attends, with every head, over the rows its own selection names
  * (TokenSelect README, "Key Takeaways": attention over the selected tokens).

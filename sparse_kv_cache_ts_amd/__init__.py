@@ -22,7 +22,8 @@ import torch
 
 __all__ = [
     "load", "lib_path", "TsError", "KvLayout", "make_layout", "score", "topk", "sparse_attend",
-    "dense_attend", "sparse_attend_prefill", "append_kv",
+    "dense_attend", "sparse_attend_prefill", "append_kv", "quest_meta", "quest_select",
+    "quest_attend",
     "SelCache", "score_prefill", "select_prefill", "Workspace", "EXPORTS",
     "profile_enable", "profile_reset", "profile_read",
 ]
@@ -42,6 +43,8 @@ EXPORTS = [
     "ts_dense_attend_workspace_size", "ts_dense_attend",
     "ts_sparse_attend_prefill_workspace_size", "ts_sparse_attend_prefill",
     "ts_append_kv",
+    "ts_quest_meta", "ts_quest_select_workspace_size", "ts_quest_select",
+    "ts_quest_attend_workspace_size", "ts_quest_attend",
     "ts_sel_cache_create", "ts_sel_cache_reset", "ts_sel_cache_destroy", "ts_sel_cache_stats",
     "ts_decode_step_workspace_size", "ts_decode_step",
     "ts_score_prefill_workspace_size", "ts_score_prefill", "ts_select_prefill",
@@ -97,6 +100,11 @@ def load():
         "ts_sparse_attend_prefill_workspace_size": ([L, I32, I32, SZP], I32),
         "ts_sparse_attend_prefill": ([L, I32, I32, P, P, P, I32, P, I32, P, P, SZ, P], I32),
         "ts_append_kv": ([L, I32, P, P, P, P, P, P, P], I32),
+        "ts_quest_meta": ([L, I32, P, P, P, I32, P, P], I32),
+        "ts_quest_select_workspace_size": ([L, I32, I32, SZP], I32),
+        "ts_quest_select": ([L, I32, P, P, P, P, I32, P, P, P, SZ, P], I32),
+        "ts_quest_attend_workspace_size": ([L, I32, I32, SZP], I32),
+        "ts_quest_attend": ([L, I32, P, P, P, P, P, P, I32, P, P, SZ, P], I32),
         "ts_sel_cache_create": ([I32, I32, I32, I32, I32, ctypes.POINTER(P)], I32),
         "ts_sel_cache_reset": ([P, P], I32),
         "ts_sel_cache_destroy": ([P], I32),
@@ -412,6 +420,68 @@ def sparse_attend_prefill(q, k_ctx, v_ctx, q_pos0: int, idx, scale=None, out=Non
     _check(lib.ts_sparse_attend_prefill(ctypes.byref(L), C, q_pos0, _ptr(q), _ptr(k_ctx), _ptr(v_ctx),
                                         n_ctx, _ptr(idx), k, _ptr(out), _ptr(w), w.numel(),
                                         _stream(stream)), "ts_sparse_attend_prefill")
+    return out
+
+
+def quest_meta(k_cache, page_table, seq_lens, meta=None, last_page_only=False, stream=None):
+    """Per-page channel min/max keys: meta [P][Hkv][2][d] in the cache dtype (pool-page indexed)."""
+    lib = load()
+    _need_cuda(k_cache, page_table, seq_lens, meta)
+    P_, ps, Hkv, d = k_cache.shape
+    if meta is None:
+        meta = torch.zeros(P_, Hkv, 2, d, dtype=k_cache.dtype, device=k_cache.device)
+    if meta.shape != (P_, Hkv, 2, d) or meta.dtype != k_cache.dtype:
+        raise ValueError("meta must be [pages][Hkv][2][d] in the cache dtype")
+    L = KvLayout(Hkv, Hkv, d, _dtype_code(k_cache), 0.0, ps, ps * page_table.shape[1],
+                 page_table.shape[1])
+    _check(lib.ts_quest_meta(ctypes.byref(L), page_table.shape[0], _ptr(k_cache), _ptr(page_table),
+                             _ptr(seq_lens), 1 if last_page_only else 0, _ptr(meta),
+                             _stream(stream)), "ts_quest_meta")
+    return meta
+
+
+def quest_select(q, k_cache, meta, page_table, seq_lens, k_pages: int, scale=None, scores=None,
+                 page_idx=None, want_scores=False, ws=None, stream=None):
+    """Top k_pages pages per (sequence, KV head): (page_idx [B][Hkv][k_pages], scores or None)."""
+    lib = load()
+    _need_cuda(q, k_cache, meta, page_table, seq_lens, scores, page_idx)
+    L = make_layout(q, k_cache, page_table, scale)
+    B = q.shape[0]
+    Hkv = k_cache.shape[2]
+    n_pages = -(-L.max_len // L.page_size)
+    if page_idx is None:
+        page_idx = torch.empty(B, Hkv, k_pages, dtype=torch.int32, device=q.device)
+    if scores is None and want_scores:
+        scores = torch.empty(B, Hkv, n_pages, dtype=torch.float32, device=q.device)
+    n = ctypes.c_size_t()
+    _check(lib.ts_quest_select_workspace_size(ctypes.byref(L), B, k_pages, ctypes.byref(n)),
+           "ts_quest_select_workspace_size")
+    w = _ws(n.value, q.device, ws)
+    _check(lib.ts_quest_select(ctypes.byref(L), B, _ptr(q), _ptr(meta), _ptr(page_table),
+                               _ptr(seq_lens), k_pages, _ptr(scores), _ptr(page_idx), _ptr(w),
+                               w.numel(), _stream(stream)), "ts_quest_select")
+    return page_idx, scores
+
+
+def quest_attend(q, k_cache, v_cache, page_table, seq_lens, page_idx, scale=None, out=None,
+                 ws=None, stream=None):
+    """Each query head over the tokens of its KV head's pages: [B][Hq][d] fp32."""
+    lib = load()
+    _need_cuda(q, k_cache, v_cache, page_table, seq_lens, page_idx)
+    if page_idx.dtype != torch.int32:
+        raise TypeError("page_idx must be int32")
+    L = make_layout(q, k_cache, page_table, scale)
+    B, Hq, d = q.shape
+    k_pages = page_idx.shape[2]
+    if out is None:
+        out = torch.empty(B, Hq, d, dtype=torch.float32, device=q.device)
+    n = ctypes.c_size_t()
+    _check(lib.ts_quest_attend_workspace_size(ctypes.byref(L), B, k_pages, ctypes.byref(n)),
+           "ts_quest_attend_workspace_size")
+    w = _ws(n.value, q.device, ws)
+    _check(lib.ts_quest_attend(ctypes.byref(L), B, _ptr(q), _ptr(k_cache), _ptr(v_cache),
+                               _ptr(page_table), _ptr(seq_lens), _ptr(page_idx), k_pages, _ptr(out),
+                               _ptr(w), w.numel(), _stream(stream)), "ts_quest_attend")
     return out
 
 

@@ -45,7 +45,8 @@ __global__ __launch_bounds__(256) void attend_kernel(AttendParams p) {
   const int bkv = p.kv_shared ? 0 : b;
   const int pbeg = split * p.split;
   const int pend = min(pbeg + p.split, p.nidx);
-  const int32_t* idx = DENSE ? nullptr : p.idx + (size_t)b * p.nidx;
+  const int32_t* idx =
+      DENSE ? nullptr : p.idx + (size_t)b * p.idx_b_stride + (size_t)kvh * p.idx_kv_stride;
   const int Hkv = p.Hkv;
 
   auto row_of = [&](int t) -> size_t {
@@ -124,15 +125,23 @@ __global__ __launch_bounds__(256) void attend_kernel(AttendParams p) {
     }
   };
 
+  // token at list position pos (-1: none, or outside the sequence)
+  auto tok_at = [&](int pos) -> int {
+    if (pos >= pend) return -1;
+    long long t;
+    if (p.sel_page_log2 > 0) {
+      const int pg = idx[pos >> p.sel_page_log2];
+      t = pg < 0 ? -1 : ((long long)pg << p.sel_page_log2) + (pos & ((1 << p.sel_page_log2) - 1));
+    } else {
+      t = idx[pos];
+    }
+    return (t >= 0 && t < len) ? (int)t : -1;
+  };
   // indices of the first batch (sparse) together with the query slice
   int tok[UA];
   if constexpr (!DENSE) {
 #pragma unroll
-    for (int u = 0; u < UA; ++u) {
-      const int pos = pbeg + rg + u * RG;
-      const int t = pos < pend ? idx[pos] : -1;
-      tok[u] = (t >= 0 && t < len) ? t : -1;
-    }
+    for (int u = 0; u < UA; ++u) tok[u] = tok_at(pbeg + rg + u * RG);
   }
 #pragma unroll
   for (int hh = 0; hh < GS; ++hh) {
@@ -200,11 +209,7 @@ __global__ __launch_bounds__(256) void attend_kernel(AttendParams p) {
     for (int pos0 = pbeg + rg; pos0 < pend; pos0 += RG * UA) {
       if (pos0 != pbeg + rg) {
 #pragma unroll
-        for (int u = 0; u < UA; ++u) {
-          const int pos = pos0 + u * RG;
-          const int t = pos < pend ? idx[pos] : -1;
-          tok[u] = (t >= 0 && t < len) ? t : -1;
-        }
+        for (int u = 0; u < UA; ++u) tok[u] = tok_at(pos0 + u * RG);
       }
       uint32_t kw[UA][W], vw[UA][W];
       load_rows(tok, kw, vw);

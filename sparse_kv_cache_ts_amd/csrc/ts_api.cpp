@@ -49,11 +49,12 @@ ts_status hip_check(hipError_t e, const char* what) {
 // ---- kernel-level timing (ts_profile_*) ---------------------------------------
 enum KernelKind {
   kKPrologue, kKScore, kKLse, kKVotes, kKTopkHist, kKTopkPartition, kKTopkFinalize, kKAttend,
-  kKCombine, kKPrefillLse, kKPrefillVotes, kKFill, kKNum
+  kKCombine, kKPrefillLse, kKPrefillVotes, kKFill, kKAppend, kKQuestMeta, kKQuestScore, kKNum
 };
 const char* const kKernelNames[kKNum] = {
   "prologue", "score_pass1", "lse", "votes", "topk_hist", "topk_partition", "topk_finalize",
-  "attend", "combine", "prefill_lse", "prefill_votes", "fill_zero"
+  "attend", "combine", "prefill_lse", "prefill_votes", "fill_zero", "append_kv", "quest_meta",
+  "quest_score"
 };
 
 struct Prof {
@@ -384,6 +385,9 @@ AttendParams attend_params(const Geo& g, const AttendPlan& a, int B, void* ws, c
   p.page_table = pt;
   p.seq_lens = lens;
   p.idx = idx;
+  p.idx_b_stride = k;
+  p.idx_kv_stride = 0;
+  p.sel_page_log2 = 0;
   p.pm = at<float>(ws, a.pm);
   p.pl = at<float>(ws, a.pl);
   p.pacc = at<float>(ws, a.pacc);
@@ -595,7 +599,143 @@ ts_status ts_append_kv(const ts_kv_layout* L, int32_t batch, const void* k_new, 
   p.ps_log2 = g.ps_log2;
   p.pt_stride = g.pt_stride;
   hipStream_t st = static_cast<hipStream_t>(stream);
-  TS_LAUNCH_K(kKFill, launch_append_kv(p, batch, st), "append K/V");
+  TS_LAUNCH_K(kKAppend, launch_append_kv(p, batch, st), "append K/V");
+  return ok();
+}
+
+// ------------------------------------------------------- Quest page selection
+
+static ts_status quest_geo(const ts_kv_layout* L, int batch, Geo* g) {
+  TS_TRY(check_layout(L, batch, g));
+  if (!g->paged) return fail(TS_ERR_UNSUPPORTED, "page selection needs a paged KV layout");
+  if (g->G > 8) return fail(TS_ERR_UNSUPPORTED, "page scoring supports up to 8 query heads per KV head");
+  if (g->Hkv > 256 / (g->d / 16))
+    return fail(TS_ERR_UNSUPPORTED, "page scoring supports up to %d KV heads at d=%d",
+                256 / (g->d / 16), g->d);
+  return TS_OK;
+}
+
+struct QuestPlan {
+  int n_pages;
+  size_t scores, row_lens, total;
+  TopkPlan t;
+};
+static void plan_quest(const Geo& g, int B, QuestPlan& q) {
+  Carve c;
+  q.n_pages = cdiv(g.max_len, g.ps);
+  q.scores = c.take((size_t)B * g.Hkv * q.n_pages * 4);
+  q.row_lens = c.take((size_t)B * g.Hkv * 4);
+  plan_topk(B * g.Hkv, q.n_pages, c, q.t, true);
+  q.total = c.off;
+}
+
+ts_status ts_quest_meta(const ts_kv_layout* L, int32_t batch, const void* k_cache,
+                        const int32_t* page_table, const int32_t* seq_lens, int32_t last_page_only,
+                        void* meta, void* stream) {
+  Geo g;
+  TS_TRY(quest_geo(L, batch, &g));
+  if (!k_cache || !page_table || !seq_lens || !meta)
+    return fail(TS_ERR_INVALID_ARG, "NULL tensor pointer");
+  QuestMetaParams p{};
+  p.k = k_cache;
+  p.page_table = page_table;
+  p.seq_lens = seq_lens;
+  p.meta = meta;
+  p.Hkv = g.Hkv;
+  p.d = g.d;
+  p.esz = g.dtype == TS_BF16 ? 2 : 4;
+  p.ps_log2 = g.ps_log2;
+  p.pt_stride = g.pt_stride;
+  p.last_only = last_page_only ? 1 : 0;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  TS_LAUNCH_K(kKQuestMeta, launch_quest_meta(p, cdiv(g.max_len, g.ps), batch, st), "page extremes");
+  return ok();
+}
+
+ts_status ts_quest_select_workspace_size(const ts_kv_layout* L, int32_t batch, int32_t k_pages,
+                                         size_t* bytes) {
+  Geo g;
+  TS_TRY(quest_geo(L, batch, &g));
+  if (k_pages < 1) return fail(TS_ERR_INVALID_ARG, "k_pages must be >= 1");
+  if (!bytes) return fail(TS_ERR_INVALID_ARG, "bytes is NULL");
+  QuestPlan q;
+  plan_quest(g, batch, q);
+  *bytes = q.total;
+  return ok();
+}
+
+ts_status ts_quest_select(const ts_kv_layout* L, int32_t batch, const void* q, const void* meta,
+                          const int32_t* page_table, const int32_t* seq_lens, int32_t k_pages,
+                          float* scores, int32_t* page_idx, void* ws, size_t ws_bytes,
+                          void* stream) {
+  Geo g;
+  TS_TRY(quest_geo(L, batch, &g));
+  if (k_pages < 1) return fail(TS_ERR_INVALID_ARG, "k_pages must be >= 1");
+  if (!q || !meta || !page_table || !seq_lens || !page_idx)
+    return fail(TS_ERR_INVALID_ARG, "NULL tensor pointer");
+  QuestPlan P;
+  plan_quest(g, batch, P);
+  TS_TRY(check_ws(ws, ws_bytes, P.total));
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  QuestScoreParams sp{};
+  sp.q = q;
+  sp.meta = meta;
+  sp.page_table = page_table;
+  sp.seq_lens = seq_lens;
+  sp.scores = scores ? scores : at<float>(ws, P.scores);
+  sp.row_lens = at<int32_t>(ws, P.row_lens);
+  sp.B = batch;
+  sp.Hq = g.Hq;
+  sp.Hkv = g.Hkv;
+  sp.G = g.G;
+  sp.ps_log2 = g.ps_log2;
+  sp.pt_stride = g.pt_stride;
+  sp.row_stride = P.n_pages;
+  sp.scale = g.scale;
+  TS_LAUNCH_K(kKQuestScore, launch_quest_score(g.dtype, g.d, sp, st), "page scores");
+  TS_TRY(run_topk(batch * g.Hkv, P.n_pages, sp.scores, sp.row_lens, 0, k_pages, page_idx, ws, P.t,
+                  P.n_pages, st));
+  return ok();
+}
+
+ts_status ts_quest_attend_workspace_size(const ts_kv_layout* L, int32_t batch, int32_t k_pages,
+                                         size_t* bytes) {
+  Geo g;
+  TS_TRY(quest_geo(L, batch, &g));
+  if (k_pages < 1) return fail(TS_ERR_INVALID_ARG, "k_pages must be >= 1");
+  if (!bytes) return fail(TS_ERR_INVALID_ARG, "bytes is NULL");
+  if ((long)k_pages * g.ps > (1l << 30)) return fail(TS_ERR_UNSUPPORTED, "k_pages * page_size too large");
+  Carve c;
+  AttendPlan a;
+  plan_attend(g, batch, k_pages * g.ps, c, a);
+  *bytes = c.off;
+  return ok();
+}
+
+ts_status ts_quest_attend(const ts_kv_layout* L, int32_t batch, const void* q, const void* k_cache,
+                          const void* v_cache, const int32_t* page_table, const int32_t* seq_lens,
+                          const int32_t* page_idx, int32_t k_pages, float* out, void* ws,
+                          size_t ws_bytes, void* stream) {
+  Geo g;
+  TS_TRY(quest_geo(L, batch, &g));
+  if (k_pages < 1) return fail(TS_ERR_INVALID_ARG, "k_pages must be >= 1");
+  if ((long)k_pages * g.ps > (1l << 30)) return fail(TS_ERR_UNSUPPORTED, "k_pages * page_size too large");
+  if (!q || !k_cache || !v_cache || !page_table || !seq_lens || !page_idx || !out)
+    return fail(TS_ERR_INVALID_ARG, "NULL tensor pointer");
+  const int nslots = k_pages * g.ps;
+  Carve c;
+  AttendPlan a;
+  plan_attend(g, batch, nslots, c, a);
+  TS_TRY(check_ws(ws, ws_bytes, c.off));
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  AttendParams ap = attend_params(g, a, batch, ws, q, k_cache, v_cache, page_table, seq_lens,
+                                  page_idx, nslots);
+  ap.idx_b_stride = g.Hkv * k_pages;
+  ap.idx_kv_stride = k_pages;
+  ap.sel_page_log2 = g.ps_log2;
+  TS_LAUNCH_K(kKAttend, launch_attend(g.dtype, g.d, true, ap, st), "page attention");
+  CombineParams cp = combine_params(g, a, batch, ws, out);
+  TS_LAUNCH_K(kKCombine, launch_combine(cp, st), "combine");
   return ok();
 }
 

@@ -136,6 +136,11 @@ struct AttendParams {
   const int32_t* page_table;
   const int32_t* seq_lens;
   const int32_t* idx;       // [B][nidx], or null: position j is token j (dense attention)
+  // where sequence b's list starts (idx_b_stride) and how far apart the lists
+  // of its KV heads are (idx_kv_stride, 0: one list shared by every head);
+  // sel_page_log2 > 0: the list holds logical pages of 2^sel_page_log2
+  // tokens, and position j is token j % 2^s of page list[j >> s]
+  int idx_b_stride, idx_kv_stride, sel_page_log2;
   float* pm;                // [B][Hq][nsplit] running max (base 2)
   float* pl;                // [B][Hq][nsplit] sum of exp2
   float* pacc;              // [B][Hq][nsplit][d] weighted value sums
@@ -159,6 +164,25 @@ struct CombineParams {
   const int32_t* seq_lens;
   int32_t* idx_out;         // [B][k] or null
   int32_t* hit_out;         // [B] or null
+};
+
+struct QuestMetaParams {
+  const void* k;            // pool [P][ps][Hkv][d]
+  const int32_t* page_table;
+  const int32_t* seq_lens;
+  void* meta;               // [P][Hkv][2][d], cache dtype: channel min, then max
+  int Hkv, d, esz, ps_log2, pt_stride, last_only;
+};
+
+struct QuestScoreParams {
+  const void* q;            // [B][Hq][d]
+  const void* meta;
+  const int32_t* page_table;
+  const int32_t* seq_lens;
+  float* scores;            // [B][Hkv][row_stride]
+  int32_t* row_lens;        // [B*Hkv] pages of each row
+  int B, Hq, Hkv, G, ps_log2, pt_stride, row_stride;
+  float scale;
 };
 
 struct AppendParams {
@@ -194,6 +218,8 @@ hipError_t launch_topk_partition(const TopkParams& p, int grid_x, hipStream_t s)
 hipError_t launch_topk_finalize(const TopkParams& p, hipStream_t s);
 hipError_t launch_attend(int dtype, int d, bool paged, const AttendParams& p, hipStream_t s);
 hipError_t launch_combine(const CombineParams& p, hipStream_t s);
+hipError_t launch_quest_meta(const QuestMetaParams& p, int pages, int batch, hipStream_t s);
+hipError_t launch_quest_score(int dtype, int d, const QuestScoreParams& p, hipStream_t s);
 hipError_t launch_append_kv(const AppendParams& p, int batch, hipStream_t s);
 hipError_t launch_prefill_lse(const PrefillParams& p, hipStream_t s);
 hipError_t launch_prefill_merge(const PrefillParams& p, hipStream_t s);

@@ -124,6 +124,25 @@ def test_null_and_workspace_errors_enqueue_nothing():
     assert st == ts.TS_ERR_INVALID_ARG
     st = lib.ts_append_kv(ctypes.byref(L), 0, fake, fake, fake, fake, None, fake, None)
     assert st == ts.TS_ERR_INVALID_ARG
+    # page selection: contiguous layout, more than 8 query heads per KV head, NULLs, k_pages
+    n = ctypes.c_size_t()
+    assert lib.ts_quest_select_workspace_size(ctypes.byref(L), 1, 16, ctypes.byref(n)) == \
+        ts.TS_ERR_UNSUPPORTED
+    Lg = _layout(Hq=36, Hkv=4, ps=16, stride=64)
+    assert lib.ts_quest_select_workspace_size(ctypes.byref(Lg), 1, 16, ctypes.byref(n)) == \
+        ts.TS_ERR_UNSUPPORTED
+    assert lib.ts_quest_select_workspace_size(ctypes.byref(Lp), 1, 0, ctypes.byref(n)) == \
+        ts.TS_ERR_INVALID_ARG
+    assert lib.ts_quest_select_workspace_size(ctypes.byref(Lp), 2, 16, ctypes.byref(n)) == ts.TS_OK
+    assert n.value > 0
+    st = lib.ts_quest_meta(ctypes.byref(Lp), 1, fake, None, fake, 0, fake, None)
+    assert st == ts.TS_ERR_INVALID_ARG
+    st = lib.ts_quest_select(ctypes.byref(Lp), 1, fake, fake, fake, fake, 16, None, None, fake,
+                             1 << 30, None)
+    assert st == ts.TS_ERR_INVALID_ARG
+    st = lib.ts_quest_attend(ctypes.byref(Lp), 1, fake, fake, fake, fake, fake, fake, 16, fake,
+                             fake, 16, None)
+    assert st == ts.TS_ERR_WORKSPACE
     # decode step without a cache
     st = lib.ts_decode_step(None, ctypes.byref(L), 1, fake, fake, fake, None, fake, 0.9, fake,
                             None, None, fake, 1 << 30, None)
