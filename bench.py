@@ -336,6 +336,16 @@ def measure_quest(ts, W, steps, warmup):
         cache.decode_step(q, kp, vp, lens, 1.0, page_table=pt, out=o2, want_idx=False)
     torch.cuda.synchronize()
     ts_us = 1e6 * (time.perf_counter() - t0) / steps
+    # the same query again at theta = 0.9: every step after the first reuses the selection
+    for _ in range(warmup):
+        cache.decode_step(q, kp, vp, lens, 0.9, page_table=pt, out=o2, want_idx=False)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        cache.decode_step(q, kp, vp, lens, 0.9, page_table=pt, out=o2, want_idx=False)
+    torch.cuda.synchronize()
+    ts_hit_us = 1e6 * (time.perf_counter() - t0) / steps
+    hits, _ = cache.stats(B)
     cache.close()
     t_score = kern.get("quest_score", float("nan"))
     del x, kp, vp, meta
@@ -347,6 +357,8 @@ def measure_quest(ts, W, steps, warmup):
             "page_score_GBps": round(meta_bytes / (t_score * 1e-6) / 1e9, 1),
             "page_score_hbm_frac": round(meta_bytes / (t_score * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4),
             "tokenselect_selection_step_us": round(ts_us, 2),
+            "tokenselect_hit_step_us": round(ts_hit_us, 2),
+            "tokenselect_hits": hits,
             "tokenselect_kscan_bytes": kscan_bytes}
 
 
