@@ -102,7 +102,8 @@ ts_status ts_score(const ts_kv_layout* layout /*[host]*/, int32_t batch, const v
  *   row_lens [rows] int32 (device), 0 <= row_lens[r] <= row_stride
  *   idx      [rows][k] int32 out: the min(k, row_lens[r]) largest entries, ties to the
  *            lower index, ascending, then -1 padding. Exact (a radix select on the
- *            order-preserving integer image of the floats; -0.0 equals +0.0).
+ *            order-preserving integer image of the floats; -0.0 equals +0.0;
+ *            subnormals are ordered; rows must not hold NaN).
  *   k >= 1.
  * ------------------------------------------------------------------------- */
 ts_status ts_topk_workspace_size(int32_t rows, int32_t row_stride, int32_t k,

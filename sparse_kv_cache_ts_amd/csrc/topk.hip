@@ -27,6 +27,28 @@ __device__ __forceinline__ int row_length(const TopkParams& p, int r) {
   return p.row_lens ? p.row_lens[r] : p.row_len_base + r;
 }
 
+// The smallest float whose key is >= t: float_key is a monotone bijection on
+// the non-NaN floats (with -0 == +0), so "key(v) >= t" is "v >= bound(t)".
+// Keys below 0x800000 belong to -inf and negative NaNs (bound -inf); a bound
+// among the positive NaNs compares false with everything. Rows hold no NaN.
+__device__ __forceinline__ float key_bound(uint32_t t) {
+  if (t < 0x800000u) return -INFINITY;
+  return __uint_as_float((t & 0x80000000u) ? (t & 0x7FFFFFFFu) : ~t);
+}
+
+// Bin b0's bounds: key(v) >> SHIFT == b0 <=> lo <= v < hi; above b0 <=> v >= hi
+struct BinBounds {
+  float lo, hi;
+  bool has_hi;
+  __device__ BinBounds(uint32_t b0, int shift) {
+    lo = key_bound(b0 << shift);
+    has_hi = (b0 + 1) < (1u << (32 - shift));
+    hi = has_hi ? key_bound((b0 + 1) << shift) : 0.f;
+  }
+  __device__ bool above(float v) const { return has_hi & (v >= hi); }
+  __device__ bool at_least(float v) const { return v >= lo; }
+};
+
 // Exclusive prefix sum of one uint32 per thread over an NT-thread block;
 // `sh` holds NT/64 words. Returns the prefix; *total gets the block sum.
 template <int NT>
@@ -134,14 +156,14 @@ __global__ __launch_bounds__(256) void topk_partition_kernel(TopkParams p) {
 
   uint32_t* bm = p.bitmap + (size_t)r * p.bm_stride + start / 32;
   uint32_t ncand = 0;
+  const BinBounds bb(b0, SHIFT);
 #pragma unroll
   for (int i = 0; i < PER; ++i) {
     const int e = start + i * 256 + tid;
-    const uint32_t key = float_key(v[i]);
-    const uint32_t bin = key >> SHIFT;
     const bool in = e < len;
-    const bool sel = in && (whole ? bin >= b0 : bin > b0);
-    ncand += (in && !whole && bin == b0) ? 1u : 0u;
+    const bool hi = bb.above(v[i]), lo = bb.at_least(v[i]);
+    const bool sel = in & (whole ? lo : hi);
+    ncand += (uint32_t)(in & !whole & lo & !hi);
     const unsigned long long m = __ballot(sel);
     if (lane == 0)
       *reinterpret_cast<uint2*>(bm + i * 8 + wv * 2) = make_uint2((uint32_t)m, (uint32_t)(m >> 32));
@@ -157,9 +179,8 @@ __global__ __launch_bounds__(256) void topk_partition_kernel(TopkParams p) {
 #pragma unroll
   for (int i = 0; i < PER; ++i) {
     const int e = start + i * 256 + tid;
-    const uint32_t key = float_key(v[i]);
-    if (e < len && (key >> SHIFT) == b0) {
-      if (pos < (uint32_t)kCandCap) cand[pos] = make_uint2(key, (uint32_t)e);
+    if ((e < len) & bb.at_least(v[i]) & !bb.above(v[i])) {
+      if (pos < (uint32_t)kCandCap) cand[pos] = make_uint2(float_key(v[i]), (uint32_t)e);
       ++pos;
     }
   }
@@ -192,10 +213,9 @@ struct RowList {
 // Among the list elements whose top 12 key bits equal b0, choose the `need`
 // largest keys (lower index first among equal keys) and set their bits in
 // `bm` (LDS or global).
-template <class List>
-__device__ void select_in_bin(const List& L, uint32_t b0, uint32_t need, uint32_t* bm,
+template <int NT, class List>
+__device__ __forceinline__ void select_in_bin(const List& L, uint32_t b0, uint32_t need, uint32_t* bm,
                               uint32_t* s_hist, uint32_t* s_sh) {
-  constexpr int NT = kFinalThreads;
   const int tid = threadIdx.x;
   const int n = L.size();
   const uint32_t pre20 = b0;                       // key >> 20
@@ -255,16 +275,16 @@ __device__ void select_in_bin(const List& L, uint32_t b0, uint32_t need, uint32_
   __syncthreads();
 }
 
-template <class List>
+template <int NT, class List>
 __device__ __forceinline__ void select_any(const TopkParams& p, int r, int len, uint32_t C,
                                            const List& lds_list, uint32_t b0, uint32_t need,
                                            uint32_t* bm, uint32_t* s_hist, uint32_t* s_sh) {
   if (C <= (uint32_t)kCandLds)
-    select_in_bin(lds_list, b0, need, bm, s_hist, s_sh);
+    select_in_bin<NT>(lds_list, b0, need, bm, s_hist, s_sh);
   else if (C <= (uint32_t)kCandCap)
-    select_in_bin(GlobalList{p.cand + (size_t)r * kCandCap, (int)C}, b0, need, bm, s_hist, s_sh);
+    select_in_bin<NT>(GlobalList{p.cand + (size_t)r * kCandCap, (int)C}, b0, need, bm, s_hist, s_sh);
   else
-    select_in_bin(RowList{p.votes + (size_t)r * p.row_stride, len}, b0, need, bm, s_hist, s_sh);
+    select_in_bin<NT>(RowList{p.votes + (size_t)r * p.row_stride, len}, b0, need, bm, s_hist, s_sh);
 }
 
 // Ascending indices of the set bits of words [0, W), at most k_eff of them.
@@ -273,10 +293,10 @@ __device__ __forceinline__ void select_any(const TopkParams& p, int r, int len, 
 // indices, so a wave loops only as often as its fullest word of the chunk
 // has bits. A first pass counts each segment; a scan of the eight segment
 // totals gives the waves their output bases.
-template <bool LDS_BM>
+template <bool LDS_BM, int NT = kFinalThreads>
 __device__ __forceinline__ void emit_bitmap(const uint32_t* bm, int W, int k_eff, int32_t* out,
                                             uint32_t* s_sh) {
-  constexpr int NW = kFinalThreads / 64;
+  constexpr int NW = NT / 64;
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int seg = (((W + NW - 1) / NW) + 63) & ~63;
   const int w0 = wv * seg, w1 = min(W, w0 + seg);
@@ -369,17 +389,219 @@ __global__ __launch_bounds__(kFinalThreads) void topk_finalize_kernel(TopkParams
 
   const LdsList lds_list{s_ck, s_ci, (int)min(C, (uint32_t)kCandLds)};
   if (lds_bm) {
-    if (need > 0) select_any(p, r, len, C, lds_list, b0, need, s_bm, s_hist, s_sh);
+    if (need > 0) select_any<NT>(p, r, len, C, lds_list, b0, need, s_bm, s_hist, s_sh);
     emit_bitmap<true>(s_bm, W, k_eff, out, s_sh);
   } else {
     if (need > 0) {
-      select_any(p, r, len, C, lds_list, b0, need, bm, s_hist, s_sh);
+      select_any<NT>(p, r, len, C, lds_list, b0, need, bm, s_hist, s_sh);
       // this work-group's bitmap updates must be visible to its own loads below
       __threadfence();
       __syncthreads();
     }
     emit_bitmap<false>(bm, W, k_eff, out, s_sh);
   }
+}
+
+// ---- steps 2 + 3 in one work-group per row ------------------------------------
+// For many rows whose bitmap fits in LDS (up to kBitmapLds * 32 keys; the
+// prefill chunk's 512 rows): one work-group of kRowThreads per row reads the
+// finished histogram, finds b0, streams the row once (16-byte loads, 16 in
+// flight per thread) building the selection bitmap in LDS (four ballots per
+// 256 keys, bit-interleaved into eight words) and the b0 candidates in LDS,
+// selects inside b0, and emits the indices; nothing goes through global
+// memory unless the candidates overflow LDS. The scan costs about ten vector
+// instructions per key on one CU, so a handful of long rows (decode) is
+// faster spread over many work-groups by the partition kernel.
+__device__ __forceinline__ uint32_t spread8(uint32_t x) {   // bit i -> bit 4i
+  x = (x | (x << 12)) & 0x000F000Fu;
+  x = (x | (x << 6)) & 0x03030303u;
+  x = (x | (x << 3)) & 0x11111111u;
+  return x;
+}
+
+template <bool VEC, bool HIST>
+__global__ __launch_bounds__(kRowThreads) void topk_row_kernel(TopkParams p) {
+  constexpr int NT = kRowThreads;
+  constexpr int NWV = NT / 64;
+  constexpr int SHIFT = 32 - kHist0Bits;
+  constexpr int UL = 8;                            // 16-byte loads per thread and buffer
+  constexpr int CAP = kCandLdsRow;                 // candidates held in LDS (gfx950: 160 KB/WG)
+  __shared__ uint32_t s_hist[1 << kHist0Bits];    // first histogram, then the select passes
+  __shared__ uint32_t s_ck[CAP];
+  __shared__ uint32_t s_ci[CAP];
+  __shared__ uint32_t s_bm[kBitmapLds];
+  __shared__ uint32_t s_sh[NWV + 8];
+  __shared__ uint32_t s_ncand;
+  const int r = blockIdx.x;
+  if (p.hit && p.hit[r]) return;
+  const int len = row_length(p, r);
+  const int k = p.k;
+  const int k_eff = min(k, len);
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  int32_t* out = p.idx + (size_t)r * k;
+  for (int i = max(k_eff, 0) + tid; i < k; i += NT) out[i] = -1;
+  if (k_eff <= 0) return;
+  const uint32_t* ctrl = p.ctrl + (size_t)r * kCtrlStride;
+  const float* row = p.votes + (size_t)r * p.row_stride;
+  const int W = (len + 31) / 32;
+
+  // the first 16 key groups of the row are requested before the histogram.
+  // Loads are unconditional (a group past the row's storage is clamped into
+  // it; keys past len are masked later), so they all stay in flight.
+  const int ng = (len + 3) / 4;                    // 4-key groups
+  float4 va[UL], vb[UL];                           // two rounds in flight
+  auto load_round = [&](int g0, float4 (&v)[UL]) {
+#pragma unroll
+    for (int u = 0; u < UL; ++u) {
+      const int e = 4 * (g0 + u * NT + tid);
+      if constexpr (VEC) {
+        v[u] = *reinterpret_cast<const float4*>(row + min(e, p.row_stride - 4));
+      } else {
+        v[u].x = row[min(e, len - 1)];
+        v[u].y = row[min(e + 1, len - 1)];
+        v[u].z = row[min(e + 2, len - 1)];
+        v[u].w = row[min(e + 3, len - 1)];
+      }
+    }
+  };
+  load_round(0, va);
+  load_round(UL * NT, vb);
+
+  // bin b0 of the k-th largest key: thread t owns bins 4t .. 4t+3
+  uint32_t c[4] = {0u, 0u, 0u, 0u};
+  if constexpr (HIST) {
+    // the whole row is in registers (len <= 2 * UL * NT * 4): histogram in LDS
+    for (int i = tid; i < (1 << kHist0Bits); i += NT) s_hist[i] = 0u;
+    if (tid == 0) s_ncand = 0u;
+    __syncthreads();
+    auto add = [&](int g0, const float4 (&v)[UL]) {
+#pragma unroll
+      for (int u = 0; u < UL; ++u) {
+        const int e = 4 * (g0 + u * NT + tid);
+        const float x[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          if (e + j < len) atomicAdd(&s_hist[float_key(x[j]) >> SHIFT], 1u);
+      }
+    };
+    add(0, va);
+    add(UL * NT, vb);
+    __syncthreads();
+    const uint4 a = *reinterpret_cast<const uint4*>(s_hist + 4 * tid);
+    c[0] = a.x; c[1] = a.y; c[2] = a.z; c[3] = a.w;
+  } else {
+    // built by the vote kernel (or topk_hist0): the sum of the copies
+    for (int cp = 0; cp < p.hist_copies; ++cp) {
+      const uint4 a = ld16(ctrl + kCtlHist0 + cp * (1 << kHist0Bits) + 4 * tid);
+      c[0] += a.x; c[1] += a.y; c[2] += a.z; c[3] += a.w;
+    }
+    if (tid == 0) s_ncand = 0u;
+  }
+  const uint2 rb = resolve_counts<4, NT>(c, (uint32_t)k_eff, s_sh);
+  const uint32_t b0 = rb.x, need = rb.y;
+  // the count of bin b0 is held by thread b0 / 4
+  if (tid == (int)(b0 >> 2)) s_sh[NWV + 2] = c[b0 & 3];
+  __syncthreads();
+  const bool whole = (need == s_sh[NWV + 2]);      // the whole bin is selected
+  const BinBounds bb(b0, SHIFT);
+
+  auto scan_round = [&](int g0, const float4 (&v)[UL]) {
+    uint32_t nc = 0;                               // this lane's candidates in the round
+#pragma unroll
+    for (int u = 0; u < UL; ++u) {
+      const int gbase = g0 + u * NT + wv * 64;     // the wave's first group
+      if (4 * gbase >= len) break;
+      const int e = 4 * (gbase + lane);
+      const float x[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
+      unsigned long long M[4];
+      // two float compares per key against the bin's bounds; branch-free
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const bool in = e + j < len;
+        const bool hi = bb.above(x[j]), lo = bb.at_least(x[j]);
+        M[j] = __ballot(in & (whole ? lo : hi));
+        nc += (uint32_t)(in & !whole & lo & !hi);
+      }
+      // eight bitmap words of the wave's 256 keys: word m holds lanes 8m..8m+7
+      if (lane < 8) {
+        const int w = (4 * gbase) / 32 + lane;
+        uint32_t word = 0;
+        if ((M[0] | M[1] | M[2] | M[3]) != 0ull) {   // most groups select nothing
+#pragma unroll
+          for (int j = 0; j < 4; ++j) word |= spread8((uint32_t)(M[j] >> (8 * lane)) & 0xFFu) << j;
+        }
+        if (w < W) s_bm[w] = word;
+      }
+    }
+    // the round's candidates: one slot reservation per wave, then the writes
+    if (whole || !__any(nc != 0)) return;
+    const uint32_t incl = wave_incl_scan_u(nc);
+    uint32_t base = 0;
+    if (lane == 63) base = atomicAdd(&s_ncand, incl);
+    base = __shfl(base, 63);
+    uint32_t pos = base + incl - nc;
+#pragma unroll
+    for (int u = 0; u < UL; ++u) {
+      const int gbase = g0 + u * NT + wv * 64;
+      if (4 * gbase >= len) break;
+      const int e = 4 * (gbase + lane);
+      const float x[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        if ((e + j < len) & bb.at_least(x[j]) & !bb.above(x[j])) {
+          if (pos < (uint32_t)CAP) {
+            s_ck[pos] = float_key(x[j]);
+            s_ci[pos] = (uint32_t)(e + j);
+          }
+          ++pos;
+        }
+      }
+    }
+  };
+  // rounds alternate between the two buffers; the next-but-one round is
+  // requested as soon as a buffer is free. Loads in the steady state are
+  // unconditional, so the compiler can count the ones in flight.
+  const int RS = UL * NT;                          // groups per round
+  const int nr = (ng + RS - 1) / RS;
+  int ri = 0;
+  for (; ri + 3 < nr; ri += 2) {
+    scan_round(ri * RS, va);
+    load_round((ri + 2) * RS, va);
+    scan_round((ri + 1) * RS, vb);
+    load_round((ri + 3) * RS, vb);
+  }
+  if (ri + 2 < nr) {
+    scan_round(ri * RS, va);
+    load_round((ri + 2) * RS, va);
+    scan_round((ri + 1) * RS, vb);
+    scan_round((ri + 2) * RS, va);
+  } else if (ri + 1 < nr) {
+    scan_round(ri * RS, va);
+    scan_round((ri + 1) * RS, vb);
+  } else {
+    scan_round(ri * RS, va);
+  }
+  __syncthreads();
+  const uint32_t C = s_ncand;
+  if (!whole && need > 0) {
+    if (C <= (uint32_t)CAP)
+      select_in_bin<NT>(LdsList{s_ck, s_ci, (int)C}, b0, need, s_bm, s_hist, s_sh);
+    else   // more candidates than LDS holds: walk the row itself
+      select_in_bin<NT>(RowList{row, len}, b0, need, s_bm, s_hist, s_sh);
+  }
+  emit_bitmap<true, NT>(s_bm, W, k_eff, out, s_sh);
+}
+
+// own_hist: rows of at most kRowKeysInRegs keys build their first histogram
+// in LDS (no prologue, no histogram kernel); otherwise it comes from ctrl
+hipError_t launch_topk_row(const TopkParams& p, bool own_hist, hipStream_t s) {
+  const bool vec = (p.row_stride & 3) == 0 && p.row_stride >= 4;
+  const dim3 g(p.rows), b(kRowThreads);
+  if (vec && own_hist) TS_KLAUNCH((topk_row_kernel<true, true>), g, b, 0, s, p);
+  else if (vec) TS_KLAUNCH((topk_row_kernel<true, false>), g, b, 0, s, p);
+  else if (own_hist) TS_KLAUNCH((topk_row_kernel<false, true>), g, b, 0, s, p);
+  else TS_KLAUNCH((topk_row_kernel<false, false>), g, b, 0, s, p);
+  return hipGetLastError();
 }
 
 hipError_t launch_topk_hist0(const TopkParams& p, int grid_x, hipStream_t s) {

@@ -49,12 +49,12 @@ ts_status hip_check(hipError_t e, const char* what) {
 // ---- kernel-level timing (ts_profile_*) ---------------------------------------
 enum KernelKind {
   kKPrologue, kKScore, kKLse, kKVotes, kKTopkHist, kKTopkPartition, kKTopkFinalize, kKAttend,
-  kKCombine, kKPrefillLse, kKPrefillVotes, kKFill, kKAppend, kKQuestMeta, kKQuestScore, kKNum
+  kKCombine, kKPrefillLse, kKPrefillVotes, kKFill, kKAppend, kKQuestMeta, kKQuestScore, kKTopkRow, kKNum
 };
 const char* const kKernelNames[kKNum] = {
   "prologue", "score_pass1", "lse", "votes", "topk_hist", "topk_partition", "topk_finalize",
   "attend", "combine", "prefill_lse", "prefill_votes", "fill_zero", "append_kv", "quest_meta",
-  "quest_score"
+  "quest_score", "topk_row"
 };
 
 struct Prof {
@@ -506,9 +506,27 @@ ts_status ts_topk_workspace_size(int32_t rows, int32_t row_stride, int32_t k, si
   return ok();
 }
 
+// many rows whose bitmap fits in LDS: one fused work-group per row; a few
+// long rows, or rows too long for LDS: the partition and finalize kernels
+static ts_status run_select(const TopkParams& tp, int gx, int max_row_len, hipStream_t st) {
+  if (tp.rows >= kRowKernelMinRows && max_row_len <= kBitmapLds * 32) {
+    TS_LAUNCH_K(kKTopkRow, launch_topk_row(tp, false, st), "top-k select");
+  } else {
+    TS_LAUNCH_K(kKTopkPartition, launch_topk_partition(tp, gx, st), "top-k partition");
+    TS_LAUNCH_K(kKTopkFinalize, launch_topk_finalize(tp, st), "top-k finalize");
+  }
+  return TS_OK;
+}
+
 static ts_status run_topk(int rows, int row_stride, const float* votes, const int32_t* row_lens,
                           int row_len_base, int k, int32_t* idx, void* ws, const TopkPlan& t,
                           int max_row_len, hipStream_t st) {
+  if (rows >= kRowKernelMinRows && max_row_len <= kRowKeysInRegs) {
+    // many short rows: one kernel, each work-group holds its row in registers
+    TopkParams tp = topk_params(t, ws, rows, row_stride, k, votes, row_lens, row_len_base, nullptr, idx);
+    TS_LAUNCH_K(kKTopkRow, launch_topk_row(tp, true, st), "top-k select");
+    return TS_OK;
+  }
   PrologueParams pp{};
   const int gx = cdiv(max_row_len, kTopkChunk);
   const int copies = hist_copies_for(gx);
@@ -519,8 +537,7 @@ static ts_status run_topk(int rows, int row_stride, const float* votes, const in
   TopkParams tp = topk_params(t, ws, rows, row_stride, k, votes, row_lens, row_len_base, nullptr, idx);
   tp.hist_copies = copies;
   TS_LAUNCH_K(kKTopkHist, launch_topk_hist0(tp, gx, st), "top-k histogram");
-  TS_LAUNCH_K(kKTopkPartition, launch_topk_partition(tp, gx, st), "top-k partition");
-  TS_LAUNCH_K(kKTopkFinalize, launch_topk_finalize(tp, st), "top-k finalize");
+  TS_TRY(run_select(tp, gx, max_row_len, st));
   return TS_OK;
 }
 
@@ -978,9 +995,7 @@ ts_status ts_decode_step(ts_sel_cache* cache, const ts_kv_layout* L, int32_t bat
   TopkParams tp = topk_params(p.t, ws, batch, g.max_len, k, votes, seq_lens, 0, hit,
                               cache->dev.sel);
   tp.hist_copies = copies;
-  const int gx = cdiv(g.max_len, kTopkChunk);
-  TS_LAUNCH_K(kKTopkPartition, launch_topk_partition(tp, gx, st), "top-k partition");
-  TS_LAUNCH_K(kKTopkFinalize, launch_topk_finalize(tp, st), "top-k finalize");
+  TS_TRY(run_select(tp, cdiv(g.max_len, kTopkChunk), g.max_len, st));
   // 5. sparse attention over the current selection; 6. combine + state update
   AttendParams ap = attend_params(g, p.a, batch, ws, q, k_cache, v_cache, pt, seq_lens,
                                   cache->dev.sel, k);

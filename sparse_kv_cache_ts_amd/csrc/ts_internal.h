@@ -47,6 +47,10 @@ constexpr int kCandCap = 8192;    // candidates kept per row; more falls back to
 constexpr int kCandLds = 2048;    // candidates the finalize work-group stages in LDS
 constexpr int kBitmapLds = 8192;  // bitmap words (rows of up to 262144 tokens) staged in LDS
 constexpr int kFinalThreads = 512;
+constexpr int kRowThreads = 1024;  // fused top-k: one work-group per row of <= kBitmapLds*32 keys
+constexpr int kRowKernelMinRows = 256; // fewer rows: partition + finalize (more CUs per row)
+constexpr int kCandLdsRow = 8192;      // candidates the fused work-group keeps in LDS
+constexpr int kRowKeysInRegs = 2 * 8 * kRowThreads * 4;   // rows the fused work-group holds whole
 
 inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 inline int cdiv(long a, long b) { return (int)((a + b - 1) / b); }
@@ -215,6 +219,7 @@ hipError_t launch_lse(const LseParams& p, hipStream_t s);
 hipError_t launch_votes(const VoteParams& p, int grid_x, hipStream_t s);
 hipError_t launch_topk_hist0(const TopkParams& p, int grid_x, hipStream_t s);
 hipError_t launch_topk_partition(const TopkParams& p, int grid_x, hipStream_t s);
+hipError_t launch_topk_row(const TopkParams& p, bool own_hist, hipStream_t s);
 hipError_t launch_topk_finalize(const TopkParams& p, hipStream_t s);
 hipError_t launch_attend(int dtype, int d, bool paged, const AttendParams& p, hipStream_t s);
 hipError_t launch_combine(const CombineParams& p, hipStream_t s);

@@ -36,6 +36,9 @@ SMALL = [
     _small_cfg("g8-d128-f32", 1, 16, 2, 128, 1500, "f32", 64, 14),
     _small_cfg("g2-d128-bf16-ragged", 3, 4, 2, 128, 257, "bf16", 300, 15, heavy=0.05),
     _small_cfg("g16-d64-bf16", 1, 16, 1, 64, 999, "bf16", 77, 16),   # G > 8: two head slices
+    _small_cfg("g2-d128-bf16-16kv", 2, 32, 16, 128, 1234, "bf16", 200, 17),  # 4 KV heads per wave
+    _small_cfg("g3-d128-bf16-3kv", 2, 9, 3, 128, 700, "bf16", 50, 18),       # vector-ALU pass
+    _small_cfg("g4-d128-bf16-1kv", 1, 4, 1, 128, 4500, "bf16", 300, 19),
 ]
 
 
@@ -103,14 +106,20 @@ def test_score_votes_paged_matches_contiguous(gpu_lib):
         assert torch.equal(v_cont[b, :n], v_pag[b, :n])
 
 
-def _topk_rows(seed):
+def _topk_rows(seed, stride=70010):
     g = torch.Generator(device="cpu").manual_seed(seed)
     lens = [0, 1, 5, 255, 4095, 4096, 4097, 10000, 70001]
-    stride = 70010
     rows = []
     for i, n in enumerate(lens):
-        kind = i % 4
-        if kind == 0:
+        kind = i % 5
+        if kind == 4:
+            # subnormals (down to 1e-45), +-0 and the smallest normals: the
+            # selection compares floats, which must not flush subnormals
+            r = torch.rand(stride, generator=g) * 2e-38
+            r[::5] = -r[::5]
+            r[::11] = 0.0
+            r[1::11] = -0.0
+        elif kind == 0:
             r = torch.rand(stride, generator=g)
         elif kind == 1:
             r = torch.randint(0, 4, (stride,), generator=g).float()        # heavy ties
@@ -128,6 +137,27 @@ def _topk_rows(seed):
 def test_topk_exact(gpu_lib, k):
     ts = gpu_lib
     votes, lens = _topk_rows(k)
+    vd = votes.cuda()
+    ld = torch.tensor(lens, dtype=torch.int32, device="cuda")
+    idx = ts.topk(vd, ld, k)
+    torch.cuda.synchronize()
+    got = idx.cpu().numpy()
+    v = votes.numpy().astype(np.float64)
+    for r, n in enumerate(lens):
+        want = O.top_k(v[r, :n], k)
+        assert np.array_equal(got[r], want), f"row {r} (len {n})"
+
+
+@pytest.mark.parametrize("stride", [70012, 65533, 65536])
+@pytest.mark.parametrize("k", [300, 9000])
+def test_topk_exact_many_rows(gpu_lib, k, stride):
+    """288 rows: the one-work-group-per-row kernel (16-byte loads when the row
+    stride is a multiple of 4, single loads otherwise; rows of at most 65536
+    keys build their histogram in the kernel)."""
+    ts = gpu_lib
+    parts = [_topk_rows(100 * k + i, stride) for i in range(32)]
+    votes = torch.cat([p[0] for p in parts])
+    lens = [min(n, stride) for n in sum((p[1] for p in parts), [])]
     vd = votes.cuda()
     ld = torch.tensor(lens, dtype=torch.int32, device="cuda")
     idx = ts.topk(vd, ld, k)
