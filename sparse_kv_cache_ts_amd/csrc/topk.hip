@@ -340,6 +340,40 @@ __device__ __forceinline__ void emit_bitmap(const uint32_t* bm, int W, int k_eff
   }
 }
 
+// Ascending indices of the set bits of an LDS bitmap of W words, at most
+// k_eff of them: thread t owns WPT consecutive words, a block scan of the
+// threads' popcounts gives each its first output slot, and it writes its
+// bits in order. One LDS pass and one scan; `sh` holds NT/64 words.
+template <int NT>
+__device__ __forceinline__ void emit_bitmap_lds(const uint32_t* bm, int W, int k_eff, int32_t* out,
+                                                uint32_t* sh) {
+  const int tid = threadIdx.x;
+  const int wpt = ((W + NT - 1) / NT + 3) & ~3;   // a multiple of 4: 16-byte LDS reads
+  const int w0 = tid * wpt;
+  uint32_t cnt = 0;
+  for (int i = 0; i < wpt; i += 4) {
+    const int w = w0 + i;
+    if (w + 3 < W) {
+      const uint4 q = *reinterpret_cast<const uint4*>(bm + w);
+      cnt += (__popc(q.x) + __popc(q.y)) + (__popc(q.z) + __popc(q.w));
+    } else {
+      for (int j = 0; j < 4; ++j)
+        if (w + j < W) cnt += __popc(bm[w + j]);
+    }
+  }
+  uint32_t total;
+  uint32_t pos = block_excl_scan<NT>(cnt, sh, &total);
+  for (int i = 0; i < wpt && pos < (uint32_t)k_eff; ++i) {
+    const int w = w0 + i;
+    if (w >= W) break;
+    uint32_t m = bm[w];
+    while (m && pos < (uint32_t)k_eff) {
+      out[pos++] = w * 32 + (__ffs(m) - 1);
+      m &= m - 1;
+    }
+  }
+}
+
 __global__ __launch_bounds__(kFinalThreads) void topk_finalize_kernel(TopkParams p) {
   constexpr int NT = kFinalThreads;
   constexpr int CPT = kCandLds / NT;               // staged candidates per thread
@@ -347,7 +381,7 @@ __global__ __launch_bounds__(kFinalThreads) void topk_finalize_kernel(TopkParams
   __shared__ uint32_t s_hist[2048];
   __shared__ uint32_t s_ck[kCandLds];
   __shared__ uint32_t s_ci[kCandLds];
-  __shared__ uint32_t s_bm[kBitmapLds];
+  __shared__ __align__(16) uint32_t s_bm[kBitmapLds];
   __shared__ uint32_t s_sh[16];
   const int r = blockIdx.x;
   if (p.hit && p.hit[r]) return;
@@ -390,7 +424,7 @@ __global__ __launch_bounds__(kFinalThreads) void topk_finalize_kernel(TopkParams
   const LdsList lds_list{s_ck, s_ci, (int)min(C, (uint32_t)kCandLds)};
   if (lds_bm) {
     if (need > 0) select_any<NT>(p, r, len, C, lds_list, b0, need, s_bm, s_hist, s_sh);
-    emit_bitmap<true>(s_bm, W, k_eff, out, s_sh);
+    emit_bitmap_lds<NT>(s_bm, W, k_eff, out, s_sh);
   } else {
     if (need > 0) {
       select_any<NT>(p, r, len, C, lds_list, b0, need, bm, s_hist, s_sh);
@@ -429,7 +463,7 @@ __global__ __launch_bounds__(kRowThreads) void topk_row_kernel(TopkParams p) {
   __shared__ uint32_t s_hist[1 << kHist0Bits];    // first histogram, then the select passes
   __shared__ uint32_t s_ck[CAP];
   __shared__ uint32_t s_ci[CAP];
-  __shared__ uint32_t s_bm[kBitmapLds];
+  __shared__ __align__(16) uint32_t s_bm[kBitmapLds];
   __shared__ uint32_t s_sh[NWV + 8];
   __shared__ uint32_t s_ncand;
   const int r = blockIdx.x;
@@ -589,7 +623,7 @@ __global__ __launch_bounds__(kRowThreads) void topk_row_kernel(TopkParams p) {
     else   // more candidates than LDS holds: walk the row itself
       select_in_bin<NT>(RowList{row, len}, b0, need, s_bm, s_hist, s_sh);
   }
-  emit_bitmap<true, NT>(s_bm, W, k_eff, out, s_sh);
+  emit_bitmap_lds<NT>(s_bm, W, k_eff, out, s_sh);
 }
 
 // own_hist: rows of at most kRowKeysInRegs keys build their first histogram
