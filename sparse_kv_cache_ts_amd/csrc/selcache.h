@@ -25,10 +25,13 @@ __device__ __forceinline__ int cache_decision(const SelCacheDev& c, const void* 
                                               int len, int r, double theta, double (*s_red)[4],
                                               int* s_hit, double* cos_out) {
   const int tid = threadIdx.x;
-  const bool can = c.valid[r] != 0 && len > 0;
+  // the state flag is loaded together with the data, not before it: the
+  // stored query is read whether or not it is valid (it is always allocated)
+  // and the flag only gates the result, so the decision costs one round trip
+  const int valid = c.valid[r];
   const int n = c.Hq * c.d;
   double dot = 0.0, nq = 0.0, np = 0.0;
-  if (can) {
+  {
     // 8 consecutive elements per thread and step; every load of a step is
     // issued before the fp64 accumulation (n = Hq*d is a multiple of 64)
     const float* pq = c.prev_q + (size_t)r * n;
@@ -82,6 +85,7 @@ __device__ __forceinline__ int cache_decision(const SelCacheDev& c, const void* 
     s_red[2][w] = np;
   }
   __syncthreads();
+  const bool can = valid != 0 && len > 0;
   if (tid == 0) {
     double D = 0.0, Q = 0.0, P = 0.0;
     for (int i = 0; i < 4; ++i) {
