@@ -13,11 +13,11 @@
 // are merged through LDS in a fixed order, and each (sequence, head, split)
 // leaves (max, sum, acc[d]). combine_kernel merges the splits by their
 // log-sum-exp and, in a decode step, also updates the Selection-Cache state.
-#include "ts_device.h"
+#include "topk_device.h"
 
 namespace ts {
 
-template <int DT, int D, int GS, bool PAGED, bool DENSE>
+template <int DT, int D, int GS, bool PAGED, bool DENSE, bool SEL>
 __global__ __launch_bounds__(256) void attend_kernel(AttendParams p) {
   constexpr int ESZ = DT ? 2 : 4;
   constexpr int ROWB = D * ESZ;
@@ -32,6 +32,13 @@ __global__ __launch_bounds__(256) void attend_kernel(AttendParams p) {
   __shared__ float s_m[4][GS];
   __shared__ float s_l[4][GS];
   __shared__ float s_acc[4 * GS * D];
+  // decode steps: the end of the top-k for this split's token range
+  __shared__ uint32_t s_ck[SEL ? kCandLds : 1];
+  __shared__ uint32_t s_ci[SEL ? kCandLds : 1];
+  __shared__ uint32_t s_hist[SEL ? 2048 : 1];
+  __shared__ uint32_t s_rw[SEL ? kSelRangeMax / 32 : 1];
+  __shared__ int32_t s_tok[SEL ? kSelRangeMax : 1];
+  __shared__ uint32_t s_sh[16];
 
   const int split = blockIdx.x;
   const int kvh = blockIdx.y / p.nslices;
@@ -43,11 +50,80 @@ __global__ __launch_bounds__(256) void attend_kernel(AttendParams p) {
   const int wv = tid >> 6, lane = tid & 63;
   const int len = p.seq_lens ? p.seq_lens[b] : p.len_base + b;
   const int bkv = p.kv_shared ? 0 : b;
-  const int pbeg = split * p.split;
-  const int pend = min(pbeg + p.split, p.nidx);
+  int pbeg = split * p.split;
+  int pend = min(pbeg + p.split, p.nidx);
   const int32_t* idx =
       DENSE ? nullptr : p.idx + (size_t)b * p.idx_b_stride + (size_t)kvh * p.idx_kv_stride;
   const int Hkv = p.Hkv;
+  bool lds_list = false;
+  if constexpr (SEL) {
+    if (!p.sel_hit[b]) {
+      // ---- the selection of tokens [r0, r1): the partition kernel set the
+      // bits of every key above the k-th key's histogram bin b0 (or of the
+      // whole bin) and listed the keys inside b0; the threshold inside b0 is
+      // found again here (every work-group of the sequence gets the same one)
+      const int k = p.sel_k;
+      const int k_eff = min(k, len);
+      const int r0 = split * p.sel_range;
+      const int r1 = max(r0, min(r0 + p.sel_range, len));
+      const uint32_t* ctrl = p.sel_ctrl + (size_t)b * kCtrlStride;
+      const uint32_t* bm = p.sel_bitmap + (size_t)b * p.sel_bm_stride;
+      const uint2* cand = p.sel_cand + (size_t)b * kCandCap;
+      const uint32_t b0 = ctrl[kCtlPrefix], need = ctrl[kCtlNeed], C = ctrl[kCtlCandCount];
+      uint2 cv[kCandLds / 256];
+#pragma unroll
+      for (int i = 0; i < kCandLds / 256; ++i) cv[i] = cand[i * 256 + tid];  // stale past C: unused
+      const int w0 = r0 >> 5, wr = (r1 - r0 + 31) >> 5;
+      uint32_t rw = tid < wr ? bm[w0 + tid] : 0u;
+      // selected base bits before the range (16-byte loads, clamped, masked)
+      uint32_t pc = 0;
+      for (int w = 4 * tid; w < w0; w += 4 * 256) {
+        const uint4 q4 = *reinterpret_cast<const uint4*>(bm + min(w, w0 - 4));
+        pc += (w + 0 < w0 ? __popc(q4.x) : 0u) + (w + 1 < w0 ? __popc(q4.y) : 0u) +
+              (w + 2 < w0 ? __popc(q4.z) : 0u) + (w + 3 < w0 ? __popc(q4.w) : 0u);
+      }
+#pragma unroll
+      for (int i = 0; i < kCandLds / 256; ++i) {
+        s_ck[i * 256 + tid] = cv[i].x;
+        s_ci[i * 256 + tid] = cv[i].y;
+      }
+      if (tid < wr) s_rw[tid] = rw;
+      __syncthreads();
+      if (need > 0 && k_eff > 0) {
+        const float* vrow = p.sel_votes + (size_t)b * p.sel_vote_stride;
+        auto visit = [&](const auto& L) {
+          const BinThreshold th = find_threshold<256>(L, b0, need, s_hist, s_sh);
+          for (int i = tid; i < L.size(); i += 256) {
+            const uint2 e = L.get(i);
+            if (th.take(e)) {
+              if (e.y < (uint32_t)r0) ++pc;
+              else if (e.y < (uint32_t)r1) atomicOr(&s_rw[(e.y >> 5) - w0], 1u << (e.y & 31));
+            }
+          }
+        };
+        if (C <= (uint32_t)kCandLds) visit(LdsList{s_ck, s_ci, (int)C});
+        else if (C <= (uint32_t)kCandCap) visit(GlobalList{cand, (int)C});
+        else visit(RowList{vrow, len});
+      }
+      __syncthreads();
+      uint32_t before, count;
+      (void)block_excl_scan<256>(pc, s_sh, &before);
+      const uint32_t wbits = tid < wr ? s_rw[tid] : 0u;
+      uint32_t o = block_excl_scan<256>(__popc(wbits), s_sh, &count);
+      for (uint32_t m = wbits; m; m &= m - 1) s_tok[o++] = (w0 + tid) * 32 + (__ffs(m) - 1);
+      __syncthreads();
+      // this range's part of the ascending selection (one work-group per range)
+      if (kvh == 0 && slice == 0) {
+        int32_t* so = p.sel_out + (size_t)b * k;
+        for (uint32_t i = tid; i < count; i += 256) so[before + i] = s_tok[i];
+        if (split == 0)
+          for (int i = max(k_eff, 0) + tid; i < k; i += 256) so[i] = -1;
+      }
+      lds_list = true;
+      pbeg = 0;
+      pend = (int)count;
+    }
+  }
 
   auto row_of = [&](int t) -> size_t {
     if constexpr (PAGED) {
@@ -129,7 +205,9 @@ __global__ __launch_bounds__(256) void attend_kernel(AttendParams p) {
   auto tok_at = [&](int pos) -> int {
     if (pos >= pend) return -1;
     long long t;
-    if (p.sel_page_log2 > 0) {
+    if (SEL && lds_list) {
+      t = s_tok[pos];
+    } else if (p.sel_page_log2 > 0) {
       const int pg = idx[pos >> p.sel_page_log2];
       t = pg < 0 ? -1 : ((long long)pg << p.sel_page_log2) + (pos & ((1 << p.sel_page_log2) - 1));
     } else {
@@ -368,11 +446,11 @@ __global__ __launch_bounds__(128) void combine_kernel(CombineParams p) {
   }
 }
 
-template <int DT, int D, bool PAGED, bool DENSE>
+template <int DT, int D, bool PAGED, bool DENSE, bool SEL = false>
 static hipError_t launch_attend_gs(const AttendParams& p, hipStream_t s) {
   dim3 grid(p.nsplit, p.Hkv * p.nslices, p.B);
   switch (p.GS) {
-#define TS_GS(n) case n: TS_KLAUNCH((attend_kernel<DT, D, n, PAGED, DENSE>), grid, dim3(256), 0, s, p); break;
+#define TS_GS(n) case n: TS_KLAUNCH((attend_kernel<DT, D, n, PAGED, DENSE, SEL>), grid, dim3(256), 0, s, p); break;
     TS_GS(1) TS_GS(2) TS_GS(3) TS_GS(4) TS_GS(5) TS_GS(6) TS_GS(7) TS_GS(8)
 #undef TS_GS
     default: return hipErrorInvalidValue;
@@ -391,6 +469,13 @@ static hipError_t launch_attend_mode(int dtype, int d, bool paged, const AttendP
 
 // idx null: dense attention over every cached token
 hipError_t launch_attend(int dtype, int d, bool paged, const AttendParams& p, hipStream_t s) {
+  if (p.sel_ctrl) {   // decode step: the selection is finished by the attention work-groups
+    if (dtype == 1 && d == 128) return paged ? launch_attend_gs<1, 128, true, false, true>(p, s) : launch_attend_gs<1, 128, false, false, true>(p, s);
+    if (dtype == 1 && d == 64) return paged ? launch_attend_gs<1, 64, true, false, true>(p, s) : launch_attend_gs<1, 64, false, false, true>(p, s);
+    if (dtype == 0 && d == 128) return paged ? launch_attend_gs<0, 128, true, false, true>(p, s) : launch_attend_gs<0, 128, false, false, true>(p, s);
+    if (dtype == 0 && d == 64) return paged ? launch_attend_gs<0, 64, true, false, true>(p, s) : launch_attend_gs<0, 64, false, false, true>(p, s);
+    return hipErrorInvalidValue;
+  }
   return p.idx ? launch_attend_mode<false>(dtype, d, paged, p, s) : launch_attend_mode<true>(dtype, d, paged, p, s);
 }
 

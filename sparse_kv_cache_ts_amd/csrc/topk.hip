@@ -19,7 +19,7 @@
 //      remaining 20 key bits, then on the index among exact ties so the lower
 //      indices win, sets their bits, and turns the bitmap into ascending
 //      indices with popcounts and a block scan.
-#include "ts_device.h"
+#include "topk_device.h"
 
 namespace ts {
 
@@ -48,27 +48,6 @@ struct BinBounds {
   __device__ bool above(float v) const { return has_hi & (v >= hi); }
   __device__ bool at_least(float v) const { return v >= lo; }
 };
-
-// Exclusive prefix sum of one uint32 per thread over an NT-thread block;
-// `sh` holds NT/64 words. Returns the prefix; *total gets the block sum.
-template <int NT>
-__device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, uint32_t* sh, uint32_t* total) {
-  constexpr int NWAVE = NT / 64;
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  const uint32_t x = wave_incl_scan_u(v);
-  if (lane == 63) sh[w] = x;
-  __syncthreads();
-  uint32_t base = 0, tot = 0;
-#pragma unroll
-  for (int i = 0; i < NWAVE; ++i) {
-    const uint32_t s = sh[i];
-    if (i < w) base += s;
-    tot += s;
-  }
-  __syncthreads();
-  *total = tot;
-  return base + x - v;
-}
 
 // ---- step 1 (standalone top-k): histogram of the top 12 key bits ------------
 __global__ __launch_bounds__(256) void topk_hist0_kernel(TopkParams p) {
@@ -187,93 +166,6 @@ __global__ __launch_bounds__(256) void topk_partition_kernel(TopkParams p) {
 }
 
 // ---- step 3: exact select among the candidates, then bitmap -> indices ------
-
-// (key, index) lists the finalize work-group walks: the candidates staged in
-// LDS, or the whole row (keys recomputed) after a candidate overflow.
-struct LdsList {
-  const uint32_t* key;
-  const uint32_t* idx;
-  int n;
-  __device__ int size() const { return n; }
-  __device__ uint2 get(int i) const { return make_uint2(key[i], idx[i]); }
-};
-struct GlobalList {
-  const uint2* c;
-  int n;
-  __device__ int size() const { return n; }
-  __device__ uint2 get(int i) const { return c[i]; }
-};
-struct RowList {
-  const float* row;
-  int n;
-  __device__ int size() const { return n; }
-  __device__ uint2 get(int i) const { return make_uint2(float_key(row[i]), (uint32_t)i); }
-};
-
-// Among the list elements whose top 12 key bits equal b0, choose the `need`
-// largest keys (lower index first among equal keys) and set their bits in
-// `bm` (LDS or global).
-template <int NT, class List>
-__device__ __forceinline__ void select_in_bin(const List& L, uint32_t b0, uint32_t need, uint32_t* bm,
-                              uint32_t* s_hist, uint32_t* s_sh) {
-  const int tid = threadIdx.x;
-  const int n = L.size();
-  const uint32_t pre20 = b0;                       // key >> 20
-  // pass A: key bits 19..10
-  for (int i = tid; i < 1024; i += NT) s_hist[i] = 0u;
-  __syncthreads();
-  for (int i = tid; i < n; i += NT) {
-    const uint2 e = L.get(i);
-    if ((e.x >> 20) == pre20) atomicAdd(&s_hist[(e.x >> 10) & 1023u], 1u);
-  }
-  __syncthreads();
-  const uint2 ra = resolve_lds<1024 / NT, NT>(s_hist, need, s_sh);
-  const uint32_t pre10 = (pre20 << 10) | ra.x;     // key >> 10
-  // pass B: key bits 9..0
-  for (int i = tid; i < 1024; i += NT) s_hist[i] = 0u;
-  __syncthreads();
-  for (int i = tid; i < n; i += NT) {
-    const uint2 e = L.get(i);
-    if ((e.x >> 10) == pre10) atomicAdd(&s_hist[e.x & 1023u], 1u);
-  }
-  __syncthreads();
-  const uint2 rbb = resolve_lds<1024 / NT, NT>(s_hist, ra.y, s_sh);
-  const uint32_t T = (pre10 << 10) | rbb.x;        // the k-th largest key
-  const uint32_t need_t = rbb.y;                   // ties at T to take
-  const uint32_t ntie = s_hist[rbb.x];
-  __syncthreads();
-  // among ties, the need_t smallest indices are the need_t largest values of
-  // ~index: three more digit passes (bits 31..21, 20..10, 9..0 of ~index)
-  uint32_t imax = 0xffffffffu;
-  if (ntie > need_t) {
-    uint32_t prefix = 0, nd = need_t;
-#pragma unroll
-    for (int ps = 0; ps < 3; ++ps) {
-      const int shift = (ps == 0) ? 21 : (ps == 1) ? 10 : 0;
-      const uint32_t mask = (ps == 2) ? 1023u : 2047u;
-      for (int i = tid; i < 2048; i += NT) s_hist[i] = 0u;
-      __syncthreads();
-      for (int i = tid; i < n; i += NT) {
-        const uint2 e = L.get(i);
-        const uint32_t ni = ~e.y;
-        const bool match = (e.x == T) && (ps == 0 || (ni >> (shift + (ps == 1 ? 11 : 10))) == prefix);
-        if (match) atomicAdd(&s_hist[(ni >> shift) & mask], 1u);
-      }
-      __syncthreads();
-      const uint2 rr = (ps < 2) ? resolve_lds<2048 / NT, NT>(s_hist, nd, s_sh)
-                                : resolve_lds<1024 / NT, NT>(s_hist, nd, s_sh);
-      prefix = (ps == 0) ? rr.x : ((prefix << (ps == 1 ? 11 : 10)) | rr.x);
-      nd = rr.y;
-    }
-    imax = ~prefix;                                 // ties with index <= imax are taken
-  }
-  for (int i = tid; i < n; i += NT) {
-    const uint2 e = L.get(i);
-    if ((e.x >> 20) == pre20 && (e.x > T || (e.x == T && e.y <= imax)))
-      atomicOr(bm + (e.y >> 5), 1u << (e.y & 31));
-  }
-  __syncthreads();
-}
 
 template <int NT, class List>
 __device__ __forceinline__ void select_any(const TopkParams& p, int r, int len, uint32_t C,

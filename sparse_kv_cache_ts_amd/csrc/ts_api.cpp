@@ -250,6 +250,7 @@ void plan_score(const Geo& g, int B, Carve& c, ScorePlan& s) {
 
 struct AttendPlan {
   int split, nsplit;
+  int range;                 // decode steps: tokens per split whose selection it finishes (0: none)
   size_t pm, pl, pacc;
 };
 void plan_attend(const Geo& g, int B, int k, Carve& c, AttendPlan& a) {
@@ -307,13 +308,41 @@ struct DecodePlan {
   size_t votes;
   size_t total;
 };
+// Decode steps: the attention work-groups finish the top-k, each for a token
+// range of the sequence. The range is the power of two (256 .. kSelRangeMax)
+// that holds about 32 selected tokens on average, so a split gathers about as
+// many rows as a split of a plain sparse attention; on a hit the same splits
+// read equal shares of the stored selection. Every work-group repeats the
+// threshold search inside the k-th key's bin, which pays only while all of
+// them run at once: with more than kSelMaxWGs work-groups (large batches,
+// many KV heads) or ranges past kSelRangeMax this returns 0, and a separate
+// finalize kernel emits the selection instead.
+int sel_range_for(const Geo& g, int B, int k) {
+  int range = 256;
+  while (range < kSelRangeMax && (long)range * k < 32l * g.max_len) range <<= 1;
+  const long wgs = (long)B * g.Hkv * g.nslices * cdiv(g.max_len, range);
+  if ((long)range * k < 32l * g.max_len || wgs > kSelMaxWGs) return 0;
+  return range;
+}
+
 void plan_decode(const Geo& g, int B, int k, DecodePlan& p) {
   Carve c;
   plan_score(g, B, c, p.s);
   plan_topk(B, g.max_len, c, p.t, false);
   p.t.ctrl = p.s.ctrl;
   p.votes = c.take((size_t)B * g.max_len * 4);
-  plan_attend(g, B, k, c, p.a);
+  const int range = sel_range_for(g, B, k);
+  if (range > 0) {
+    p.a.range = range;
+    p.a.nsplit = cdiv(g.max_len, range);
+    p.a.split = cdiv(k, p.a.nsplit);
+    p.a.pm = c.take((size_t)B * g.Hq * p.a.nsplit * 4);
+    p.a.pl = c.take((size_t)B * g.Hq * p.a.nsplit * 4);
+    p.a.pacc = c.take((size_t)B * g.Hq * p.a.nsplit * g.d * 4);
+  } else {
+    plan_attend(g, B, k, c, p.a);
+    p.a.range = 0;
+  }
   p.total = c.off;
 }
 
@@ -991,14 +1020,33 @@ ts_status ts_decode_step(ts_sel_cache* cache, const ts_kv_layout* L, int32_t bat
   VoteParams vp = vote_params(g, p.s, batch, ws, seq_lens, hit, votes, g.max_len, 1);
   vp.hist_copies = copies;
   TS_LAUNCH_K(kKVotes, launch_votes(vp, vote_wgs, st), "votes");
-  // 4. top-k into the cache's stored selection
+  // 4. top-k into the cache's stored selection: the partition here, its end
+  // in the attention work-groups (or, for rows too long for that, in the
+  // finalize kernel)
   TopkParams tp = topk_params(p.t, ws, batch, g.max_len, k, votes, seq_lens, 0, hit,
                               cache->dev.sel);
   tp.hist_copies = copies;
-  TS_TRY(run_select(tp, cdiv(g.max_len, kTopkChunk), g.max_len, st));
+  const int gx = cdiv(g.max_len, kTopkChunk);
+  if (p.a.range > 0) {
+    TS_LAUNCH_K(kKTopkPartition, launch_topk_partition(tp, gx, st), "top-k partition");
+  } else {
+    TS_TRY(run_select(tp, gx, g.max_len, st));
+  }
   // 5. sparse attention over the current selection; 6. combine + state update
   AttendParams ap = attend_params(g, p.a, batch, ws, q, k_cache, v_cache, pt, seq_lens,
                                   cache->dev.sel, k);
+  if (p.a.range > 0) {
+    ap.sel_ctrl = tp.ctrl;
+    ap.sel_bitmap = tp.bitmap;
+    ap.sel_cand = tp.cand;
+    ap.sel_votes = votes;
+    ap.sel_hit = hit;
+    ap.sel_out = cache->dev.sel;
+    ap.sel_bm_stride = p.t.bm_stride;
+    ap.sel_vote_stride = g.max_len;
+    ap.sel_range = p.a.range;
+    ap.sel_k = k;
+  }
   TS_LAUNCH_K(kKAttend, launch_attend(g.dtype, g.d, g.paged, ap, st), "sparse attention");
   CombineParams cp = combine_params(g, p.a, batch, ws, out);
   cp.cache = cache->dev;

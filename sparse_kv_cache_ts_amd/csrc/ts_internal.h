@@ -50,6 +50,8 @@ constexpr int kFinalThreads = 512;
 constexpr int kRowThreads = 1024;  // fused top-k: one work-group per row of <= kBitmapLds*32 keys
 constexpr int kRowKernelMinRows = 256; // fewer rows: partition + finalize (more CUs per row)
 constexpr int kCandLdsRow = 8192;      // candidates the fused work-group keeps in LDS
+constexpr int kSelRangeMax = 4096;     // decode attention: tokens per split whose selection it finishes
+constexpr int kSelMaxWGs = 512;        // ... when that many attention work-groups cover the step
 constexpr int kRowKeysInRegs = 2 * 8 * kRowThreads * 4;   // rows the fused work-group holds whole
 
 inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
@@ -145,6 +147,20 @@ struct AttendParams {
   // sel_page_log2 > 0: the list holds logical pages of 2^sel_page_log2
   // tokens, and position j is token j % 2^s of page list[j >> s]
   int idx_b_stride, idx_kv_stride, sel_page_log2;
+  // decode steps (sel_ctrl != null): this kernel also finishes the top-k. On
+  // a miss, split s owns tokens [s*sel_range, (s+1)*sel_range) of its
+  // sequence: it completes the selection of that range from the partition's
+  // bitmap and threshold-bin candidates, counts the selected tokens before
+  // it, writes its part of the ascending selection into sel_out [B][k] and
+  // attends over it. On a hit (sel_hit[b]) split s reads positions
+  // [s*split, (s+1)*split) of the stored selection, sel_out itself.
+  const uint32_t* sel_ctrl;  // [B][kCtrlStride]
+  const uint32_t* sel_bitmap;
+  const uint2* sel_cand;
+  const float* sel_votes;    // [B][sel_vote_stride]: the row, when the candidates overflowed
+  const int32_t* sel_hit;
+  int32_t* sel_out;
+  int sel_bm_stride, sel_vote_stride, sel_range, sel_k;
   float* pm;                // [B][Hq][nsplit] running max (base 2)
   float* pl;                // [B][Hq][nsplit] sum of exp2
   float* pacc;              // [B][Hq][nsplit][d] weighted value sums
