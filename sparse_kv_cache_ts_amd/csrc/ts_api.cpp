@@ -1001,17 +1001,37 @@ ts_status ts_decode_step(ts_sel_cache* cache, const ts_kv_layout* L, int32_t bat
   hipStream_t st = static_cast<hipStream_t>(stream);
   const int32_t* pt = g.paged ? page_table : nullptr;
 
-  // 1+2. Selection-Cache decision per sequence, then the K-scan on misses
-  // (one kernel: every scoring work-group evaluates its sequence's decision),
+  // 1+2. Selection-Cache decision per sequence, then the K-scan on misses,
   // and the reset of the top-k control blocks
   const int vote_wgs = cdiv(g.max_len, kVoteTile);
   const int copies = hist_copies_for(vote_wgs);
   const int32_t* hit = cache->dev.hit;
-  ScoreParams sp = score_params(g, p.s, batch, ws, q, k_cache, pt, seq_lens, nullptr);
-  sp.cache = cache->dev;
-  sp.theta = theta;
-  sp.ctrl = at<uint32_t>(ws, p.s.ctrl);
-  sp.ctrl_words = ctrl_words_for(copies);
+  // Fused, every K-scan work-group requests its first keys before the
+  // decision is known: free on a miss, wasted on a hit. With a large K-scan
+  // grid (large batches, long rows) those wasted bytes dominate a hit step,
+  // so the decision runs first in a small kernel and the K-scan reads it.
+  const long kscan_wgs = (long)batch * g.nslices * p.s.ntiles;
+  ScoreParams sp;
+  if (kscan_wgs < kFusedDecisionMaxWGs) {
+    sp = score_params(g, p.s, batch, ws, q, k_cache, pt, seq_lens, nullptr);
+    sp.cache = cache->dev;
+    sp.theta = theta;
+    sp.ctrl = at<uint32_t>(ws, p.s.ctrl);
+    sp.ctrl_words = ctrl_words_for(copies);
+  } else {
+    PrologueParams pp{};
+    pp.ctrl = at<uint32_t>(ws, p.s.ctrl);
+    pp.rows = batch;
+    pp.ctrl_words = ctrl_words_for(copies);
+    pp.cache = cache->dev;
+    pp.q = q;
+    pp.dtype = g.dtype;
+    pp.seq_lens = seq_lens;
+    pp.B = batch;
+    pp.theta = theta;
+    TS_LAUNCH_K(kKPrologue, launch_prologue(pp, batch, st), "selection-cache decision");
+    sp = score_params(g, p.s, batch, ws, q, k_cache, pt, seq_lens, hit);
+  }
   TS_LAUNCH_K(kKScore, launch_score_pass1(g.dtype, g.d, g.paged, sp, st), "score pass 1");
   LseParams lp = lse_params(g, p.s, batch, ws, seq_lens, hit);
   TS_LAUNCH_K(kKLse, launch_lse(lp, st), "log-sum-exp");
