@@ -37,7 +37,7 @@ __global__ __launch_bounds__(256) void attend_kernel(AttendParams p) {
   __shared__ uint32_t s_ci[SEL ? kCandLds : 1];
   __shared__ uint32_t s_hist[SEL ? 2048 : 1];
   __shared__ uint32_t s_rw[SEL ? kSelRangeMax / 32 : 1];
-  __shared__ int32_t s_tok[SEL ? kSelRangeMax : 1];
+  __shared__ int32_t s_tok[SEL ? kSelRangeMax : (DENSE ? 1 : kAttendStage)];
   __shared__ uint32_t s_sh[16];
 
   const int split = blockIdx.x;
@@ -137,9 +137,10 @@ __global__ __launch_bounds__(256) void attend_kernel(AttendParams p) {
   auto load_rows = [&](const int (&tok)[UA], uint32_t (&kw)[UA][W], uint32_t (&vw)[UA][W]) {
 #pragma unroll
     for (int u = 0; u < UA; ++u) {
-      if (DENSE || tok[u] >= 0) {
-        // (dense: tok is clamped into the sequence, validity is tracked apart)
-        const size_t row = row_of(DENSE ? tok[u] : tok[u]);
+      {
+        // tok is clamped into the sequence by every caller; validity is
+        // tracked apart, so the loads are unconditional
+        const size_t row = row_of(tok[u]);
         const char* kp = (const char*)p.k + row * ROWB;
         const char* vp = (const char*)p.v + row * ROWB;
 #pragma unroll
@@ -149,9 +150,6 @@ __global__ __launch_bounds__(256) void attend_kernel(AttendParams p) {
           kw[u][4 * c + 0] = a.x; kw[u][4 * c + 1] = a.y; kw[u][4 * c + 2] = a.z; kw[u][4 * c + 3] = a.w;
           vw[u][4 * c + 0] = v.x; vw[u][4 * c + 1] = v.y; vw[u][4 * c + 2] = v.z; vw[u][4 * c + 3] = v.w;
         }
-      } else {
-#pragma unroll
-        for (int w = 0; w < W; ++w) { kw[u][w] = 0u; vw[u][w] = 0u; }
       }
     }
   };
@@ -201,13 +199,11 @@ __global__ __launch_bounds__(256) void attend_kernel(AttendParams p) {
     }
   };
 
-  // token at list position pos (-1: none, or outside the sequence)
+  // token at list position pos of a global list (-1: none, or outside the sequence)
   auto tok_at = [&](int pos) -> int {
     if (pos >= pend) return -1;
     long long t;
-    if (SEL && lds_list) {
-      t = s_tok[pos];
-    } else if (p.sel_page_log2 > 0) {
+    if (p.sel_page_log2 > 0) {
       const int pg = idx[pos >> p.sel_page_log2];
       t = pg < 0 ? -1 : ((long long)pg << p.sel_page_log2) + (pos & ((1 << p.sel_page_log2) - 1));
     } else {
@@ -215,12 +211,6 @@ __global__ __launch_bounds__(256) void attend_kernel(AttendParams p) {
     }
     return (t >= 0 && t < len) ? (int)t : -1;
   };
-  // indices of the first batch (sparse) together with the query slice
-  int tok[UA];
-  if constexpr (!DENSE) {
-#pragma unroll
-    for (int u = 0; u < UA; ++u) tok[u] = tok_at(pbeg + rg + u * RG);
-  }
 #pragma unroll
   for (int hh = 0; hh < GS; ++hh) {
     const int head = kvh * p.G + slice * GS + hh;
@@ -283,18 +273,59 @@ __global__ __launch_bounds__(256) void attend_kernel(AttendParams p) {
     } else if (bi < nb) {
       consume(oA, kA, vA);
     }
-  } else {
-    for (int pos0 = pbeg + rg; pos0 < pend; pos0 += RG * UA) {
-      if (pos0 != pbeg + rg) {
-#pragma unroll
-        for (int u = 0; u < UA; ++u) tok[u] = tok_at(pos0 + u * RG);
+  } else if (len > 0) {
+    // The list's tokens go to LDS first (one round of index loads per chunk
+    // of CAP positions; a decode step's own selection is there already);
+    // then the rows stream through a two-stage pipeline whose loads are
+    // unconditional: an empty slot reads token 0 and is masked.
+    constexpr int CAP = SEL ? kSelRangeMax : kAttendStage;
+    const int n = pend - pbeg;
+    uint32_t kA[UA][W], vA[UA][W], kB[UA][W], vB[UA][W];
+    int tA[UA], tB[UA];
+    bool oA[UA], oB[UA];
+    // a list of one batch is read straight from global memory (staging it
+    // would only add a barrier)
+    const bool direct = !lds_list && n <= RG * UA;
+    for (int c0 = 0; c0 < n; c0 += CAP) {
+      const int cn = min(CAP, n - c0);
+      if (!lds_list && !direct) {
+        __syncthreads();                         // the previous chunk's readers are done
+        for (int i = tid; i < cn; i += 256) s_tok[i] = tok_at(pbeg + c0 + i);
+        __syncthreads();
       }
-      uint32_t kw[UA][W], vw[UA][W];
-      load_rows(tok, kw, vw);
-      bool ok[UA];
+      const int nit = (cn + RG * UA - 1) / (RG * UA);
+      auto toks = [&](int it, int (&t)[UA], bool (&ok)[UA]) {
 #pragma unroll
-      for (int u = 0; u < UA; ++u) ok[u] = tok[u] >= 0;
-      consume(ok, kw, vw);
+        for (int u = 0; u < UA; ++u) {
+          const int q = it * RG * UA + u * RG + rg;
+          const int tt = direct ? tok_at(pbeg + c0 + q) : s_tok[min(q, cn - 1)];
+          ok[u] = q < cn && tt >= 0 && tt < len;
+          t[u] = ok[u] ? tt : 0;
+        }
+      };
+      toks(0, tA, oA);
+      load_rows(tA, kA, vA);
+      int it = 0;
+      for (; it + 2 < nit; it += 2) {
+        toks(it + 1, tB, oB);
+        load_rows(tB, kB, vB);
+        __builtin_amdgcn_sched_barrier(0);
+        consume(oA, kA, vA);
+        __builtin_amdgcn_sched_barrier(0);
+        toks(it + 2, tA, oA);
+        load_rows(tA, kA, vA);
+        __builtin_amdgcn_sched_barrier(0);
+        consume(oB, kB, vB);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      if (it + 1 < nit) {
+        toks(it + 1, tB, oB);
+        load_rows(tB, kB, vB);
+        consume(oA, kA, vA);
+        consume(oB, kB, vB);
+      } else {
+        consume(oA, kA, vA);
+      }
     }
   }
 

@@ -51,6 +51,7 @@ constexpr int kRowThreads = 1024;  // fused top-k: one work-group per row of <= 
 constexpr int kRowKernelMinRows = 256; // fewer rows: partition + finalize (more CUs per row)
 constexpr int kCandLdsRow = 8192;      // candidates the fused work-group keeps in LDS
 constexpr int kSelRangeMax = 4096;     // decode attention: tokens per split whose selection it finishes
+constexpr int kAttendStage = 1024;     // sparse attention: list positions staged in LDS at a time
 constexpr int kSelMaxWGs = 512;        // ... when that many attention work-groups cover the step
 constexpr int kFusedDecisionMaxWGs = 1024;  // K-scan grids this large take the decision in its own kernel
 constexpr int kRowKeysInRegs = 2 * 8 * kRowThreads * 4;   // rows the fused work-group holds whole
