@@ -393,6 +393,22 @@ __global__ __launch_bounds__(128) void combine_kernel(CombineParams p) {
   float a[SB];
 #pragma unroll
   for (int s = 0; s < SB; ++s) a[s] = (own_d && s < ns) ? pa[(size_t)s * p.d] : 0.f;
+  // the cache update's inputs (decision, query element, first selection
+  // entry of this head's share) are requested now, not after the merge
+  const bool upd = p.cache.prev_q != nullptr;
+  const int ck = upd ? p.cache.k : 0;
+  const int per = upd ? (ck + p.Hq - 1) / p.Hq : 0;
+  const int lo = h * per, hi = min(ck, lo + per);
+  int hit = 0;
+  uint32_t qbits = 0;
+  int32_t sel0 = 0;
+  if (upd) {
+    hit = p.cache.hit[b];
+    const size_t qo = ((size_t)b * p.Hq + h) * p.d + min(tid, p.d - 1);
+    qbits = p.dtype == 1 ? (uint32_t)((const uint16_t*)p.q)[qo] << 16
+                         : __float_as_uint(((const float*)p.q)[qo]);
+    if (p.idx_out && lo + tid < hi) sel0 = p.cache.sel[(size_t)b * ck + lo + tid];
+  }
   float pmv = -INFINITY, plv = 0.f;
   if (tid < ns) {
     pmv = p.pm[base + tid];
@@ -450,24 +466,17 @@ __global__ __launch_bounds__(128) void combine_kernel(CombineParams p) {
   if (own_d) p.out[((size_t)b * p.Hq + h) * p.d + tid] = (L > 0.f) ? ((o0 + o1) + (o2 + o3)) / L : 0.f;
 
   // Selection-Cache state update, spread over the head blocks of a sequence
-  if (p.cache.prev_q == nullptr) return;
+  if (!upd) return;
   const SelCacheDev& c = p.cache;
-  const int hit = c.hit[b];
   const int n = c.Hq * c.d;
   if (c.mode == 0 || !hit) {
     float* pq = c.prev_q + (size_t)b * n + (size_t)h * c.d;
-    for (int i = tid; i < c.d; i += 128) {
-      if (p.dtype == 1)
-        pq[i] = __uint_as_float((uint32_t)((const uint16_t*)p.q)[(size_t)b * n + (size_t)h * c.d + i] << 16);
-      else
-        pq[i] = ((const float*)p.q)[(size_t)b * n + (size_t)h * c.d + i];
-    }
+    if (own_d) pq[tid] = __uint_as_float(qbits);
   }
   if (p.idx_out) {
-    const int per = (c.k + p.Hq - 1) / p.Hq;
-    const int lo = h * per, hi = min(c.k, lo + per);
     const int32_t* sel = c.sel + (size_t)b * c.k;
-    for (int i = lo + tid; i < hi; i += 128) p.idx_out[(size_t)b * c.k + i] = sel[i];
+    if (lo + tid < hi) p.idx_out[(size_t)b * c.k + lo + tid] = sel0;
+    for (int i = lo + tid + 128; i < hi; i += 128) p.idx_out[(size_t)b * c.k + i] = sel[i];
   }
   if (h == 0 && tid == 0) {
     c.valid[b] = p.seq_lens[b] > 0 ? 1 : 0;
