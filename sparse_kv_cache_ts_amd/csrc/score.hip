@@ -159,6 +159,16 @@ __global__ __launch_bounds__(256) void score_pass1_kernel(ScoreParams p) {
   // full tiles with every row group busy need no per-row guards
   const bool full = (tl == TILE) && (TPI * Hkv == RG) && (TILE % (TPI * U) == 0);
 
+  // rows u0 .. u1-1 of a full batch (no guards)
+  auto load_part = [&](int i0, uint4 (&kc)[U][CPL], int u0, int u1) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      if (u < u0 || u >= u1) continue;
+      const char* rp = row_ptr(toff + (i0 + u) * TPI) + j * 16;
+#pragma unroll
+      for (int c = 0; c < CPL; ++c) kc[u][c] = ld16_nt(rp + c * 16 * LPR);
+    }
+  };
   auto load_batch = [&](int i0, uint4 (&kc)[U][CPL], bool guard) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
@@ -173,8 +183,12 @@ __global__ __launch_bounds__(256) void score_pass1_kernel(ScoreParams p) {
     }
   };
 
+  // Half of the first batch is requested before the Selection-Cache
+  // decision, the rest after it: on a hit the wasted reads are halved, and on
+  // a miss the decision's own few bytes queue behind fewer keys (measured:
+  // both steps faster than with the whole batch first)
   uint4 bufA[U][CPL], bufB[U][CPL];
-  if (full) load_batch(0, bufA, false);
+  if (full) load_part(0, bufA, 0, U / 2);
   else if (n_iter > 0) load_batch(0, bufA, true);
 
   // query slice of this lane's KV-head group, slot s holding head s ^ f(j)
@@ -203,6 +217,7 @@ __global__ __launch_bounds__(256) void score_pass1_kernel(ScoreParams p) {
     if (tile == 0 && slice == 0 && tid == 0) { p.cache.hit[b] = h; p.cache.cos[b] = cs; }
     if (h) return;
   }
+  if (full) load_part(0, bufA, U / 2, U);
   const float scale2 = p.scale2;
   // logits are staged in LDS and written to HBM once per tile, so the loop
   // issues no global stores: every wait on the vector-memory counter is then a
