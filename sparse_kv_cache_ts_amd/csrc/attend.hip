@@ -6,13 +6,18 @@
 // V[j]; one selection is shared by every head of the sequence.
 //
 // attend_kernel: one work-group per (split of the index list, KV head,
-// sequence). A row group of LPR lanes gathers one selected token's K row and V
-// row (16-byte loads), computes the dot products of the GS query heads of that
-// KV head (v_dot2c_f32_bf16 for bf16), combines them with DPP, and keeps an
-// online softmax (running max, sum and weighted V in fp32, base 2). Row groups
-// are merged through LDS in a fixed order, and each (sequence, head, split)
-// leaves (max, sum, acc[d]). combine_kernel merges the splits by their
-// log-sum-exp and, in a decode step, also updates the Selection-Cache state.
+// sequence), with an online softmax in fp32, base 2, and (max, sum, acc[d])
+// left per (sequence, head, split).
+//  * bf16 index lists: the GS query heads of a KV head share every gathered
+//    row, so the scores of a 64-token chunk are one small matrix product
+//    (16 tokens x 16 padded heads per wave on v_mfma_f32_16x16x32_bf16); the
+//    weights and V rows go through LDS and the weighted sum is taken on the
+//    vector units, each (head, dimension pair) owned by one thread.
+//  * fp32 rows and dense ranges: a row group of LPR lanes gathers one token's
+//    K and V rows (16-byte loads), takes the GS dot products and combines
+//    them with DPP; row groups are merged through LDS in a fixed order.
+// combine_kernel merges the splits by their log-sum-exp and, in a decode
+// step, also updates the Selection-Cache state.
 #include "topk_device.h"
 
 namespace ts {
@@ -28,10 +33,18 @@ __global__ __launch_bounds__(256) void attend_kernel(AttendParams p) {
   constexpr int W = 4 * CPL;                               // 32-bit words per lane
   constexpr int UA = 4;                                    // rows in flight per row group
   constexpr int RG = 256 / LPR;
+  // bf16 lists take the matrix-core path below; fp32 and dense ranges the
+  // row-group path
+  constexpr bool MF = DT == 1 && !DENSE;
+  constexpr int kVRow = D / 2 + 4;     // words per LDS row of V (padded: no bank conflicts)
+  constexpr int kPRow = 17;            // weights per LDS token row (16 heads, padded)
 
-  __shared__ float s_m[4][GS];
-  __shared__ float s_l[4][GS];
-  __shared__ float s_acc[4 * GS * D];
+  __shared__ float s_m[4][MF ? 1 : GS];
+  __shared__ float s_l[4][MF ? 1 : GS];
+  __shared__ float s_acc[MF ? 1 : 4 * GS * D];
+  __shared__ __align__(16) uint32_t s_v[MF ? 64 * kVRow : 1];
+  __shared__ float s_p[MF ? 64 * kPRow : 1];
+  __shared__ float s_wm[MF ? 64 : 1];
   // decode steps: the end of the top-k for this split's token range
   __shared__ uint32_t s_ck[SEL ? kCandLds : 1];
   __shared__ uint32_t s_ci[SEL ? kCandLds : 1];
@@ -211,167 +224,320 @@ __global__ __launch_bounds__(256) void attend_kernel(AttendParams p) {
     }
     return (t >= 0 && t < len) ? (int)t : -1;
   };
+  if constexpr (MF) {
+    // ---- bf16 lists. Each wave takes 16 tokens of a 64-token chunk (lane l:
+    // token l%16, dimensions 32s + 8*(l/16) .. +7 of its K and V rows, one
+    // 16-byte load per k-step). The matrix cores give S^T = K_tile * Q^T for
+    // the slice's heads padded to 16 (lane l: tokens 4*(l/16) .. +3, head
+    // l%16); the chunk's max per head and the weights 2^(s - M) go through
+    // LDS together with the V rows, and the weighted V sum runs on the vector
+    // units with every (head, dimension pair) owned by one thread, so no
+    // cross-lane merge is left at the end.
+    constexpr int KS = D / 32;                 // k-steps of 32 dimensions
+    constexpr int NSLOT = 256 / (D / 2);       // head slots of the weighted sum
+    constexpr int HPS = (GS + NSLOT - 1) / NSLOT;
+    const int tl = lane & 15, g4 = lane >> 4;
+    const int dp = tid % (D / 2), slot = tid / (D / 2);
+    uint4 qf[KS];
+    {
+      const int head = kvh * p.G + slice * GS + min(tl, GS - 1);
+      const char* qb = (const char*)p.q + ((size_t)b * p.Hq + head) * ROWB + g4 * 16;
 #pragma unroll
-  for (int hh = 0; hh < GS; ++hh) {
-    const int head = kvh * p.G + slice * GS + hh;
-    const char* qb = (const char*)p.q + ((size_t)b * p.Hq + head) * ROWB;
-#pragma unroll
-    for (int c = 0; c < CPL; ++c) {
-      const uint4 v = ld16(qb + (c * LPR + j) * 16);
-      qw[hh][4 * c + 0] = v.x; qw[hh][4 * c + 1] = v.y;
-      qw[hh][4 * c + 2] = v.z; qw[hh][4 * c + 3] = v.w;
+      for (int s = 0; s < KS; ++s) {
+        const uint4 v = ld16(qb + s * 64);
+        qf[s] = tl < GS ? v : make_uint4(0u, 0u, 0u, 0u);
+      }
     }
-  }
+    float Mc = -INFINITY;                      // running max of head tl
+    float Mp[HPS], Lp[HPS], A0[HPS], A1[HPS];  // per owned head: max, sum, two dims
 #pragma unroll
-  for (int hh = 0; hh < GS; ++hh) {
-    m[hh] = -INFINITY;
-    l[hh] = 0.f;
+    for (int jh = 0; jh < HPS; ++jh) {
+      Mp[jh] = -INFINITY;
+      Lp[jh] = 0.f;
+      A0[jh] = 0.f;
+      A1[jh] = 0.f;
+    }
+    if (len > 0) {
+      constexpr int CAP = SEL ? kSelRangeMax : kAttendStage;
+      const int n = pend - pbeg;
+      const bool direct = !lds_list && n <= 64;
+      for (int c0 = 0; c0 < n; c0 += CAP) {
+        const int cn = min(CAP, n - c0);
+        if (!lds_list && !direct) {
+          __syncthreads();                     // the previous chunk's readers are done
+          for (int i = tid; i < cn; i += 256) s_tok[i] = tok_at(pbeg + c0 + i);
+          __syncthreads();
+        }
+        const int nit = (cn + 63) / 64;
+        // this lane's row of chunk it (an empty slot reads token 0, masked)
+        auto tok = [&](int it, bool& ok) -> int {
+          const int q = it * 64 + 16 * wv + tl;
+          const int tt = direct ? tok_at(pbeg + c0 + q) : s_tok[min(q, cn - 1)];
+          ok = q < cn && tt >= 0 && tt < len;
+          return ok ? tt : 0;
+        };
+        auto load = [&](int t, uint4 (&kf)[KS], uint4 (&vf)[KS]) {
+          const size_t row = row_of(t);
+          const char* kp = (const char*)p.k + row * ROWB + g4 * 16;
+          const char* vp = (const char*)p.v + row * ROWB + g4 * 16;
 #pragma unroll
-    for (int e = 0; e < EPL; ++e) acc[hh][e] = 0.f;
-  }
+          for (int s = 0; s < KS; ++s) {
+            kf[s] = ld16(kp + s * 64);
+            vf[s] = ld16(vp + s * 64);
+          }
+        };
+        auto chunk = [&](int it, bool ok, const uint4 (&kf)[KS], const uint4 (&vf)[KS]) {
+          f32x4_t sc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int s = 0; s < KS; ++s) sc = mfma16(as_bf8(kf[s]), as_bf8(qf[s]), sc);
+          const uint64_t okm = __ballot(ok);   // bit t < 16: token t of the wave is valid
+          float sv[4], mx = -INFINITY;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const bool v = (okm >> (4 * g4 + i)) & 1u;
+            sv[i] = v ? sc[i] * p.scale2 : -INFINITY;
+            mx = fmaxf(mx, sv[i]);
+          }
+          mx = xor_max<32>(xor_max<16>(mx));
+          uint32_t* vr = s_v + (16 * wv + tl) * kVRow + g4 * 4;
+#pragma unroll
+          for (int s = 0; s < KS; ++s) *reinterpret_cast<uint4*>(vr + s * 16) = vf[s];
+          if (g4 == 0) s_wm[wv * 16 + tl] = mx;
+          __syncthreads();
+          const float cm = fmaxf(fmaxf(s_wm[tl], s_wm[16 + tl]), fmaxf(s_wm[32 + tl], s_wm[48 + tl]));
+          Mc = fmaxf(Mc, cm);
+          if (tl < GS) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+              s_p[(16 * wv + 4 * g4 + i) * kPRow + tl] = sv[i] == -INFINITY ? 0.f : ex2(sv[i] - Mc);
+          }
+#pragma unroll
+          for (int jh = 0; jh < HPS; ++jh) {
+            const int h = min(slot + jh * NSLOT, 15);
+            const float cmh = fmaxf(fmaxf(s_wm[h], s_wm[16 + h]), fmaxf(s_wm[32 + h], s_wm[48 + h]));
+            const float mn = fmaxf(Mp[jh], cmh);
+            const float corr = mn == -INFINITY ? 1.f : ex2(Mp[jh] - mn);
+            Mp[jh] = mn;
+            A0[jh] *= corr;
+            A1[jh] *= corr;
+            Lp[jh] *= corr;
+          }
+          __syncthreads();
+          const int ncnt = min(64, cn - it * 64);
+#pragma unroll 4
+          for (int t = 0; t < ncnt; ++t) {
+            const uint32_t w = s_v[t * kVRow + dp];
+            const float v0 = bf16_lo(w), v1 = bf16_hi(w);
+#pragma unroll
+            for (int jh = 0; jh < HPS; ++jh) {
+              const float pw = s_p[t * kPRow + min(slot + jh * NSLOT, 15)];
+              A0[jh] = fmaf(pw, v0, A0[jh]);
+              A1[jh] = fmaf(pw, v1, A1[jh]);
+              Lp[jh] += pw;
+            }
+          }
+          // the next chunk's V rows and weights overwrite these
+          if (it + 1 < nit || c0 + CAP < n) __syncthreads();
+        };
+        uint4 kA[KS], vA[KS], kB[KS], vB[KS];
+        bool okA, okB;
+        load(tok(0, okA), kA, vA);
+        int it = 0;
+        for (; it + 2 < nit; it += 2) {
+          load(tok(it + 1, okB), kB, vB);
+          __builtin_amdgcn_sched_barrier(0);
+          chunk(it, okA, kA, vA);
+          __builtin_amdgcn_sched_barrier(0);
+          load(tok(it + 2, okA), kA, vA);
+          __builtin_amdgcn_sched_barrier(0);
+          chunk(it + 1, okB, kB, vB);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+        if (it + 1 < nit) {
+          load(tok(it + 1, okB), kB, vB);
+          chunk(it, okA, kA, vA);
+          chunk(it + 1, okB, kB, vB);
+        } else {
+          chunk(it, okA, kA, vA);
+        }
+      }
+    }
+#pragma unroll
+    for (int jh = 0; jh < HPS; ++jh) {
+      const int h = slot + jh * NSLOT;
+      if (h < GS) {
+        const int head = kvh * p.G + slice * GS + h;
+        const size_t o = ((size_t)b * p.Hq + head) * p.nsplit + split;
+        *reinterpret_cast<float2*>(p.pacc + o * D + 2 * dp) = make_float2(A0[jh], A1[jh]);
+        if (dp == 0) {
+          p.pm[o] = Mp[jh];
+          p.pl[o] = Lp[jh];
+        }
+      }
+    }
+  } else {
+#pragma unroll
+    for (int hh = 0; hh < GS; ++hh) {
+      const int head = kvh * p.G + slice * GS + hh;
+      const char* qb = (const char*)p.q + ((size_t)b * p.Hq + head) * ROWB;
+#pragma unroll
+      for (int c = 0; c < CPL; ++c) {
+        const uint4 v = ld16(qb + (c * LPR + j) * 16);
+        qw[hh][4 * c + 0] = v.x; qw[hh][4 * c + 1] = v.y;
+        qw[hh][4 * c + 2] = v.z; qw[hh][4 * c + 3] = v.w;
+      }
+    }
+#pragma unroll
+    for (int hh = 0; hh < GS; ++hh) {
+      m[hh] = -INFINITY;
+      l[hh] = 0.f;
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) acc[hh][e] = 0.f;
+    }
 
-  if constexpr (DENSE) {
-    // contiguous token range [pbeg, pe): batches of RG*UA rows, the next
-    // batch in flight while one is consumed; rows past the end are clamped
-    // to the last token (in bounds) and masked, so every load is
-    // unconditional and the compiler can count them
-    const int pe = min(pend, len);
-    const int nb = pe > pbeg ? (pe - pbeg + RG * UA - 1) / (RG * UA) : 0;
-    uint32_t kA[UA][W], vA[UA][W], kB[UA][W], vB[UA][W];
-    auto batch = [&](int bi, int (&t)[UA], bool (&ok)[UA]) {
-#pragma unroll
-      for (int u = 0; u < UA; ++u) {
-        const int pos = pbeg + bi * RG * UA + u * RG + rg;
-        ok[u] = pos < pe;
-        t[u] = min(pos, pe - 1);
-      }
-    };
-    int tA[UA], tB[UA];
-    bool oA[UA], oB[UA];
-    if (nb > 0) {
-      batch(0, tA, oA);
-      load_rows(tA, kA, vA);
-    }
-    int bi = 0;
-    for (; bi + 2 < nb; bi += 2) {
-      batch(bi + 1, tB, oB);
-      load_rows(tB, kB, vB);
-      __builtin_amdgcn_sched_barrier(0);
-      consume(oA, kA, vA);
-      __builtin_amdgcn_sched_barrier(0);
-      batch(bi + 2, tA, oA);
-      load_rows(tA, kA, vA);
-      __builtin_amdgcn_sched_barrier(0);
-      consume(oB, kB, vB);
-      __builtin_amdgcn_sched_barrier(0);
-    }
-    if (bi + 1 < nb) {
-      batch(bi + 1, tB, oB);
-      load_rows(tB, kB, vB);
-      consume(oA, kA, vA);
-      consume(oB, kB, vB);
-    } else if (bi < nb) {
-      consume(oA, kA, vA);
-    }
-  } else if (len > 0) {
-    // The list's tokens go to LDS first (one round of index loads per chunk
-    // of CAP positions; a decode step's own selection is there already);
-    // then the rows stream through a two-stage pipeline whose loads are
-    // unconditional: an empty slot reads token 0 and is masked.
-    constexpr int CAP = SEL ? kSelRangeMax : kAttendStage;
-    const int n = pend - pbeg;
-    uint32_t kA[UA][W], vA[UA][W], kB[UA][W], vB[UA][W];
-    int tA[UA], tB[UA];
-    bool oA[UA], oB[UA];
-    // a list of one batch is read straight from global memory (staging it
-    // would only add a barrier)
-    const bool direct = !lds_list && n <= RG * UA;
-    for (int c0 = 0; c0 < n; c0 += CAP) {
-      const int cn = min(CAP, n - c0);
-      if (!lds_list && !direct) {
-        __syncthreads();                         // the previous chunk's readers are done
-        for (int i = tid; i < cn; i += 256) s_tok[i] = tok_at(pbeg + c0 + i);
-        __syncthreads();
-      }
-      const int nit = (cn + RG * UA - 1) / (RG * UA);
-      auto toks = [&](int it, int (&t)[UA], bool (&ok)[UA]) {
+    if constexpr (DENSE) {
+      // contiguous token range [pbeg, pe): batches of RG*UA rows, the next
+      // batch in flight while one is consumed; rows past the end are clamped
+      // to the last token (in bounds) and masked, so every load is
+      // unconditional and the compiler can count them
+      const int pe = min(pend, len);
+      const int nb = pe > pbeg ? (pe - pbeg + RG * UA - 1) / (RG * UA) : 0;
+      uint32_t kA[UA][W], vA[UA][W], kB[UA][W], vB[UA][W];
+      auto batch = [&](int bi, int (&t)[UA], bool (&ok)[UA]) {
 #pragma unroll
         for (int u = 0; u < UA; ++u) {
-          const int q = it * RG * UA + u * RG + rg;
-          const int tt = direct ? tok_at(pbeg + c0 + q) : s_tok[min(q, cn - 1)];
-          ok[u] = q < cn && tt >= 0 && tt < len;
-          t[u] = ok[u] ? tt : 0;
+          const int pos = pbeg + bi * RG * UA + u * RG + rg;
+          ok[u] = pos < pe;
+          t[u] = min(pos, pe - 1);
         }
       };
-      toks(0, tA, oA);
-      load_rows(tA, kA, vA);
-      int it = 0;
-      for (; it + 2 < nit; it += 2) {
-        toks(it + 1, tB, oB);
+      int tA[UA], tB[UA];
+      bool oA[UA], oB[UA];
+      if (nb > 0) {
+        batch(0, tA, oA);
+        load_rows(tA, kA, vA);
+      }
+      int bi = 0;
+      for (; bi + 2 < nb; bi += 2) {
+        batch(bi + 1, tB, oB);
         load_rows(tB, kB, vB);
         __builtin_amdgcn_sched_barrier(0);
         consume(oA, kA, vA);
         __builtin_amdgcn_sched_barrier(0);
-        toks(it + 2, tA, oA);
+        batch(bi + 2, tA, oA);
         load_rows(tA, kA, vA);
         __builtin_amdgcn_sched_barrier(0);
         consume(oB, kB, vB);
         __builtin_amdgcn_sched_barrier(0);
       }
-      if (it + 1 < nit) {
-        toks(it + 1, tB, oB);
+      if (bi + 1 < nb) {
+        batch(bi + 1, tB, oB);
         load_rows(tB, kB, vB);
         consume(oA, kA, vA);
         consume(oB, kB, vB);
-      } else {
+      } else if (bi < nb) {
         consume(oA, kA, vA);
       }
+    } else if (len > 0) {
+      // The list's tokens go to LDS first (one round of index loads per chunk
+      // of CAP positions; a decode step's own selection is there already);
+      // then the rows stream through a two-stage pipeline whose loads are
+      // unconditional: an empty slot reads token 0 and is masked.
+      constexpr int CAP = SEL ? kSelRangeMax : kAttendStage;
+      const int n = pend - pbeg;
+      uint32_t kA[UA][W], vA[UA][W], kB[UA][W], vB[UA][W];
+      int tA[UA], tB[UA];
+      bool oA[UA], oB[UA];
+      // a list of one batch is read straight from global memory (staging it
+      // would only add a barrier)
+      const bool direct = !lds_list && n <= RG * UA;
+      for (int c0 = 0; c0 < n; c0 += CAP) {
+        const int cn = min(CAP, n - c0);
+        if (!lds_list && !direct) {
+          __syncthreads();                         // the previous chunk's readers are done
+          for (int i = tid; i < cn; i += 256) s_tok[i] = tok_at(pbeg + c0 + i);
+          __syncthreads();
+        }
+        const int nit = (cn + RG * UA - 1) / (RG * UA);
+        auto toks = [&](int it, int (&t)[UA], bool (&ok)[UA]) {
+#pragma unroll
+          for (int u = 0; u < UA; ++u) {
+            const int q = it * RG * UA + u * RG + rg;
+            const int tt = direct ? tok_at(pbeg + c0 + q) : s_tok[min(q, cn - 1)];
+            ok[u] = q < cn && tt >= 0 && tt < len;
+            t[u] = ok[u] ? tt : 0;
+          }
+        };
+        toks(0, tA, oA);
+        load_rows(tA, kA, vA);
+        int it = 0;
+        for (; it + 2 < nit; it += 2) {
+          toks(it + 1, tB, oB);
+          load_rows(tB, kB, vB);
+          __builtin_amdgcn_sched_barrier(0);
+          consume(oA, kA, vA);
+          __builtin_amdgcn_sched_barrier(0);
+          toks(it + 2, tA, oA);
+          load_rows(tA, kA, vA);
+          __builtin_amdgcn_sched_barrier(0);
+          consume(oB, kB, vB);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+        if (it + 1 < nit) {
+          toks(it + 1, tB, oB);
+          load_rows(tB, kB, vB);
+          consume(oA, kA, vA);
+          consume(oB, kB, vB);
+        } else {
+          consume(oA, kA, vA);
+        }
+      }
     }
-  }
 
-  // merge the row groups (fixed order: deterministic): the common max and the
-  // sums over a wave's row groups by lane swaps, over the 4 waves in LDS
+    // merge the row groups (fixed order: deterministic): the common max and the
+    // sums over a wave's row groups by lane swaps, over the 4 waves in LDS
 #pragma unroll
-  for (int hh = 0; hh < GS; ++hh) {
-    float mw = m[hh];
-    if constexpr (LPR <= 8) mw = xor_max<8>(mw);
-    mw = xor_max<32>(xor_max<16>(mw));
-    if (lane == 0) s_m[wv][hh] = mw;
-  }
-  __syncthreads();
-#pragma unroll
-  for (int hh = 0; hh < GS; ++hh) {
-    const float M = fmaxf(fmaxf(s_m[0][hh], s_m[1][hh]), fmaxf(s_m[2][hh], s_m[3][hh]));
-    const float f = (l[hh] > 0.f) ? ex2(m[hh] - M) : 0.f;
-    float lw = l[hh] * f;
-    if constexpr (LPR <= 8) lw = xor_sum<8>(lw);
-    lw = xor_sum<32>(xor_sum<16>(lw));
-#pragma unroll
-    for (int e = 0; e < EPL; ++e) {
-      float v = acc[hh][e] * f;
-      if constexpr (LPR <= 8) v = xor_sum<8>(v);
-      acc[hh][e] = xor_sum<32>(xor_sum<16>(v));
+    for (int hh = 0; hh < GS; ++hh) {
+      float mw = m[hh];
+      if constexpr (LPR <= 8) mw = xor_max<8>(mw);
+      mw = xor_max<32>(xor_max<16>(mw));
+      if (lane == 0) s_m[wv][hh] = mw;
     }
-    if (lane < LPR) {
+    __syncthreads();
 #pragma unroll
-      for (int c = 0; c < CPL; ++c)
+    for (int hh = 0; hh < GS; ++hh) {
+      const float M = fmaxf(fmaxf(s_m[0][hh], s_m[1][hh]), fmaxf(s_m[2][hh], s_m[3][hh]));
+      const float f = (l[hh] > 0.f) ? ex2(m[hh] - M) : 0.f;
+      float lw = l[hh] * f;
+      if constexpr (LPR <= 8) lw = xor_sum<8>(lw);
+      lw = xor_sum<32>(xor_sum<16>(lw));
 #pragma unroll
-        for (int e = 0; e < EPC; ++e)
-          s_acc[(wv * GS + hh) * D + (c * LPR + j) * EPC + e] = acc[hh][c * EPC + e];
+      for (int e = 0; e < EPL; ++e) {
+        float v = acc[hh][e] * f;
+        if constexpr (LPR <= 8) v = xor_sum<8>(v);
+        acc[hh][e] = xor_sum<32>(xor_sum<16>(v));
+      }
+      if (lane < LPR) {
+#pragma unroll
+        for (int c = 0; c < CPL; ++c)
+#pragma unroll
+          for (int e = 0; e < EPC; ++e)
+            s_acc[(wv * GS + hh) * D + (c * LPR + j) * EPC + e] = acc[hh][c * EPC + e];
+      }
+      if (lane == 0) s_l[wv][hh] = lw;
     }
-    if (lane == 0) s_l[wv][hh] = lw;
-  }
-  __syncthreads();
-  for (int i = tid; i < GS * D; i += 256) {
-    const int hh = i / D, d = i - hh * D;
-    const float sum = (s_acc[(0 * GS + hh) * D + d] + s_acc[(1 * GS + hh) * D + d]) +
-                      (s_acc[(2 * GS + hh) * D + d] + s_acc[(3 * GS + hh) * D + d]);
-    const int head = kvh * p.G + slice * GS + hh;
-    const size_t o = ((size_t)b * p.Hq + head) * p.nsplit + split;
-    p.pacc[o * D + d] = sum;
-    if (d == 0) {
-      p.pm[o] = fmaxf(fmaxf(s_m[0][hh], s_m[1][hh]), fmaxf(s_m[2][hh], s_m[3][hh]));
-      p.pl[o] = (s_l[0][hh] + s_l[1][hh]) + (s_l[2][hh] + s_l[3][hh]);
+    __syncthreads();
+    for (int i = tid; i < GS * D; i += 256) {
+      const int hh = i / D, d = i - hh * D;
+      const float sum = (s_acc[(0 * GS + hh) * D + d] + s_acc[(1 * GS + hh) * D + d]) +
+                        (s_acc[(2 * GS + hh) * D + d] + s_acc[(3 * GS + hh) * D + d]);
+      const int head = kvh * p.G + slice * GS + hh;
+      const size_t o = ((size_t)b * p.Hq + head) * p.nsplit + split;
+      p.pacc[o * D + d] = sum;
+      if (d == 0) {
+        p.pm[o] = fmaxf(fmaxf(s_m[0][hh], s_m[1][hh]), fmaxf(s_m[2][hh], s_m[3][hh]));
+        p.pl[o] = (s_l[0][hh] + s_l[1][hh]) + (s_l[2][hh] + s_l[3][hh]);
+      }
     }
   }
 }

@@ -28,15 +28,6 @@
 
 namespace ts {
 
-typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
-typedef float f32x4_t __attribute__((ext_vector_type(4)));
-
-__device__ __forceinline__ bf16x8_t as_bf8(uint4 v) { return __builtin_bit_cast(bf16x8_t, v); }
-
-__device__ __forceinline__ f32x4_t mfma16(bf16x8_t a, bf16x8_t b, f32x4_t c) {
-  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
-}
-
 // Work-group b runs on XCD b % 8. Renumber so that each XCD gets a contiguous
 // range of flat ids; flat ids that share a KV head's key range are adjacent,
 // so the keys they all read are fetched into one XCD's L2 once.

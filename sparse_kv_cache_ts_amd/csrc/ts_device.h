@@ -22,6 +22,16 @@ __device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float acc) {
                                          __builtin_bit_cast(bf16x2_t, b), acc, false);
 }
 
+// v_mfma_f32_16x16x32_bf16 on 16-byte fragments. Lane l of a wave holds row
+// l%16 of A and column l%16 of B, eight consecutive k (8*(l/16) .. +7) of
+// each, and rows 4*(l/16) .. +3 of column l%16 of the fp32 result.
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ bf16x8_t as_bf8(uint4 v) { return __builtin_bit_cast(bf16x8_t, v); }
+__device__ __forceinline__ f32x4_t mfma16(bf16x8_t a, bf16x8_t b, f32x4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
 // 2^x with the hardware v_exp_f32 alone: results below 2^-126 flush to zero.
 // Used only on non-positive log-ratios whose exponentials are summed, where
 // such terms are negligible against the sum's 1-ulp rounding.
