@@ -48,7 +48,7 @@ __global__ __launch_bounds__(256) void attend_kernel(AttendParams p) {
   // decode steps: the end of the top-k for this split's token range
   __shared__ uint32_t s_ck[SEL ? kCandLds : 1];
   __shared__ uint32_t s_ci[SEL ? kCandLds : 1];
-  __shared__ uint32_t s_hist[SEL ? 2048 : 1];
+  __shared__ __align__(16) uint32_t s_hist[SEL ? 2048 : 1];
   __shared__ uint32_t s_rw[SEL ? kSelRangeMax / 32 : 1];
   __shared__ int32_t s_tok[SEL ? kSelRangeMax : (DENSE ? 1 : kAttendStage)];
   __shared__ uint32_t s_sh[16];
@@ -73,8 +73,9 @@ __global__ __launch_bounds__(256) void attend_kernel(AttendParams p) {
     if (!p.sel_hit[b]) {
       // ---- the selection of tokens [r0, r1): the partition kernel set the
       // bits of every key above the k-th key's histogram bin b0 (or of the
-      // whole bin) and listed the keys inside b0; the threshold inside b0 is
-      // found again here (every work-group of the sequence gets the same one)
+      // whole bin), listed the keys inside b0 and counted them by key bits
+      // 19..10; the threshold inside b0 is found again here (every
+      // work-group of the sequence gets the same one)
       const int k = p.sel_k;
       const int k_eff = min(k, len);
       const int r0 = split * p.sel_range;
@@ -86,6 +87,8 @@ __global__ __launch_bounds__(256) void attend_kernel(AttendParams p) {
       uint2 cv[kCandLds / 256];
 #pragma unroll
       for (int i = 0; i < kCandLds / 256; ++i) cv[i] = cand[i * 256 + tid];  // stale past C: unused
+      // the partition kernel's histogram of key bits 19..10 over bin b0
+      const uint4 hb = ld16(ctrl + kCtlHistB + 4 * tid);
       const int w0 = r0 >> 5, wr = (r1 - r0 + 31) >> 5;
       uint32_t rw = tid < wr ? bm[w0 + tid] : 0u;
       // selected base bits before the range (16-byte loads, clamped, masked)
@@ -101,11 +104,12 @@ __global__ __launch_bounds__(256) void attend_kernel(AttendParams p) {
         s_ci[i * 256 + tid] = cv[i].y;
       }
       if (tid < wr) s_rw[tid] = rw;
+      *reinterpret_cast<uint4*>(s_hist + 4 * tid) = hb;
       __syncthreads();
       if (need > 0 && k_eff > 0) {
         const float* vrow = p.sel_votes + (size_t)b * p.sel_vote_stride;
         auto visit = [&](const auto& L) {
-          const BinThreshold th = find_threshold<256>(L, b0, need, s_hist, s_sh);
+          const BinThreshold th = find_threshold<256, true>(L, b0, need, s_hist, s_sh);
           for (int i = tid; i < L.size(); i += 256) {
             const uint2 e = L.get(i);
             if (th.take(e)) {

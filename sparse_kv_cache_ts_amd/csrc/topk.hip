@@ -159,8 +159,10 @@ __global__ __launch_bounds__(256) void topk_partition_kernel(TopkParams p) {
   for (int i = 0; i < PER; ++i) {
     const int e = start + i * 256 + tid;
     if ((e < len) & bb.at_least(v[i]) & !bb.above(v[i])) {
-      if (pos < (uint32_t)kCandCap) cand[pos] = make_uint2(float_key(v[i]), (uint32_t)e);
+      const uint32_t key = float_key(v[i]);
+      if (pos < (uint32_t)kCandCap) cand[pos] = make_uint2(key, (uint32_t)e);
       ++pos;
+      atomicAdd(ctrl + kCtlHistB + ((key >> 10) & 1023u), 1u);
     }
   }
 }

@@ -62,25 +62,71 @@ struct BinThreshold {
   }
 };
 
-// Exact radix search of that rule over a (key, index) list, in LDS
-// histograms: key bits 19..10, then 9..0, then up to three digits of ~index
-// among ties. Every thread of the NT-thread block must call it.
-template <int NT, class List>
+// Exact search of that rule over a (key, index) list, in LDS (s_hist holds
+// at least 2048 words): a histogram of key bits 19..10 picks the second-level
+// bin of the k-th key (PRE: the caller has put that histogram, built by the
+// partition kernel, in s_hist[0, 1024) already). When that bin holds at most
+// kSubRank keys, as it nearly always does, they are gathered into LDS and
+// ranked against each other (key descending, index ascending): the key of
+// rank need-1 is T and its index is imax. Otherwise a histogram of key bits
+// 9..0 and up to three digits of ~index among ties finish the search. Every
+// thread of the NT-thread block must call it.
+constexpr uint32_t kSubRank = 256;
+template <int NT, bool PRE = false, class List>
 __device__ __forceinline__ BinThreshold find_threshold(const List& L, uint32_t b0, uint32_t need,
                                                        uint32_t* s_hist, uint32_t* s_sh) {
   const int tid = threadIdx.x;
   const int n = L.size();
   const uint32_t pre20 = b0;                       // key >> 20
-  // pass A: key bits 19..10
-  for (int i = tid; i < 1024; i += NT) s_hist[i] = 0u;
-  __syncthreads();
-  for (int i = tid; i < n; i += NT) {
-    const uint2 e = L.get(i);
-    if ((e.x >> 20) == pre20) atomicAdd(&s_hist[(e.x >> 10) & 1023u], 1u);
+  if constexpr (!PRE) {
+    // pass A: key bits 19..10
+    for (int i = tid; i < 1024; i += NT) s_hist[i] = 0u;
+    __syncthreads();
+    for (int i = tid; i < n; i += NT) {
+      const uint2 e = L.get(i);
+      if ((e.x >> 20) == pre20) atomicAdd(&s_hist[(e.x >> 10) & 1023u], 1u);
+    }
+    __syncthreads();
   }
-  __syncthreads();
   const uint2 ra = resolve_lds<1024 / NT, NT>(s_hist, need, s_sh);
   const uint32_t pre10 = (pre20 << 10) | ra.x;     // key >> 10
+  const uint32_t nb = s_hist[ra.x];                // keys in that bin (>= ra.y >= 1)
+  if (nb <= kSubRank) {
+    // the bin's keys as (key, index) pairs in s_hist[1024 ..], a counter and
+    // the result after them
+    uint32_t* sub = s_hist + 1024;
+    uint32_t* cnt = s_hist + 1024 + 2 * kSubRank;
+    __syncthreads();                               // every thread has read s_hist[ra.x]
+    if (tid == 0) cnt[0] = 0u;
+    __syncthreads();
+    for (int i = tid; i < n; i += NT) {
+      const uint2 e = L.get(i);
+      if ((e.x >> 10) == pre10) {
+        const uint32_t pos = atomicAdd(cnt, 1u);
+        if (pos < kSubRank) {
+          sub[2 * pos] = e.x;
+          sub[2 * pos + 1] = e.y;
+        }
+      }
+    }
+    __syncthreads();
+    if ((uint32_t)tid < nb) {
+      const uint32_t kx = sub[2 * tid], ix = sub[2 * tid + 1];
+      uint32_t rank = 0;
+      for (uint32_t j = 0; j < nb; ++j) {
+        const uint32_t kj = sub[2 * j], ij = sub[2 * j + 1];
+        rank += (uint32_t)((kj > kx) | ((kj == kx) & (ij < ix)));
+      }
+      if (rank == ra.y - 1) {
+        cnt[1] = kx;
+        cnt[2] = ix;
+      }
+    }
+    __syncthreads();
+    const BinThreshold th{pre20, cnt[1], cnt[2]};
+    __syncthreads();                               // s_hist is free again for the caller
+    return th;
+  }
   // pass B: key bits 9..0
   for (int i = tid; i < 1024; i += NT) s_hist[i] = 0u;
   __syncthreads();
