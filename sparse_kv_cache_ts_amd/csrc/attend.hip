@@ -8,14 +8,15 @@
 // attend_kernel: one work-group per (split of the index list, KV head,
 // sequence), with an online softmax in fp32, base 2, and (max, sum, acc[d])
 // left per (sequence, head, split).
-//  * bf16 index lists: the GS query heads of a KV head share every gathered
-//    row, so the scores of a 64-token chunk are one small matrix product
-//    (16 tokens x 16 padded heads per wave on v_mfma_f32_16x16x32_bf16); the
-//    weights and V rows go through LDS and the weighted sum is taken on the
-//    vector units, each (head, dimension pair) owned by one thread.
-//  * fp32 rows and dense ranges: a row group of LPR lanes gathers one token's
-//    K and V rows (16-byte loads), takes the GS dot products and combines
-//    them with DPP; row groups are merged through LDS in a fixed order.
+//  * bf16 rows (index lists and dense ranges): the GS query heads of a KV
+//    head share every row, so the scores of a 64-token chunk are one small
+//    matrix product (16 tokens x 16 padded heads per wave on
+//    v_mfma_f32_16x16x32_bf16); the weights and V rows go through LDS and the
+//    weighted sum is taken on the vector units, each (head, dimension pair)
+//    owned by one thread.
+//  * fp32 rows: a row group of LPR lanes gathers one token's K and V rows
+//    (16-byte loads), takes the GS dot products and combines them with DPP;
+//    row groups are merged through LDS in a fixed order.
 // combine_kernel merges the splits by their log-sum-exp and, in a decode
 // step, also updates the Selection-Cache state.
 #include "topk_device.h"
@@ -33,9 +34,8 @@ __global__ __launch_bounds__(256) void attend_kernel(AttendParams p) {
   constexpr int W = 4 * CPL;                               // 32-bit words per lane
   constexpr int UA = 4;                                    // rows in flight per row group
   constexpr int RG = 256 / LPR;
-  // bf16 lists take the matrix-core path below; fp32 and dense ranges the
-  // row-group path
-  constexpr bool MF = DT == 1 && !DENSE;
+  // bf16 rows take the matrix-core path below; fp32 rows the row-group path
+  constexpr bool MF = DT == 1;
   constexpr int kVRow = D / 2 + 4;     // words per LDS row of V (padded: no bank conflicts)
   constexpr int kPRow = 17;            // weights per LDS token row (16 heads, padded)
 
@@ -263,8 +263,9 @@ __global__ __launch_bounds__(256) void attend_kernel(AttendParams p) {
     }
     if (len > 0) {
       constexpr int CAP = SEL ? kSelRangeMax : kAttendStage;
-      const int n = pend - pbeg;
-      const bool direct = !lds_list && n <= 64;
+      // dense: the contiguous tokens [pbeg, min(pend, len)), no list
+      const int n = DENSE ? max(0, min(pend, len) - pbeg) : pend - pbeg;
+      const bool direct = DENSE || (!lds_list && n <= 64);
       for (int c0 = 0; c0 < n; c0 += CAP) {
         const int cn = min(CAP, n - c0);
         if (!lds_list && !direct) {
@@ -276,7 +277,9 @@ __global__ __launch_bounds__(256) void attend_kernel(AttendParams p) {
         // this lane's row of chunk it (an empty slot reads token 0, masked)
         auto tok = [&](int it, bool& ok) -> int {
           const int q = it * 64 + 16 * wv + tl;
-          const int tt = direct ? tok_at(pbeg + c0 + q) : s_tok[min(q, cn - 1)];
+          int tt;
+          if constexpr (DENSE) tt = pbeg + c0 + q;
+          else tt = direct ? tok_at(pbeg + c0 + q) : s_tok[min(q, cn - 1)];
           ok = q < cn && tt >= 0 && tt < len;
           return ok ? tt : 0;
         };

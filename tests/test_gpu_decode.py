@@ -169,6 +169,47 @@ def test_topk_exact_many_rows(gpu_lib, k, stride):
         assert np.array_equal(got[r], want), f"row {r} (len {n})"
 
 
+def _crowded_row(seed, n, nb, ties):
+    """n values whose k-th largest (k = 1500 + nb // 2) lies in one 10-bit
+    second-level bin of its 12-bit first-level bin, with nb keys in that
+    second-level bin (pairs of equal keys when `ties`)."""
+    r = np.random.default_rng(seed)
+    hi = r.uniform(2.0, 3.0, 1000).astype(np.float32)
+    mid = r.uniform(1.01, 1.9, 500).astype(np.float32)         # same first-level bin, higher sub-bins
+    nd = nb // 2 if ties else nb
+    low10 = r.permutation(1024)[:nd].astype(np.uint32)
+    sub = (np.uint32(0x3F800000) + low10).view(np.float32)      # 1.0 .. 1.0 + 1023 ulp
+    if ties:
+        sub = np.concatenate([sub, sub])
+    low = r.uniform(0.0, 0.9, n - 1500 - sub.size).astype(np.float32)
+    row = np.concatenate([hi, mid, sub, low])
+    return row[r.permutation(n)], 1500 + nb // 2
+
+
+@pytest.mark.parametrize("rows", [3, 256])
+def test_topk_crowded_second_level_bin(gpu_lib, rows):
+    """The k-th key's second-level bin holds at most 256 keys (ranked directly)
+    or more (two further histogram passes), with and without equal keys: the
+    partition/finalize kernels (3 rows) and the one-row-per-work-group kernel
+    (256 rows)."""
+    ts = gpu_lib
+    n = 20000
+    for nb in (1, 200, 256, 257, 600):
+        for ties in (False, True):
+            if ties and nb < 2:
+                continue
+            made = [_crowded_row(1000 * nb + 10 * i + ties, n, nb, ties) for i in range(rows)]
+            k = made[0][1]
+            votes = torch.from_numpy(np.stack([m[0] for m in made]))
+            ld = torch.full((rows,), n, dtype=torch.int32, device="cuda")
+            idx = ts.topk(votes.cuda(), ld, k)
+            torch.cuda.synchronize()
+            got = idx.cpu().numpy()
+            v = votes.numpy().astype(np.float64)
+            for r in range(rows):
+                assert np.array_equal(got[r], O.top_k(v[r], k)), (nb, ties, r)
+
+
 def test_topk_repeat_is_deterministic(gpu_lib):
     ts = gpu_lib
     votes, lens = _topk_rows(3)
