@@ -36,15 +36,19 @@ __global__ __launch_bounds__(256) void attend_kernel(AttendParams p) {
   constexpr int RG = 256 / LPR;
   // bf16 rows take the matrix-core path below; fp32 rows the row-group path
   constexpr bool MF = DT == 1;
-  constexpr int kVRow = D / 2 + 4;     // words per LDS row of V (padded: no bank conflicts)
-  constexpr int kPRow = 17;            // weights per LDS token row (16 heads, padded)
+  // LDS rows of the matrix-core path: V rows of D/2 + 2 words (8-byte aligned;
+  // rows 8 apart fall 16 banks apart, so the column reads of P * V do not
+  // conflict), and bf16 weight parts in rows of 64 tokens per head (+4 words)
+  constexpr int kVRow = D / 2 + 2;
+  constexpr int kPtRow = 36;
 
   __shared__ float s_m[4][MF ? 1 : GS];
   __shared__ float s_l[4][MF ? 1 : GS];
   __shared__ float s_acc[MF ? 1 : 4 * GS * D];
   __shared__ __align__(16) uint32_t s_v[MF ? 64 * kVRow : 1];
-  __shared__ float s_p[MF ? 64 * kPRow : 1];
+  __shared__ __align__(16) uint32_t s_pt[MF ? 2 * 16 * kPtRow : 1];   // hi rows, then lo rows
   __shared__ float s_wm[MF ? 64 : 1];
+  __shared__ float s_wl[MF ? 64 : 1];
   // decode steps: the end of the top-k for this split's token range
   __shared__ uint32_t s_ck[SEL ? kCandLds : 1];
   __shared__ uint32_t s_ci[SEL ? kCandLds : 1];
@@ -229,19 +233,20 @@ __global__ __launch_bounds__(256) void attend_kernel(AttendParams p) {
     return (t >= 0 && t < len) ? (int)t : -1;
   };
   if constexpr (MF) {
-    // ---- bf16 lists. Each wave takes 16 tokens of a 64-token chunk (lane l:
+    // ---- bf16 rows. Each wave takes 16 tokens of a 64-token chunk (lane l:
     // token l%16, dimensions 32s + 8*(l/16) .. +7 of its K and V rows, one
     // 16-byte load per k-step). The matrix cores give S^T = K_tile * Q^T for
     // the slice's heads padded to 16 (lane l: tokens 4*(l/16) .. +3, head
-    // l%16); the chunk's max per head and the weights 2^(s - M) go through
-    // LDS together with the V rows, and the weighted V sum runs on the vector
-    // units with every (head, dimension pair) owned by one thread, so no
-    // cross-lane merge is left at the end.
+    // l%16). The chunk's max per head, the weights P = 2^(s - M) and the V
+    // rows go through LDS, and the matrix cores add P * V_chunk into O (lane
+    // l: heads 4*(l/16) .. +3, dimension l%16 of each of the wave's
+    // 16-dimension tiles); V's columns are read from LDS 16 bits at a time.
+    // P enters as two bf16 parts, hi = bf16(P) and lo = bf16(P - hi), so the
+    // weights keep about 16 significant bits (fp32-level accuracy of the
+    // output; V rows are bf16 already), and the row sums add the same hi + lo.
     constexpr int KS = D / 32;                 // k-steps of 32 dimensions
-    constexpr int NSLOT = 256 / (D / 2);       // head slots of the weighted sum
-    constexpr int HPS = (GS + NSLOT - 1) / NSLOT;
+    constexpr int NTW = D / 64;                // 16-dimension tiles of O per wave
     const int tl = lane & 15, g4 = lane >> 4;
-    const int dp = tid % (D / 2), slot = tid / (D / 2);
     uint4 qf[KS];
     {
       const int head = kvh * p.G + slice * GS + min(tl, GS - 1);
@@ -252,15 +257,16 @@ __global__ __launch_bounds__(256) void attend_kernel(AttendParams p) {
         qf[s] = tl < GS ? v : make_uint4(0u, 0u, 0u, 0u);
       }
     }
-    float Mc = -INFINITY;                      // running max of head tl
-    float Mp[HPS], Lp[HPS], A0[HPS], A1[HPS];  // per owned head: max, sum, two dims
+    float Mc = -INFINITY;                      // running max of head tl (score side)
+    float Mo[4], Lo[4];                        // running max and sum of heads 4*g4 + i
+    f32x4_t O[NTW];
 #pragma unroll
-    for (int jh = 0; jh < HPS; ++jh) {
-      Mp[jh] = -INFINITY;
-      Lp[jh] = 0.f;
-      A0[jh] = 0.f;
-      A1[jh] = 0.f;
+    for (int i = 0; i < 4; ++i) {
+      Mo[i] = -INFINITY;
+      Lo[i] = 0.f;
     }
+#pragma unroll
+    for (int nt = 0; nt < NTW; ++nt) O[nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     if (len > 0) {
       constexpr int CAP = SEL ? kSelRangeMax : kAttendStage;
       // dense: the contiguous tokens [pbeg, min(pend, len)), no list
@@ -306,41 +312,70 @@ __global__ __launch_bounds__(256) void attend_kernel(AttendParams p) {
             mx = fmaxf(mx, sv[i]);
           }
           mx = xor_max<32>(xor_max<16>(mx));
+          // V rows at LDS row 16*wv + tl (8-byte stores: the padded row is 8-byte aligned)
           uint32_t* vr = s_v + (16 * wv + tl) * kVRow + g4 * 4;
 #pragma unroll
-          for (int s = 0; s < KS; ++s) *reinterpret_cast<uint4*>(vr + s * 16) = vf[s];
+          for (int s = 0; s < KS; ++s) {
+            *reinterpret_cast<uint2*>(vr + s * 16) = make_uint2(vf[s].x, vf[s].y);
+            *reinterpret_cast<uint2*>(vr + s * 16 + 2) = make_uint2(vf[s].z, vf[s].w);
+          }
           if (g4 == 0) s_wm[wv * 16 + tl] = mx;
           __syncthreads();
-          const float cm = fmaxf(fmaxf(s_wm[tl], s_wm[16 + tl]), fmaxf(s_wm[32 + tl], s_wm[48 + tl]));
-          Mc = fmaxf(Mc, cm);
-          if (tl < GS) {
+          // weights of head tl as bf16 hi + lo parts, and their sum over the wave's tokens
+          Mc = fmaxf(Mc, fmaxf(fmaxf(s_wm[tl], s_wm[16 + tl]), fmaxf(s_wm[32 + tl], s_wm[48 + tl])));
+          uint32_t ph[4], pl[4];
+          float ls = 0.f;
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
-              s_p[(16 * wv + 4 * g4 + i) * kPRow + tl] = sv[i] == -INFINITY ? 0.f : ex2(sv[i] - Mc);
+          for (int i = 0; i < 4; ++i) {
+            const float pw = sv[i] == -INFINITY ? 0.f : ex2(sv[i] - Mc);
+            ph[i] = bf16_bits(pw);
+            const float hv = __uint_as_float(ph[i] << 16);
+            pl[i] = bf16_bits(pw - hv);          // exact difference
+            ls += hv + __uint_as_float(pl[i] << 16);
+          }
+          ls = xor_sum<32>(xor_sum<16>(ls));
+          *reinterpret_cast<uint2*>(s_pt + tl * kPtRow + 8 * wv + 2 * g4) =
+              make_uint2(ph[0] | (ph[1] << 16), ph[2] | (ph[3] << 16));
+          *reinterpret_cast<uint2*>(s_pt + (16 + tl) * kPtRow + 8 * wv + 2 * g4) =
+              make_uint2(pl[0] | (pl[1] << 16), pl[2] | (pl[3] << 16));
+          if (g4 == 0) s_wl[wv * 16 + tl] = ls;
+          // rescale this lane's rows of O (heads 4*g4 + i) to the new max
+          float corr[4];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int h = 4 * g4 + i;
+            const float mn = fmaxf(Mo[i], fmaxf(fmaxf(s_wm[h], s_wm[16 + h]), fmaxf(s_wm[32 + h], s_wm[48 + h])));
+            corr[i] = mn == -INFINITY ? 1.f : ex2(Mo[i] - mn);
+            Mo[i] = mn;
           }
 #pragma unroll
-          for (int jh = 0; jh < HPS; ++jh) {
-            const int h = min(slot + jh * NSLOT, 15);
-            const float cmh = fmaxf(fmaxf(s_wm[h], s_wm[16 + h]), fmaxf(s_wm[32 + h], s_wm[48 + h]));
-            const float mn = fmaxf(Mp[jh], cmh);
-            const float corr = mn == -INFINITY ? 1.f : ex2(Mp[jh] - mn);
-            Mp[jh] = mn;
-            A0[jh] *= corr;
-            A1[jh] *= corr;
-            Lp[jh] *= corr;
-          }
+          for (int nt = 0; nt < NTW; ++nt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) O[nt][i] *= corr[i];
           __syncthreads();
-          const int ncnt = min(64, cn - it * 64);
-#pragma unroll 4
-          for (int t = 0; t < ncnt; ++t) {
-            const uint32_t w = s_v[t * kVRow + dp];
-            const float v0 = bf16_lo(w), v1 = bf16_hi(w);
 #pragma unroll
-            for (int jh = 0; jh < HPS; ++jh) {
-              const float pw = s_p[t * kPRow + min(slot + jh * NSLOT, 15)];
-              A0[jh] = fmaf(pw, v0, A0[jh]);
-              A1[jh] = fmaf(pw, v1, A1[jh]);
-              Lp[jh] += pw;
+          for (int i = 0; i < 4; ++i) {
+            const int h = 4 * g4 + i;
+            Lo[i] = Lo[i] * corr[i] + ((s_wl[h] + s_wl[16 + h]) + (s_wl[32 + h] + s_wl[48 + h]));
+          }
+          // O += P * V over the chunk's 64 tokens, two k-steps of 32
+          const uint16_t* vh = reinterpret_cast<const uint16_t*>(s_v);
+#pragma unroll
+          for (int ks = 0; ks < 2; ++ks) {
+            const uint4 pa = *reinterpret_cast<const uint4*>(s_pt + tl * kPtRow + 16 * ks + 4 * g4);
+            const uint4 pb = *reinterpret_cast<const uint4*>(s_pt + (16 + tl) * kPtRow + 16 * ks + 4 * g4);
+            const int r0 = 32 * ks + 8 * g4;
+#pragma unroll
+            for (int nt = 0; nt < NTW; ++nt) {
+              const int dim = 16 * (NTW * wv + nt) + tl;
+              uint32_t w[4];
+#pragma unroll
+              for (int j = 0; j < 4; ++j)
+                w[j] = (uint32_t)vh[(r0 + 2 * j) * (2 * kVRow) + dim] |
+                       ((uint32_t)vh[(r0 + 2 * j + 1) * (2 * kVRow) + dim] << 16);
+              const bf16x8_t vb = as_bf8(make_uint4(w[0], w[1], w[2], w[3]));
+              O[nt] = mfma16(as_bf8(pa), vb, O[nt]);
+              O[nt] = mfma16(as_bf8(pb), vb, O[nt]);
             }
           }
           // the next chunk's V rows and weights overwrite these
@@ -369,16 +404,18 @@ __global__ __launch_bounds__(256) void attend_kernel(AttendParams p) {
         }
       }
     }
+    // this lane's rows of O: heads 4*g4 + i, dimension tl of the wave's tiles
 #pragma unroll
-    for (int jh = 0; jh < HPS; ++jh) {
-      const int h = slot + jh * NSLOT;
+    for (int i = 0; i < 4; ++i) {
+      const int h = 4 * g4 + i;
       if (h < GS) {
         const int head = kvh * p.G + slice * GS + h;
         const size_t o = ((size_t)b * p.Hq + head) * p.nsplit + split;
-        *reinterpret_cast<float2*>(p.pacc + o * D + 2 * dp) = make_float2(A0[jh], A1[jh]);
-        if (dp == 0) {
-          p.pm[o] = Mp[jh];
-          p.pl[o] = Lp[jh];
+#pragma unroll
+        for (int nt = 0; nt < NTW; ++nt) p.pacc[o * D + 16 * (NTW * wv + nt) + tl] = O[nt][i];
+        if (wv == 0 && tl == 0) {
+          p.pm[o] = Mo[i];
+          p.pl[o] = Lo[i];
         }
       }
     }

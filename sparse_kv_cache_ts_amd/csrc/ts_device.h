@@ -14,6 +14,12 @@ constexpr float kLog2e = 1.4426950408889634f;
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 
+// fp32 -> bf16 bits, rounded to nearest even (finite, non-NaN inputs).
+__device__ __forceinline__ uint32_t bf16_bits(float x) {
+  const uint32_t u = __float_as_uint(x);
+  return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+}
+
 typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2_t;
 
 // fp32 += a.lo*b.lo + a.hi*b.hi on packed bf16 pairs (v_dot2c_f32_bf16).
