@@ -162,7 +162,7 @@ __global__ __launch_bounds__(256) void topk_partition_kernel(TopkParams p) {
       const uint32_t key = float_key(v[i]);
       if (pos < (uint32_t)kCandCap) cand[pos] = make_uint2(key, (uint32_t)e);
       ++pos;
-      atomicAdd(ctrl + kCtlHistB + ((key >> 10) & 1023u), 1u);
+      if (p.hist_b) atomicAdd(ctrl + kCtlHistB + ((key >> 10) & 1023u), 1u);
     }
   }
 }

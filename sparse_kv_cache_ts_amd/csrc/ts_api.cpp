@@ -841,10 +841,14 @@ ts_status ts_sparse_attend_prefill(const ts_kv_layout* L, int32_t chunk, int32_t
 }  // extern "C"
 
 namespace {
-// split-K over every cached token: 256-row multiples, at most 256 splits
+// split-K over every cached token: 256-row multiples, at most 256 splits, and
+// grown in steps of 64 rows while the grid exceeds 768 work-groups (three per
+// CU, what the matrix-core attention kernel's registers allow at once: a
+// second, partial round of work-groups costs more than longer splits)
 void plan_dense(const Geo& g, int B, Carve& c, AttendPlan& a) {
   int split = 256;
   while (cdiv(g.max_len, split) > 256) split += 256;
+  while (split < g.max_len && (long)B * g.Hkv * g.nslices * cdiv(g.max_len, split) > 768) split += 64;
   a.split = split;
   a.nsplit = cdiv(g.max_len, split);
   a.pm = c.take((size_t)B * g.Hq * a.nsplit * 4);
@@ -1048,6 +1052,7 @@ ts_status ts_decode_step(ts_sel_cache* cache, const ts_kv_layout* L, int32_t bat
   tp.hist_copies = copies;
   const int gx = cdiv(g.max_len, kTopkChunk);
   if (p.a.range > 0) {
+    tp.hist_b = 1;     // the attention work-groups start their threshold search from it
     TS_LAUNCH_K(kKTopkPartition, launch_topk_partition(tp, gx, st), "top-k partition");
   } else {
     TS_TRY(run_select(tp, gx, g.max_len, st));

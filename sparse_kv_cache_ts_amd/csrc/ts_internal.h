@@ -136,6 +136,7 @@ struct TopkParams {
   uint2* cand;              // [rows][kCandCap] (key, index) of threshold-bin candidates
   int rows, row_stride, k, bm_stride;
   int hist_copies;          // copies of the first histogram (1 .. kHistCopiesMax)
+  int hist_b;               // partition: also count bin b0's keys by bits 19..10 (kCtlHistB)
 };
 
 struct AttendParams {
