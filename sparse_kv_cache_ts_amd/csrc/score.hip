@@ -348,19 +348,25 @@ __global__ __launch_bounds__(256) void score_pass1_kernel(ScoreParams p) {
 // over all N tokens. One wave per (head, sequence); all loads issued at once.
 __global__ __launch_bounds__(64) void lse_kernel(LseParams p) {
   const int h = blockIdx.x, b = blockIdx.y, lane = threadIdx.x;
-  if (p.hit && p.hit[b]) return;
+  // the decision, the length and the first 1024 tile partials are requested
+  // together (partials past the sequence are allocated and masked below)
+  const int hitv = p.hit ? p.hit[b] : 0;
   const int len = p.seq_lens[b];
-  if (len <= 0) return;
-  const int nt = (len + p.tile - 1) / p.tile;
   const float2* pp = p.partials + ((size_t)b * p.Hq + h) * p.ntiles;
+  float2 pr[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) pr[i] = pp[min(i * 64 + lane, p.ntiles - 1)];
+  if (hitv || len <= 0) return;
+  const int nt = (len + p.tile - 1) / p.tile;
   float M = -INFINITY, L = 0.f;
   for (int t0 = 0; t0 < nt; t0 += 64 * 16) {
-    float2 pr[16];
+    if (t0 > 0) {
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int t = t0 + i * 64 + lane;
-      pr[i] = t < nt ? pp[t] : make_float2(-INFINITY, 0.f);
+      for (int i = 0; i < 16; ++i) pr[i] = pp[min(t0 + i * 64 + lane, p.ntiles - 1)];
     }
+#pragma unroll
+    for (int i = 0; i < 16; ++i)
+      if (t0 + i * 64 + lane >= nt) pr[i] = make_float2(-INFINITY, 0.f);
     float m = M;
 #pragma unroll
     for (int i = 0; i < 16; ++i) m = fmaxf(m, pr[i].x);
@@ -386,21 +392,27 @@ __global__ __launch_bounds__(256) void votes_kernel(VoteParams p) {
   __shared__ uint32_t s_hist[1 << kHist0Bits];
 
   const int b = blockIdx.y;
-  if (p.hit && p.hit[b]) return;
-  const int len = p.seq_lens[b];
-  const int start = blockIdx.x * kVoteTile;
-  if (start >= len) return;
   const int tid = threadIdx.x;
   const int Hq = p.Hq;
-  for (int h = tid; h < Hq; h += 256) s_lse[h] = p.lse[(size_t)b * Hq + h];
+  const bool fast = (Hq & 3) == 0 && Hq <= kMaxQHeads;
+  // the decision, the length and (fast path) this lane's four log-sum-exps
+  // are requested together
+  const int hitv = p.hit ? p.hit[b] : 0;
+  const int len = p.seq_lens[b];
+  const int li = tid & 7;                        // lane in the group (fast path)
+  float4 lse4 = make_float4(0.f, 0.f, 0.f, 0.f);
+  if (fast && Hq <= 32) lse4 = ldf4(p.lse + (size_t)b * Hq + min(4 * li, Hq - 4));
+  const int start = blockIdx.x * kVoteTile;
+  if (hitv || start >= len) return;
+  if (!fast || Hq > 32)
+    for (int h = tid; h < Hq; h += 256) s_lse[h] = p.lse[(size_t)b * Hq + h];
   if (p.do_hist)
     for (int i = tid; i < (1 << kHist0Bits); i += 256) s_hist[i] = 0u;
   __syncthreads();
 
-  if ((Hq & 3) == 0 && Hq <= kMaxQHeads) {
+  if (fast) {
     constexpr int TPG = 8;                       // tokens per lane group and round
     constexpr int WT = kVoteTile / 4;            // tokens per wave
-    const int li = tid & 7;                      // lane in the group
     const int wv = tid >> 6, gi = (tid >> 3) & 7;
     const int nr = (Hq + 31) / 32;               // 16-byte loads per lane and token
     for (int c0 = 0; c0 < WT; c0 += 8 * TPG) {
@@ -418,7 +430,12 @@ __global__ __launch_bounds__(256) void votes_kernel(VoteParams p) {
                                   : make_float4(-INFINITY, -INFINITY, -INFINITY, -INFINITY);
         }
         if (has) {
-          const float l0 = s_lse[h], l1 = s_lse[h + 1], l2 = s_lse[h + 2], l3 = s_lse[h + 3];
+          float l0, l1, l2, l3;
+          if (Hq <= 32) {
+            l0 = lse4.x; l1 = lse4.y; l2 = lse4.z; l3 = lse4.w;
+          } else {
+            l0 = s_lse[h]; l1 = s_lse[h + 1]; l2 = s_lse[h + 2]; l3 = s_lse[h + 3];
+          }
 #pragma unroll
           for (int t = 0; t < TPG; ++t)
             v[t] += (ex2(x[t].x - l0) + ex2(x[t].y - l1)) + (ex2(x[t].z - l2) + ex2(x[t].w - l3));

@@ -54,10 +54,10 @@ __global__ __launch_bounds__(256) void topk_hist0_kernel(TopkParams p) {
   constexpr int PER = kTopkChunk / 256;
   __shared__ uint32_t s_hist[1 << kHist0Bits];
   const int r = blockIdx.y;
-  if (p.hit && p.hit[r]) return;
+  const int hitv = p.hit ? p.hit[r] : 0;         // requested together with the length
   const int len = row_length(p, r);
   const int start = blockIdx.x * kTopkChunk;
-  if (start >= len) return;
+  if (hitv || start >= len) return;
   const int tid = threadIdx.x;
   for (int i = tid; i < (1 << kHist0Bits); i += 256) s_hist[i] = 0u;
   const float* row = p.votes + (size_t)r * p.row_stride;
@@ -85,10 +85,10 @@ __global__ __launch_bounds__(256) void topk_partition_kernel(TopkParams p) {
   __shared__ uint32_t s_sh[8];
   __shared__ uint32_t s_base;
   const int r = blockIdx.y;
-  if (p.hit && p.hit[r]) return;
+  const int hitv = p.hit ? p.hit[r] : 0;         // requested together with the length
   const int len = row_length(p, r);
   const int start = blockIdx.x * kTopkChunk;
-  if (start >= len) return;
+  if (hitv || start >= len) return;
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const uint32_t k_eff = (uint32_t)min(p.k, len);
   uint32_t* ctrl = p.ctrl + (size_t)r * kCtrlStride;
@@ -123,10 +123,9 @@ __global__ __launch_bounds__(256) void topk_partition_kernel(TopkParams p) {
         c[4 * q + 2] += a[u][q].z; c[4 * q + 3] += a[u][q].w;
       }
   }
-  const uint2 rb = resolve_counts<16>(c, k_eff, s_sh);
+  uint32_t cnt_b0;
+  const uint2 rb = resolve_counts<16>(c, k_eff, s_sh, &cnt_b0);
   const uint32_t b0 = rb.x, need = rb.y;
-  uint32_t cnt_b0 = 0;
-  for (int cp = 0; cp < p.hist_copies; ++cp) cnt_b0 += ctrl[kCtlHist0 + cp * (1 << kHist0Bits) + b0];
   const bool whole = (need == cnt_b0);     // the whole bin is selected: no candidates
   if (blockIdx.x == 0 && tid == 0) {
     ctrl[kCtlPrefix] = b0;
@@ -278,8 +277,9 @@ __global__ __launch_bounds__(kFinalThreads) void topk_finalize_kernel(TopkParams
   __shared__ __align__(16) uint32_t s_bm[kBitmapLds];
   __shared__ uint32_t s_sh[16];
   const int r = blockIdx.x;
-  if (p.hit && p.hit[r]) return;
+  const int hitv = p.hit ? p.hit[r] : 0;         // requested together with the length
   const int len = row_length(p, r);
+  if (hitv) return;
   const int k = p.k;
   const int k_eff = min(k, len);
   const int tid = threadIdx.x;
@@ -361,8 +361,9 @@ __global__ __launch_bounds__(kRowThreads) void topk_row_kernel(TopkParams p) {
   __shared__ uint32_t s_sh[NWV + 8];
   __shared__ uint32_t s_ncand;
   const int r = blockIdx.x;
-  if (p.hit && p.hit[r]) return;
+  const int hitv = p.hit ? p.hit[r] : 0;         // requested together with the length
   const int len = row_length(p, r);
+  if (hitv) return;
   const int k = p.k;
   const int k_eff = min(k, len);
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
@@ -425,12 +426,10 @@ __global__ __launch_bounds__(kRowThreads) void topk_row_kernel(TopkParams p) {
     }
     if (tid == 0) s_ncand = 0u;
   }
-  const uint2 rb = resolve_counts<4, NT>(c, (uint32_t)k_eff, s_sh);
+  uint32_t cnt_b0;
+  const uint2 rb = resolve_counts<4, NT>(c, (uint32_t)k_eff, s_sh, &cnt_b0);
   const uint32_t b0 = rb.x, need = rb.y;
-  // the count of bin b0 is held by thread b0 / 4
-  if (tid == (int)(b0 >> 2)) s_sh[NWV + 2] = c[b0 & 3];
-  __syncthreads();
-  const bool whole = (need == s_sh[NWV + 2]);      // the whole bin is selected
+  const bool whole = (need == cnt_b0);             // the whole bin is selected
   const BinBounds bb(b0, SHIFT);
 
   auto scan_round = [&](int g0, const float4 (&v)[UL]) {

@@ -204,9 +204,11 @@ __device__ __forceinline__ uint32_t block_excl_scan_256(uint32_t v, uint32_t* sh
 // t owns bins t*PER .. t*PER+PER-1), find the highest bin whose suffix sum
 // (bins >= it) reaches `need` (1 <= need <= total) and how many elements are
 // still needed inside it. Block-wide over NT threads (a multiple of 64); `sh`
-// needs NT/64 + 2 words. Returns (bin, still needed) in every thread.
+// needs NT/64 + 3 words. Returns (bin, still needed) in every thread and, if
+// bin_count is given, that bin's count.
 template <int PER, int NT = 256>
-__device__ __forceinline__ uint2 resolve_counts(const uint32_t (&c)[PER], uint32_t need, uint32_t* sh) {
+__device__ __forceinline__ uint2 resolve_counts(const uint32_t (&c)[PER], uint32_t need, uint32_t* sh,
+                                                uint32_t* bin_count = nullptr) {
   constexpr int NWAVE = NT / 64;
   const int t = threadIdx.x, lane = t & 63, w = t >> 6;
   uint32_t s = 0;
@@ -233,6 +235,7 @@ __device__ __forceinline__ uint2 resolve_counts(const uint32_t (&c)[PER], uint32
       if (!done && cum + c[i] >= need) {
         sh[0] = (uint32_t)(t * PER + i);
         sh[1] = need - cum;
+        sh[2 + NWAVE] = c[i];
         done = true;
       }
       cum += c[i];
@@ -240,6 +243,7 @@ __device__ __forceinline__ uint2 resolve_counts(const uint32_t (&c)[PER], uint32
   }
   __syncthreads();
   const uint2 r = make_uint2(sh[0], sh[1]);
+  if (bin_count) *bin_count = sh[2 + NWAVE];
   __syncthreads();
   return r;
 }
