@@ -266,7 +266,7 @@ __global__ __launch_bounds__(512) void prefill_votes_kernel(PrefillParams p) {
   constexpr int QB = 16 * RT / G;  // queries per work-group
   constexpr int KT = kPrefillKeys2;
   static_assert(G == 4, "a lane's four C rows must be one query's four heads");
-  __shared__ float s_v[2][8][QB][16];           // [buffer][KV head][query][key]
+  __shared__ float s_v[2][8][QB][32];           // [buffer][KV head][query][key of a tile pair]
   __shared__ float s_out[QB][KT];               // the work-group's votes
   const int nqb = (p.chunk + QB - 1) / QB;
   const int f = xcd_flat(blockIdx.x, gridDim.x);
@@ -299,9 +299,11 @@ __global__ __launch_bounds__(512) void prefill_votes_kernel(PrefillParams p) {
     }
   const float sc2 = p.scale2;
 
-  // one tile: this wave's head-group terms into s_v[b], a barrier, then the
-  // fixed-order sum over the KV heads into the LDS vote tile
-  auto tile = [&](int t, const uint4 (&kf)[KS], int b) {
+  // one tile: this wave's head-group terms into half `half` of s_v[b]; after
+  // two tiles a barrier, then the fixed-order sum over the KV heads into the
+  // LDS vote tile (flush). Tile pairs alternate between the two buffers, so
+  // one barrier per 32 keys suffices.
+  auto tile_c = [&](int t, const uint4 (&kf)[KS], int b, int half) {
     const int kb = k0 + t * 16;
     f32x4_t sc[RT];
     qk_tile<RT, KS>(qf, kf, sc);
@@ -314,15 +316,19 @@ __global__ __launch_bounds__(512) void prefill_votes_kernel(PrefillParams p) {
       for (int i = 0; i < 4; ++i) v += ex2(fmaf(sc[rt][i], sc2, -lse[rt][i]));
       const int ql = rt * 4 + (lane >> 4);
       if (!all && key > p.q_pos0 + qbase + ql) v = 0.f;
-      s_v[b][g][ql][lane & 15] = v;
+      s_v[b][g][ql][half * 16 + (lane & 15)] = v;
     }
+  };
+  auto flush = [&](int t, int b, int nk) {
     __syncthreads();
-    for (int e = tid; e < QB * 16; e += blockDim.x) {
-      const int ql = e >> 4, c = e & 15;
-      float v = 0.f;
+    for (int e = tid; e < QB * 32; e += blockDim.x) {
+      const int ql = e >> 5, c = e & 31;
+      if (c < nk) {
+        float v = 0.f;
 #pragma unroll
-      for (int gg = 0; gg < 8; ++gg) v += (gg < nw) ? s_v[b][gg][ql][c] : 0.f;
-      s_out[ql][t * 16 + c] = v;
+        for (int gg = 0; gg < 8; ++gg) v += (gg < nw) ? s_v[b][gg][ql][c] : 0.f;
+        s_out[ql][t * 16 + c] = v;
+      }
     }
   };
 
@@ -332,23 +338,27 @@ __global__ __launch_bounds__(512) void prefill_votes_kernel(PrefillParams p) {
   // issued.
   uint4 ka[KS], kb_[KS];
   if (nt > 0) load_k_tile<D>(p, g, k0, lane, ka);
-  int t = 0;
+  int t = 0, pb = 0;
   for (; t + 2 < nt; t += 2) {
     load_k_tile<D>(p, g, k0 + (t + 1) * 16, lane, kb_);
     __builtin_amdgcn_sched_barrier(0);
-    tile(t, ka, 0);
+    tile_c(t, ka, pb, 0);
     __builtin_amdgcn_sched_barrier(0);
     load_k_tile<D>(p, g, k0 + (t + 2) * 16, lane, ka);
     __builtin_amdgcn_sched_barrier(0);
-    tile(t + 1, kb_, 1);
+    tile_c(t + 1, kb_, pb, 1);
     __builtin_amdgcn_sched_barrier(0);
+    flush(t, pb, 32);
+    pb ^= 1;
   }
   if (t + 1 < nt) {
     load_k_tile<D>(p, g, k0 + (t + 1) * 16, lane, kb_);
-    tile(t, ka, 0);
-    tile(t + 1, kb_, 1);
+    tile_c(t, ka, pb, 0);
+    tile_c(t + 1, kb_, pb, 1);
+    flush(t, pb, 32);
   } else if (t < nt) {
-    tile(t, ka, 0);
+    tile_c(t, ka, pb, 0);
+    flush(t, pb, 16);
   }
   __syncthreads();
   // the vote tile, coalesced along each query's row; keys no query of the
