@@ -254,11 +254,15 @@ struct AttendPlan {
   size_t pm, pl, pacc;
 };
 void plan_attend(const Geo& g, int B, int k, Carve& c, AttendPlan& a) {
-  // about two work-groups per CU, each gathering 32..256 selected rows
+  // at least about two work-groups per CU, each gathering 32..256 selected
+  // rows; then longer splits (steps of 64 rows) while the grid exceeds what
+  // runs at once, since a partial second round of work-groups costs more
+  // than longer lists
   const long cols = (long)B * g.Hkv * g.nslices;
   int split = 256;
   while (split > 32 && cols * cdiv(k, split) < 512) split >>= 1;
   while (cdiv(k, split) > kMaxSplits) split <<= 1;
+  while (split < k && cols * cdiv(k, split) > kAttendResidentWGs) split += 64;
   a.split = split;
   a.nsplit = cdiv(k, split);
   a.pm = c.take((size_t)B * g.Hq * a.nsplit * 4);
@@ -842,13 +846,13 @@ ts_status ts_sparse_attend_prefill(const ts_kv_layout* L, int32_t chunk, int32_t
 
 namespace {
 // split-K over every cached token: 256-row multiples, at most 256 splits, and
-// grown in steps of 64 rows while the grid exceeds 768 work-groups (three per
-// CU, what the matrix-core attention kernel's registers allow at once: a
-// second, partial round of work-groups costs more than longer splits)
+// grown in steps of 64 rows while the grid exceeds what runs at once
 void plan_dense(const Geo& g, int B, Carve& c, AttendPlan& a) {
   int split = 256;
   while (cdiv(g.max_len, split) > 256) split += 256;
-  while (split < g.max_len && (long)B * g.Hkv * g.nslices * cdiv(g.max_len, split) > 768) split += 64;
+  while (split < g.max_len &&
+         (long)B * g.Hkv * g.nslices * cdiv(g.max_len, split) > kAttendResidentWGs)
+    split += 64;
   a.split = split;
   a.nsplit = cdiv(g.max_len, split);
   a.pm = c.take((size_t)B * g.Hq * a.nsplit * 4);

@@ -16,6 +16,9 @@ constexpr int kTopkChunk = 4096;   // elements per top-k work-group
 constexpr int kMaxHeadsPerWG = 64; // Hkv * heads-per-slice held by one scoring WG
 constexpr int kMaxQHeads = 256;
 constexpr int kMaxSplits = 1024;  // attention splits per (sequence, head)
+// attention work-groups resident at once on MI355X: 256 CUs x 3 (the bf16
+// attention kernel's ~150 registers per lane allow three 256-thread groups)
+constexpr long kAttendResidentWGs = 768;
 constexpr float kLog2eHost = 1.4426950408889634f;
 // prefill log-sum-exp pass: 16-row MFMA tiles per wave (4 waves per work-group,
 // one KV head); every wave reads the same keys, so more rows per wave means
