@@ -62,7 +62,10 @@ typedef enum ts_dtype { TS_F32 = 0, TS_BF16 = 1 } ts_dtype;
  *   contiguous (page_size == 0): K and V are [batch][max_len][num_kv_heads][head_dim];
  *   paged      (page_size  > 0): K and V are pools [num_pages][page_size][num_kv_heads][head_dim]
  *     and token j of sequence b lives in pool page page_table[b * page_table_stride + j / page_size],
- *     slot j % page_size. page_size must be a power of two.                              */
+ *     slot j % page_size. page_size must be a power of two. Every page that holds a token
+ *     below seq_lens[b] must map to a pool page that exists (0 <= entry < pool pages): the
+ *     scoring and attention kernels read those entries unchecked, and a bad entry is an
+ *     out-of-bounds device read. Entries past the sequence are never read by them.       */
 typedef struct ts_kv_layout {
   int32_t num_q_heads;        /* Hq                                                  */
   int32_t num_kv_heads;       /* Hkv, divides Hq                                     */
