@@ -72,6 +72,27 @@ __global__ __launch_bounds__(256) void attend_kernel(AttendParams p) {
   const int32_t* idx =
       DENSE ? nullptr : p.idx + (size_t)b * p.idx_b_stride + (size_t)kvh * p.idx_kv_stride;
   const int Hkv = p.Hkv;
+  // requested first, whatever the path (bf16 rows): the query fragments and
+  // this lane's first list entry, so that on a hit step (or any list read
+  // straight from global memory) neither waits behind the hit flag
+  const int tl = lane & 15, g4 = lane >> 4;
+  uint4 qf[MF ? D / 32 : 1];
+  int raw0 = -1;
+  if constexpr (MF) {
+    const int head = kvh * p.G + slice * GS + min(tl, GS - 1);
+    const char* qb = (const char*)p.q + ((size_t)b * p.Hq + head) * ROWB + g4 * 16;
+#pragma unroll
+    for (int s = 0; s < D / 32; ++s) {
+      const uint4 v = ld16(qb + s * 64);
+      qf[s] = tl < GS ? v : make_uint4(0u, 0u, 0u, 0u);
+    }
+    if constexpr (!DENSE) {
+      // (on a decode miss step the list is the stored selection that this
+      // kernel is rewriting: the entry is then stale and not used)
+      const int pos = pbeg + 16 * wv + tl;
+      if (pos < pend) raw0 = idx[p.sel_page_log2 > 0 ? (pos >> p.sel_page_log2) : pos];
+    }
+  }
   bool lds_list = false;
   if constexpr (SEL) {
     if (!p.sel_hit[b]) {
@@ -220,17 +241,20 @@ __global__ __launch_bounds__(256) void attend_kernel(AttendParams p) {
     }
   };
 
-  // token at list position pos of a global list (-1: none, or outside the sequence)
-  auto tok_at = [&](int pos) -> int {
+  // token at list position pos of a global list (-1: none, or outside the
+  // sequence), from the list entry `raw` that holds it
+  auto tok_from = [&](int pos, int raw) -> int {
     if (pos >= pend) return -1;
     long long t;
-    if (p.sel_page_log2 > 0) {
-      const int pg = idx[pos >> p.sel_page_log2];
-      t = pg < 0 ? -1 : ((long long)pg << p.sel_page_log2) + (pos & ((1 << p.sel_page_log2) - 1));
-    } else {
-      t = idx[pos];
-    }
+    if (p.sel_page_log2 > 0)
+      t = raw < 0 ? -1 : ((long long)raw << p.sel_page_log2) + (pos & ((1 << p.sel_page_log2) - 1));
+    else
+      t = raw;
     return (t >= 0 && t < len) ? (int)t : -1;
+  };
+  auto tok_at = [&](int pos) -> int {
+    if (pos >= pend) return -1;
+    return tok_from(pos, idx[p.sel_page_log2 > 0 ? (pos >> p.sel_page_log2) : pos]);
   };
   if constexpr (MF) {
     // ---- bf16 rows. Each wave takes 16 tokens of a 64-token chunk (lane l:
@@ -246,17 +270,6 @@ __global__ __launch_bounds__(256) void attend_kernel(AttendParams p) {
     // output; V rows are bf16 already), and the row sums add the same hi + lo.
     constexpr int KS = D / 32;                 // k-steps of 32 dimensions
     constexpr int NTW = D / 64;                // 16-dimension tiles of O per wave
-    const int tl = lane & 15, g4 = lane >> 4;
-    uint4 qf[KS];
-    {
-      const int head = kvh * p.G + slice * GS + min(tl, GS - 1);
-      const char* qb = (const char*)p.q + ((size_t)b * p.Hq + head) * ROWB + g4 * 16;
-#pragma unroll
-      for (int s = 0; s < KS; ++s) {
-        const uint4 v = ld16(qb + s * 64);
-        qf[s] = tl < GS ? v : make_uint4(0u, 0u, 0u, 0u);
-      }
-    }
     float Mc = -INFINITY;                      // running max of head tl (score side)
     float Mo[4], Lo[4];                        // running max and sum of heads 4*g4 + i
     f32x4_t O[NTW];
@@ -285,6 +298,7 @@ __global__ __launch_bounds__(256) void attend_kernel(AttendParams p) {
           const int q = it * 64 + 16 * wv + tl;
           int tt;
           if constexpr (DENSE) tt = pbeg + c0 + q;
+          else if (direct && c0 == 0 && it == 0) tt = tok_from(pbeg + q, raw0);  // requested at the start
           else tt = direct ? tok_at(pbeg + c0 + q) : s_tok[min(q, cn - 1)];
           ok = q < cn && tt >= 0 && tt < len;
           return ok ? tt : 0;
