@@ -82,3 +82,29 @@ def test_dense_attend_full_size(gpu_lib):
     ref = O.sparse_attention(np64(x["q"])[0], np32(x["k_cache"][0]), np32(x["v_cache"][0]),
                              np.arange(n))
     check_attention(np64(out)[0], ref, 1e-2)
+
+
+def test_attend_more_columns_than_resident_groups(gpu_lib):
+    """200 sequences x 4 KV heads = 800 (sequence, KV head) columns, more than
+    the attention work-groups resident at once: the dense and the sparse plans
+    grow their splits to whole lists (one split per column)."""
+    ts = gpu_lib
+    cfg = _cfg("g2-d64-bf16-b200", 200, 8, 4, 64, 300, "bf16", 65)
+    x = W.gen_decode(cfg, device="cuda")
+    lens = [1 + (37 * b) % cfg.seq_len for b in range(cfg.batch)]
+    x["seq_lens"] = torch.tensor(lens, dtype=torch.int32, device="cuda")
+    k = 128
+    g = torch.Generator(device="cpu").manual_seed(66)
+    idx = torch.full((cfg.batch, k), -1, dtype=torch.int32)
+    for b, n in enumerate(lens):
+        m = min(k, n)
+        idx[b, :m] = torch.sort(torch.randperm(n, generator=g)[:m]).values.int()
+    dense = ts.dense_attend(x["q"], x["k_cache"], x["v_cache"], x["seq_lens"])
+    sparse = ts.sparse_attend(x["q"], x["k_cache"], x["v_cache"], x["seq_lens"], idx.cuda())
+    torch.cuda.synchronize()
+    q64, od, osp = np64(x["q"]), np64(dense), np64(sparse)
+    for b in range(0, cfg.batch, 7):
+        n = lens[b]
+        K, V = np32(x["k_cache"][b, :n]), np32(x["v_cache"][b, :n])
+        check_attention(od[b], O.sparse_attention(q64[b], K, V, np.arange(n)), 2e-5)
+        check_attention(osp[b], O.sparse_attention(q64[b], K, V, idx[b].numpy()), 2e-5)
