@@ -196,6 +196,7 @@ __global__ __launch_bounds__(256) void attend_kernel(AttendParams p) {
     }
   };
 
+  // the row-group path (fp32 rows): GS query rows, running max, sum and acc
   uint32_t qw[GS][W];
   float m[GS], l[GS], acc[GS][EPL];
   // scores of a batch, one rescale of the running sums per batch
@@ -208,10 +209,7 @@ __global__ __launch_bounds__(256) void attend_kernel(AttendParams p) {
       for (int u = 0; u < UA; ++u) {
         float a = 0.f;
 #pragma unroll
-        for (int w = 0; w < W; ++w) {
-          if constexpr (DT == 1) a = dot2_bf16(kw[u][w], qw[hh][w], a);
-          else a = fmaf(__uint_as_float(kw[u][w]), __uint_as_float(qw[hh][w]), a);
-        }
+        for (int w = 0; w < W; ++w) a = fmaf(__uint_as_float(kw[u][w]), __uint_as_float(qw[hh][w]), a);
         sc[u] = ok[u] ? group_sum<LPR>(a) * p.scale2 : -INFINITY;
         bm = fmaxf(bm, sc[u]);
       }
@@ -230,12 +228,7 @@ __global__ __launch_bounds__(256) void attend_kernel(AttendParams p) {
       for (int e = 0; e < EPL; ++e) {
         float a = acc[hh][e] * corr;
 #pragma unroll
-        for (int u = 0; u < UA; ++u) {
-          float vf;
-          if constexpr (DT == 1) vf = (e & 1) ? bf16_hi(vw[u][e >> 1]) : bf16_lo(vw[u][e >> 1]);
-          else vf = __uint_as_float(vw[u][e]);
-          a = fmaf(pw[u], vf, a);
-        }
+        for (int u = 0; u < UA; ++u) a = fmaf(pw[u], __uint_as_float(vw[u][e]), a);
         acc[hh][e] = a;
       }
     }
