@@ -16,17 +16,21 @@
 // use v_dot2c_f32_bf16 (two bf16 products per instruction, fp32 accumulate);
 // the LPR partial sums are combined with DPP row operations (a reduce-scatter
 // that leaves each lane a few fully summed heads). Logits (base 2:
-// scale*log2(e)*q.k) are stored token-major, [B][Lpad][Hq], straight from the
-// registers: a token's Hq logits are contiguous, so the lanes of a row group
-// write one short contiguous run. Each (head, tile) leaves its max and sum of
-// exp2, folded from per-lane online values through a small LDS table.
+// scale*log2(e)*q.k) are staged in LDS and written token-major, [B][Lpad][Hq],
+// once per tile (a token's Hq logits are contiguous, so a tile is one
+// contiguous range); the streaming loop issues no global stores. Each (head,
+// tile) leaves its max and sum of exp2, folded from per-lane online values
+// through a small LDS table. In a decode step the work-groups also take the
+// Selection-Cache decision (selcache.h) and reset the top-k control blocks.
 //
-// Pass 2 (votes_kernel): every work-group first folds the tile partials into
-// each head's log-sum-exp (redundantly: a few KB from L2, and no cross-work-
-// group synchronisation, whose device-scope fences cost far more on this
-// multi-XCD part), then turns its logits into votes v[j] = sum_h
+// lse_kernel: one wave per (sequence, head) folds the tile partials into the
+// head's log-sum-exp (a kernel boundary is the cross-work-group step: device-
+// scope fences cost far more on this multi-XCD part).
+//
+// Pass 2 (votes_kernel) turns the logits into votes v[j] = sum_h
 // exp2(s[h,j] - lse[h]) and, for the decode path, adds them to the first
-// radix histogram of the top-k.
+// radix histogram of the top-k (an LDS histogram per work-group, flushed with
+// global atomics into one of up to four copies).
 #include "selcache.h"
 
 namespace ts {
