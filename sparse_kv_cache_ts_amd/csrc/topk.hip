@@ -14,11 +14,18 @@
 //      largest key from the finished histogram, sets the selection bits of
 //      its keys above b0 in a bitmap (one ballot per 64 keys), and appends the
 //      keys inside b0 to a short candidate list;
-//   3. finalize, one work-group per row: an exact radix select among the
-//      candidates (in LDS; a rescan of the row if the list overflowed) on the
-//      remaining 20 key bits, then on the index among exact ties so the lower
-//      indices win, sets their bits, and turns the bitmap into ascending
-//      indices with popcounts and a block scan.
+//   3. finalize, one work-group per row: the exact threshold among the
+//      candidates (in LDS; a rescan of the row if the list overflowed) from a
+//      histogram of key bits 19..10 and then either a direct ranking of the
+//      few keys of that second-level bin or further radix passes (key bits
+//      9..0, then the index among exact ties, so lower indices win); it sets
+//      their bits and turns the bitmap into ascending indices with popcounts
+//      and a block scan (topk_device.h holds the threshold search).
+// In a decode step the partition also counts bin b0's keys by bits 19..10
+// and step 3 runs inside the attention work-groups, each for its own token
+// range (attend.hip). Many short rows (a prefill chunk) take topk_row_kernel:
+// one 1024-thread work-group per row does all three steps with the row in
+// registers.
 #include "topk_device.h"
 
 namespace ts {
