@@ -78,6 +78,12 @@ __device__ __forceinline__ BinThreshold find_threshold(const List& L, uint32_t b
   const int tid = threadIdx.x;
   const int n = L.size();
   const uint32_t pre20 = b0;                       // key >> 20
+  // the second-level bin's keys as (key, index) pairs in s_hist[1024 ..], an
+  // append counter and the result after them; the counter is cleared before
+  // the barriers below
+  uint32_t* sub = s_hist + 1024;
+  uint32_t* cnt = s_hist + 1024 + 2 * kSubRank;
+  if (tid == 0) cnt[0] = 0u;
   if constexpr (!PRE) {
     // pass A: key bits 19..10
     for (int i = tid; i < 1024; i += NT) s_hist[i] = 0u;
@@ -88,17 +94,10 @@ __device__ __forceinline__ BinThreshold find_threshold(const List& L, uint32_t b
     }
     __syncthreads();
   }
-  const uint2 ra = resolve_lds<1024 / NT, NT>(s_hist, need, s_sh);
+  uint32_t nb;                                     // keys in the chosen bin (>= ra.y >= 1)
+  const uint2 ra = resolve_lds<1024 / NT, NT>(s_hist, need, s_sh, &nb);
   const uint32_t pre10 = (pre20 << 10) | ra.x;     // key >> 10
-  const uint32_t nb = s_hist[ra.x];                // keys in that bin (>= ra.y >= 1)
   if (nb <= kSubRank) {
-    // the bin's keys as (key, index) pairs in s_hist[1024 ..], a counter and
-    // the result after them
-    uint32_t* sub = s_hist + 1024;
-    uint32_t* cnt = s_hist + 1024 + 2 * kSubRank;
-    __syncthreads();                               // every thread has read s_hist[ra.x]
-    if (tid == 0) cnt[0] = 0u;
-    __syncthreads();
     for (int i = tid; i < n; i += NT) {
       const uint2 e = L.get(i);
       if ((e.x >> 10) == pre10) {
@@ -123,9 +122,8 @@ __device__ __forceinline__ BinThreshold find_threshold(const List& L, uint32_t b
       }
     }
     __syncthreads();
-    const BinThreshold th{pre20, cnt[1], cnt[2]};
-    __syncthreads();                               // s_hist is free again for the caller
-    return th;
+    // (callers write nothing into s_hist after this search)
+    return BinThreshold{pre20, cnt[1], cnt[2]};
   }
   // pass B: key bits 9..0
   for (int i = tid; i < 1024; i += NT) s_hist[i] = 0u;

@@ -250,11 +250,12 @@ __device__ __forceinline__ uint2 resolve_counts(const uint32_t (&c)[PER], uint32
 
 // Same over a histogram held in LDS (NT*PER bins).
 template <int PER, int NT>
-__device__ __forceinline__ uint2 resolve_lds(const uint32_t* hist, uint32_t need, uint32_t* sh) {
+__device__ __forceinline__ uint2 resolve_lds(const uint32_t* hist, uint32_t need, uint32_t* sh,
+                                             uint32_t* bin_count = nullptr) {
   uint32_t c[PER];
 #pragma unroll
   for (int i = 0; i < PER; ++i) c[i] = hist[threadIdx.x * PER + i];
-  return resolve_counts<PER, NT>(c, need, sh);
+  return resolve_counts<PER, NT>(c, need, sh, bin_count);
 }
 
 }  // namespace ts
