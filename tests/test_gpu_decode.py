@@ -341,3 +341,37 @@ def test_selcache_reset(gpu_lib):
     torch.cuda.synchronize()
     assert h0.tolist() == [0, 0] and h1.tolist() == [1, 1] and h2.tolist() == [0, 0]
     assert cache.stats(2) == ([0, 0], [1, 1])
+
+
+@pytest.mark.parametrize("n_copy", [5500, 11500], ids=["global-list", "row-rescan"])
+def test_decode_step_crowded_threshold_bin(gpu_lib, n_copy):
+    """Runs of identical keys give bitwise-equal votes, so the k-th vote's bin
+    holds every copy: more candidates than the attention work-groups stage in
+    LDS (5500: read from the global candidate list) or than the list keeps
+    (11500: each work-group rescans the vote row). The selection is then the
+    copies of lowest index (ties go to the lower index), exactly."""
+    ts = gpu_lib
+    Hq, Hkv, d, k = 8, 2, 64, 1000
+    n = 500 + n_copy
+    g = torch.Generator(device="cpu").manual_seed(97)
+    q = torch.randn(1, Hq, d, generator=g)
+    K = torch.randn(1, n, Hkv, d, generator=g)
+    V = torch.randn(1, n, Hkv, d, generator=g)
+    # the copies point along the mean query of each KV head's group: the
+    # largest votes of the row
+    for h in range(Hkv):
+        dirn = q[0, h * (Hq // Hkv):(h + 1) * (Hq // Hkv)].mean(0)
+        K[0, 500:, h] = 3.0 * dirn / dirn.norm() * d ** 0.5
+    q, K, V = q.to(torch.bfloat16).cuda(), K.to(torch.bfloat16).cuda(), V.to(torch.bfloat16).cuda()
+    lens = torch.tensor([n], dtype=torch.int32, device="cuda")
+    cache = ts.SelCache(1, Hq, d, k)
+    out, idx, hit = cache.decode_step(q, K, V, lens, 0.9)
+    torch.cuda.synchronize()
+    assert hit.cpu().tolist() == [0]
+    gidx = idx.cpu().numpy()[0]
+    q64, K32, V32 = np64(q)[0], np32(K)[0], np32(V)[0]
+    v_ref = _oracle_votes(q64, K32, n)
+    assert np.array_equal(gidx, O.top_k(v_ref, k))
+    assert np.array_equal(gidx, np.arange(500, 500 + k))
+    check_attention(np64(out)[0], O.sparse_attention(q64, K32, V32, gidx), 1e-2)
+    cache.close()
