@@ -375,3 +375,29 @@ def test_decode_step_crowded_threshold_bin(gpu_lib, n_copy):
     assert np.array_equal(gidx, np.arange(500, 500 + k))
     check_attention(np64(out)[0], O.sparse_attention(q64, K32, V32, gidx), 1e-2)
     cache.close()
+
+
+@pytest.mark.parametrize("ps", [1, 64, 512])
+def test_decode_step_paged_page_sizes(gpu_lib, ps):
+    """Paged decode steps with one-token pages, pages of 64 and pages larger
+    than a scoring tile: the selection equals the contiguous cache's (the
+    votes are the same bits) and the oracle's, the output matches the oracle."""
+    ts = gpu_lib
+    cfg = _small_cfg("paged-ps", 2, 8, 2, 128, 3000, "bf16", 256, 98, heavy=0.01)
+    x = W.gen_decode(cfg, device="cuda")
+    lens = [3000, 2111]
+    _varlen(x, lens)
+    c1 = ts.SelCache(2, 8, 128, 256)
+    _, idx_c, _ = c1.decode_step(x["q"], x["k_cache"], x["v_cache"], x["seq_lens"], 0.9)
+    kp, vp, pt = _to_paged(x["k_cache"], x["v_cache"], lens, ps, 99)
+    c2 = ts.SelCache(2, 8, 128, 256)
+    out, idx, hit = c2.decode_step(x["q"], kp, vp, x["seq_lens"], 0.9, page_table=pt)
+    torch.cuda.synchronize()
+    assert torch.equal(idx, idx_c)
+    q64, K32, V32 = np64(x["q"]), np32(x["k_cache"]), np32(x["v_cache"])
+    gidx, o = idx.cpu().numpy(), np64(out)
+    for b, n in enumerate(lens):
+        check_selection(gidx[b], _oracle_votes(q64[b], K32[b], n), 256)
+        check_attention(o[b], O.sparse_attention(q64[b], K32[b, :n], V32[b, :n], gidx[b]), 1e-2)
+    c1.close()
+    c2.close()
