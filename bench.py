@@ -362,6 +362,63 @@ def measure_quest(ts, W, steps, warmup):
             "tokenselect_kscan_bytes": kscan_bytes}
 
 
+def measure_selcache_run(ts, W):
+    """The selection-cache decode run as a whole: 256 steps over 8 paged
+    sequences of 16K..256K tokens (32/8 heads, d=128, bf16, page 16, top-4096)
+    with slowly drifting queries and a fresh random query every 32 steps,
+    theta = 0.9, the stored query compared with the previous step's. Returns
+    the mean step time over the run and each sequence's hits."""
+    import torch
+    cfg = W.SELCACHE_RUN
+    x = W.gen_run(cfg, device="cuda")
+    qs, lens, pt = x["queries"], x["seq_lens"], x["page_table"]
+    kp, vp = x["k_pool"], x["v_pool"]
+    B, Hq, d = cfg.batch, cfg.num_q_heads, cfg.head_dim
+    out = torch.empty(B, Hq, d, dtype=torch.float32, device="cuda")
+
+    def run():
+        cache = ts.SelCache(B, Hq, d, cfg.k)
+        for t in range(cfg.steps):
+            cache.decode_step(qs[t], kp, vp, lens, cfg.theta, page_table=pt, out=out,
+                              want_idx=False)
+        torch.cuda.synchronize()
+        return cache
+
+    run().close()                                    # warm-up run
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record()
+    cache = run()
+    e1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    hits, misses = cache.stats(B)
+    cache.close()
+    del x, kp, vp
+    torch.cuda.empty_cache()
+    return {"workload": f"{cfg.name}: {cfg.steps} steps, {B} paged sequences of "
+                        f"{cfg.min_len}..{cfg.max_len} tokens, {Hq}/{cfg.num_kv_heads} heads, "
+                        f"d={d}, bf16, page {cfg.page_size}, top-{cfg.k}, theta {cfg.theta}, "
+                        f"a fresh query every {cfg.jump_every} steps",
+            "us_per_step": round(1e6 * wall / cfg.steps, 2),
+            "gpu_us_per_step": round(1e3 * e0.elapsed_time(e1) / cfg.steps, 2),
+            "hits": hits, "misses": misses}
+
+
+def measure_configs(ts, W, steps, warmup):
+    """Decode steps (selection every step) at the other decode shapes."""
+    res = {}
+    for name, cfg, copies in (("qwen2-7b-shape-32k", W.QWEN_32K, 6),
+                              ("llama3-8b-shape-4x128k", W.LLAMA_4x128K, 2)):
+        r, _ = measure_decode(ts, W, cfg, steps, warmup, copies, 1.0, False, name)
+        res[name] = {"batch": cfg.batch, "seq_len": cfg.seq_len, "k": cfg.k,
+                     "heads": f"{cfg.num_q_heads}/{cfg.num_kv_heads}",
+                     "us_per_step": round(1e3 * r["ms_per_step"], 2),
+                     "steps_per_s": round(r["steps_per_s"], 1)}
+    return res
+
+
 def cpu_baseline(O, W, cfg, x, seconds):
     """The fp64 oracle (as written, untuned) on host copies of the same inputs."""
     import numpy as np
@@ -404,6 +461,8 @@ def main():
     ap.add_argument("--no-loop", action="store_true", help="skip the multi-layer decode loop")
     ap.add_argument("--loop-layers", type=int, default=28)
     ap.add_argument("--no-quest", action="store_true", help="skip the page-selection variant")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="skip the 32K and 4x128K decode shapes and the 256-step selection-cache run")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 512 MiB copy kernel (for HBM byte counters)")
     args = ap.parse_args()
@@ -478,6 +537,11 @@ def main():
 
     if not args.no_quest:
         extra["quest_pages"] = measure_quest(ts, W, max(1, args.steps // 4), max(1, args.warmup // 4))
+
+    if not args.no_configs:
+        extra["other_decode_shapes"] = measure_configs(ts, W, max(1, args.steps // 2),
+                                                       max(1, args.warmup // 2))
+        extra["selcache_run"] = measure_selcache_run(ts, W)
 
     cpu = None
     if not args.no_cpu_baseline:
