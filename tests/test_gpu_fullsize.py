@@ -116,3 +116,16 @@ def test_decode_step_300k_tokens(gpu_lib):
                          head_dim=128, seq_len=300000, dtype="bf16", k=4096, seed=78,
                          heavy_frac=0.01)
     _decode_full(gpu_lib, cfg)
+
+
+@pytest.mark.parametrize("cfg", [
+    W.DecodeConfig("g8-d64-bf16-131k", batch=2, num_q_heads=32, num_kv_heads=4, head_dim=64,
+                   seq_len=131072, dtype="bf16", k=2048, seed=79, heavy_frac=0.01),
+    W.DecodeConfig("g4-d128-f32-65k", batch=1, num_q_heads=16, num_kv_heads=4, head_dim=128,
+                   seq_len=65536, dtype="f32", k=1024, seed=80, heavy_frac=0.01),
+], ids=lambda c: c.name)
+def test_decode_step_other_full_sizes(gpu_lib, cfg):
+    """head_dim 64 on the matrix-core attention (2 k-steps, one 16-dimension
+    tile per wave) and fp32 rows (the row-group attention), both with the
+    selection finished inside the attention work-groups."""
+    _decode_full(gpu_lib, cfg)
