@@ -34,7 +34,9 @@
  *     ts_sel_cache must be ordered on one stream.
  *
  * Supported shapes: head_dim 64 or 128; dtype fp32 or bf16 (q, K and V share
- * it; accumulation is fp32); num_kv_heads divides num_q_heads; num_kv_heads <= 64.
+ * it; accumulation is fp32); num_kv_heads divides num_q_heads; num_kv_heads <= 64 for
+ * bf16, <= 32 for fp32 with head_dim 64 and <= 16 for fp32 with head_dim 128 (one scoring
+ * work-group holds a token's rows of every KV head); other shapes return TS_ERR_UNSUPPORTED.
  */
 #ifndef TS_H
 #define TS_H

@@ -60,6 +60,8 @@ def _ws_size(fn, *args):
     (dict(ps=12, stride=100), ts.TS_ERR_INVALID_ARG),  # page size not a power of two
     (dict(ps=16, stride=10), ts.TS_ERR_INVALID_ARG),   # page table too short for max_len
     (dict(Hq=128, Hkv=128), ts.TS_ERR_UNSUPPORTED),  # too many KV heads
+    (dict(Hq=32, Hkv=32, dtype=ts.TS_F32), ts.TS_ERR_UNSUPPORTED),         # fp32 d=128: <= 16
+    (dict(Hq=64, Hkv=64, d=64, dtype=ts.TS_F32), ts.TS_ERR_UNSUPPORTED),  # fp32 d=64: <= 32
     (dict(scale=float("inf")), ts.TS_ERR_INVALID_ARG),
 ])
 def test_layout_validation(kw, want):
@@ -68,6 +70,15 @@ def test_layout_validation(kw, want):
     st, _ = _ws_size(lib.ts_score_workspace_size, ctypes.byref(L), 1)
     assert st == want
     assert lib.ts_last_error().decode() != ""
+
+
+@pytest.mark.parametrize("kw", [dict(Hq=64, Hkv=64), dict(Hq=16, Hkv=16, dtype=ts.TS_F32),
+                                dict(Hq=32, Hkv=32, d=64, dtype=ts.TS_F32)])
+def test_layout_kv_head_limits_accepted(kw):
+    lib = _lib()
+    L = _layout(**kw)
+    st, n = _ws_size(lib.ts_score_workspace_size, ctypes.byref(L), 1)
+    assert st == 0 and n > 0
 
 
 def test_workspace_sizes_positive_and_monotone():
