@@ -87,7 +87,7 @@ __global__ __launch_bounds__(256) void topk_hist0_kernel(TopkParams p) {
 
 // ---- step 2: partition into selected bits / threshold-bin candidates --------
 __global__ __launch_bounds__(256) void topk_partition_kernel(TopkParams p) {
-  constexpr int PER = kTopkChunk / 256;           // 16 keys per thread
+  constexpr int PER = kTopkChunk / 256;           // 8 keys per thread
   constexpr int SHIFT = 32 - kHist0Bits;
   __shared__ uint32_t s_sh[8];
   __shared__ uint32_t s_base;

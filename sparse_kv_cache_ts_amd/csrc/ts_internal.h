@@ -12,7 +12,7 @@ namespace ts {
 // ---- tiling constants -------------------------------------------------------
 constexpr int kScoreTileMax = 256; // largest token tile of a scoring work-group (128 or 256)
 constexpr int kVoteTile = 256;     // tokens per vote work-group (pass 2)
-constexpr int kTopkChunk = 4096;   // elements per top-k work-group
+constexpr int kTopkChunk = 2048;   // elements per top-k histogram/partition work-group
 constexpr int kMaxHeadsPerWG = 64; // Hkv * heads-per-slice held by one scoring WG
 constexpr int kMaxQHeads = 256;
 constexpr int kMaxSplits = 1024;  // attention splits per (sequence, head)
