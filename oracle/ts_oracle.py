@@ -48,7 +48,8 @@ textbook results (full attention when k = N, a library sort when Hq = Hkv =
 1, exhaustive subset search on tiny inputs), invariants (per-head softmax
 sums to 1, votes sum to Hq, permutation invariance), a hand-derived worked
 example (tests/golden/worked_example.txt), closed forms of the
-selection-cache decisions, and planted-mistake tests.
+selection-cache decisions, a hand-written paged pool for the paged-layout
+helper (tests/golden/paged_layout.txt), and planted-mistake tests.
 """
 from __future__ import annotations
 

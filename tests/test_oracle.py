@@ -253,6 +253,25 @@ def pin_edge_cases():
     assert not hit and not cache.valid and (out == 0).all()
 
 
+def pin_paged_layout():
+    """The paged-layout helper against a hand-written pool whose rows name
+    their own (page, slot): a shuffled page table, an unused pool page and a
+    partial last page (tests/golden/paged_layout.txt)."""
+    g = golden.load("paged_layout.txt")
+    P, npages = int(g["page_size"][0]), int(g["pages"][0])
+    pool = np.zeros((npages, P, 1, 2))
+    for pg in range(npages):
+        for s in range(P):
+            pool[pg, s, 0] = [10 * pg + s, -(10 * pg + s)]
+    pt = np.array([int(x) for x in g["page_table"]])
+    rows = O.paged_to_contiguous(pool, pt, int(g["n"][0]))
+    assert rows.shape == (int(g["n"][0]), 1, 2)
+    assert rows[:, 0, 0].tolist() == g["rows_ch0"]
+    assert rows[:, 0, 1].tolist() == g["rows_ch1"]
+    short = O.paged_to_contiguous(pool, pt, int(g["n_short"][0]))
+    assert short[:, 0, 0].tolist() == g["rows_short_ch0"]
+
+
 PINS = {name: fn for name, fn in list(globals().items()) if name.startswith("pin_")}
 
 
@@ -367,7 +386,14 @@ def _mut_prefill_offbyone(Q, K, q_pos0, rows=None, scale=None):
             for i in rows]
 
 
+def _mut_paged_swapped(pool, page_table_row, n):
+    P = pool.shape[1]
+    j = np.arange(n)
+    return pool[page_table_row[j % P], j // P]
+
+
 MUTANTS = {
+    "paged_page_slot_swapped": ("paged_to_contiguous", _mut_paged_swapped),
     "scale_dropped": ("default_scale", _mut_scale),
     "gqa_map_modulo": ("kv_head_of", _mut_kv_head),
     "softmax_over_heads": ("head_softmax", _mut_softmax_axis),
