@@ -251,8 +251,15 @@ typedef struct ts_sel_cache ts_sel_cache;
 /* Allocates the device state (hipMalloc) and zeroes it; synchronises the device. */
 ts_status ts_sel_cache_create(int32_t max_batch, int32_t num_q_heads, int32_t head_dim, int32_t k,
                               int32_t compare_mode, ts_sel_cache** out /*[host]*/);
-/* Marks every sequence invalid and clears the counters (asynchronous on stream). */
-ts_status ts_sel_cache_reset(ts_sel_cache* cache, void* stream);
+/* Marks sequences invalid and clears their hit/miss counters, so that their
+ * next step misses (TokenSelect README, "Key Takeaways", third point: the
+ * Selection Cache is state of one sequence; a batch slot that a new sequence
+ * takes over must not reuse the previous occupant's query or selection).
+ *   seq_mask  [max_batch] int32 (device) or NULL: sequence b is reset where
+ *             seq_mask[b] != 0; NULL resets every sequence.
+ * One small kernel on `stream` (no memset and no allocation, so the call can
+ * be captured in a HIP graph); asynchronous like a decode step. */
+ts_status ts_sel_cache_reset(ts_sel_cache* cache, const int32_t* seq_mask, void* stream);
 /* Frees the device state; synchronises the device. */
 ts_status ts_sel_cache_destroy(ts_sel_cache* cache);
 /* Copies hit and miss counts of sequences 0..n-1 to host arrays; synchronises `stream`. */

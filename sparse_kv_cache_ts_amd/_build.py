@@ -33,23 +33,23 @@ def sources() -> list:
     return [os.path.join(CSRC, f) for f in names]
 
 
-def _compile(src: str, out_dir: str = OUT_DIR, defines=()) -> str:
+def _compile(src: str, out_dir: str = OUT_DIR) -> str:
     obj = os.path.join(out_dir, os.path.basename(src) + ".o")
-    cmd = [HIPCC, *COMMON, *[f"-D{d}" for d in defines], "-x", "hip", "-c", src, "-o", obj]
+    cmd = [HIPCC, *COMMON, "-x", "hip", "-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed on {src}:\n{r.stderr}")
     return obj
 
 
-def build(verbose: bool = True, lib: str = LIB, defines=()) -> str:
-    """Compile every source and link `lib` (default: the in-tree libts.so)."""
-    out_dir = OUT_DIR if lib == LIB else lib + ".objs"
+def build(verbose: bool = True) -> str:
+    """Compile every source and link the in-tree libts.so."""
+    out_dir, lib = OUT_DIR, LIB
     os.makedirs(out_dir, exist_ok=True)
     srcs = sources()
     jobs = min(len(srcs), int(os.environ.get("MAX_JOBS", "8")), 16)
     with ThreadPoolExecutor(max_workers=max(1, jobs)) as ex:
-        objs = list(ex.map(lambda f: _compile(f, out_dir, defines), srcs))
+        objs = list(ex.map(lambda f: _compile(f, out_dir), srcs))
     tmp = lib + ".tmp"
     cmd = [HIPCC, "-shared", "-fPIC", f"--offload-arch={ARCH}", *objs, "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)

@@ -116,12 +116,17 @@ __global__ __launch_bounds__(256) void attend_kernel(AttendParams p) {
       const uint4 hb = ld16(ctrl + kCtlHistB + 4 * tid);
       const int w0 = r0 >> 5, wr = (r1 - r0 + 31) >> 5;
       uint32_t rw = tid < wr ? bm[w0 + tid] : 0u;
-      // selected base bits before the range (16-byte loads, clamped, masked)
+      // selected base bits before the range: 16-byte loads of whole groups of
+      // four words below w0 (the row's bitmap is 16-byte aligned), then single
+      // words for a partial last group, so no word at or past w0 is counted
       uint32_t pc = 0;
       for (int w = 4 * tid; w < w0; w += 4 * 256) {
-        const uint4 q4 = *reinterpret_cast<const uint4*>(bm + min(w, w0 - 4));
-        pc += (w + 0 < w0 ? __popc(q4.x) : 0u) + (w + 1 < w0 ? __popc(q4.y) : 0u) +
-              (w + 2 < w0 ? __popc(q4.z) : 0u) + (w + 3 < w0 ? __popc(q4.w) : 0u);
+        if (w + 4 <= w0) {
+          const uint4 q4 = *reinterpret_cast<const uint4*>(bm + w);
+          pc += (__popc(q4.x) + __popc(q4.y)) + (__popc(q4.z) + __popc(q4.w));
+        } else {
+          for (int i = w; i < w0; ++i) pc += __popc(bm[i]);
+        }
       }
 #pragma unroll
       for (int i = 0; i < kCandLds / 256; ++i) {

@@ -491,11 +491,7 @@ template <int DT, int D, bool PAGED, int TILE>
 static hipError_t launch_pass1_gs(const ScoreParams& p, hipStream_t s) {
   dim3 grid(p.ntiles, p.B * p.nslices);
   const size_t shmem = (size_t)TILE * p.Hkv * p.GS * sizeof(float);
-#ifdef TS_SCORE_LPR
-  constexpr int LPR = TS_SCORE_LPR;
-#else
   constexpr int LPR = score_lpr<DT, D>();
-#endif
   switch (p.GS) {
 #define TS_GS(n) case n: TS_KLAUNCH((score_pass1_kernel<DT, D, n, PAGED, TILE, LPR>), grid, dim3(256), shmem, s, p); break;
     TS_GS(1) TS_GS(2) TS_GS(3) TS_GS(4) TS_GS(5) TS_GS(6) TS_GS(7) TS_GS(8)

@@ -1,5 +1,6 @@
 // selcache.hip — per-call prologue: control-block reset and, for callers
-// that do not fuse it into scoring, the Selection-Cache decision (selcache.h).
+// that do not fuse it into scoring, the Selection-Cache decision (selcache.h);
+// and the per-sequence reset of the Selection-Cache state.
 #include "selcache.h"
 
 namespace ts {
@@ -21,14 +22,20 @@ __global__ __launch_bounds__(256) void prologue_kernel(PrologueParams p) {
   }
 }
 
-__global__ __launch_bounds__(256) void fill_zero_kernel(uint32_t* p, size_t n) {
-  for (size_t i = blockIdx.x * 256ull + threadIdx.x; i < n; i += (size_t)gridDim.x * 256ull) p[i] = 0u;
+// Selection-Cache reset of the sequences whose mask entry is non-zero (all
+// sequences when the mask is null): they become invalid, so their next step
+// misses, and their counters restart from zero.
+__global__ __launch_bounds__(256) void sel_reset_kernel(SelCacheDev c, const int32_t* mask) {
+  const int b = blockIdx.x * 256 + threadIdx.x;
+  if (b >= c.max_batch) return;
+  if (mask && mask[b] == 0) return;
+  c.valid[b] = 0;
+  c.hits[b] = 0;
+  c.misses[b] = 0;
 }
 
-hipError_t launch_fill_zero(void* ptr, size_t words, hipStream_t s) {
-  if (words == 0) return hipSuccess;
-  const int grid = (int)((words + 255) / 256 < 1024 ? (words + 255) / 256 : 1024);
-  TS_KLAUNCH(fill_zero_kernel, dim3(grid), dim3(256), 0, s, (uint32_t*)ptr, words);
+hipError_t launch_sel_reset(const SelCacheDev& c, const int32_t* mask, hipStream_t s) {
+  TS_KLAUNCH(sel_reset_kernel, dim3((c.max_batch + 255) / 256), dim3(256), 0, s, c, mask);
   return hipGetLastError();
 }
 

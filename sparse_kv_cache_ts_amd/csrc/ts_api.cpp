@@ -49,11 +49,11 @@ ts_status hip_check(hipError_t e, const char* what) {
 // ---- kernel-level timing (ts_profile_*) ---------------------------------------
 enum KernelKind {
   kKPrologue, kKScore, kKLse, kKVotes, kKTopkHist, kKTopkPartition, kKTopkFinalize, kKAttend,
-  kKCombine, kKPrefillLse, kKPrefillVotes, kKFill, kKAppend, kKQuestMeta, kKQuestScore, kKTopkRow, kKNum
+  kKCombine, kKPrefillLse, kKPrefillVotes, kKSelReset, kKAppend, kKQuestMeta, kKQuestScore, kKTopkRow, kKNum
 };
 const char* const kKernelNames[kKNum] = {
   "prologue", "score_pass1", "lse", "votes", "topk_hist", "topk_partition", "topk_finalize",
-  "attend", "combine", "prefill_lse", "prefill_votes", "fill_zero", "append_kv", "quest_meta",
+  "attend", "combine", "prefill_lse", "prefill_votes", "sel_reset", "append_kv", "quest_meta",
   "quest_score", "topk_row"
 };
 
@@ -237,9 +237,6 @@ void plan_score(const Geo& g, int B, Carve& c, ScorePlan& s) {
   s.tile = wg256 >= 512 ? 256 : 128;
   // the tile's logits are staged in LDS: keep that within 48 KB
   if ((long)s.tile * g.Hkv * g.GS * 4 > 48 * 1024) s.tile = 128;
-#ifdef TS_FORCE_SCORE_TILE
-  s.tile = TS_FORCE_SCORE_TILE;   // build-time override for tuning sweeps
-#endif
   s.ntiles = cdiv(g.max_len, s.tile);
   s.Lpad = cdiv(g.max_len, kVoteTile) * kVoteTile;
   s.ctrl = c.take((size_t)B * kCtrlStride * 4);
@@ -326,7 +323,10 @@ int sel_range_for(const Geo& g, int B, int k) {
   while (range < kSelRangeMax && (long)range * k < 32l * g.max_len) range <<= 1;
   const long wgs = (long)B * g.Hkv * g.nslices * cdiv(g.max_len, range);
   if ((long)range * k < 32l * g.max_len || wgs > kSelMaxWGs) return 0;
-  return range;
+  // a range starts on a whole 32-bit bitmap word (and on a 16-byte group of
+  // them, the attention kernel's fast path for the bits before its range)
+  static_assert(kSelRangeMax % 128 == 0, "selection ranges are multiples of 128 tokens");
+  return (range % 128 == 0) ? range : 0;
 }
 
 void plan_decode(const Geo& g, int B, int k, DecodePlan& p) {
@@ -938,13 +938,10 @@ ts_status ts_sel_cache_create(int32_t max_batch, int32_t num_q_heads, int32_t he
   return ok();
 }
 
-ts_status ts_sel_cache_reset(ts_sel_cache* c, void* stream) {
+ts_status ts_sel_cache_reset(ts_sel_cache* c, const int32_t* seq_mask, void* stream) {
   if (!c) return fail(TS_ERR_INVALID_ARG, "cache is NULL");
   hipStream_t st = static_cast<hipStream_t>(stream);
-  const size_t n = (size_t)c->dev.max_batch;
-  TS_LAUNCH_K(kKFill, launch_fill_zero(c->dev.valid, n, st), "reset");
-  TS_LAUNCH_K(kKFill, launch_fill_zero(c->dev.hits, 2 * n, st), "reset");
-  TS_LAUNCH_K(kKFill, launch_fill_zero(c->dev.misses, 2 * n, st), "reset");
+  TS_LAUNCH_K(kKSelReset, launch_sel_reset(c->dev, seq_mask, st), "reset");
   return ok();
 }
 

@@ -236,7 +236,9 @@ struct PrefillParams {
 
 // ---- launchers (defined in the .hip sources) --------------------------------
 hipError_t launch_prologue(const PrologueParams& p, int grid, hipStream_t s);
-hipError_t launch_fill_zero(void* ptr, size_t words, hipStream_t s);   // 32-bit words
+// Selection-Cache reset: valid, hits and misses of sequence b cleared where
+// mask[b] != 0 (mask null: every sequence)
+hipError_t launch_sel_reset(const SelCacheDev& c, const int32_t* mask, hipStream_t s);
 hipError_t launch_score_pass1(int dtype, int d, bool paged, const ScoreParams& p, hipStream_t s);
 hipError_t launch_lse(const LseParams& p, hipStream_t s);
 hipError_t launch_votes(const VoteParams& p, int grid_x, hipStream_t s);

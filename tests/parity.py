@@ -114,8 +114,10 @@ def check_run(ts, rc, mode: int, theta: float, sel_steps=None, att_steps=None, d
     sel_set = None if sel_steps is None else set(sel_steps)
     att_set = None if att_steps is None else set(att_steps)
     for b in range(B):
-        Kb = O.paged_to_contiguous(kp, ptn[b], lens[b])
-        Vb = O.paged_to_contiguous(vp, ptn[b], lens[b])
+        # exact fp64 copies once per sequence (the oracle's dot products then
+        # run on contiguous fp64 rows instead of upcasting on every call)
+        Kb = O.paged_to_contiguous(kp, ptn[b], lens[b]).astype(np.float64)
+        Vb = O.paged_to_contiguous(vp, ptn[b], lens[b]).astype(np.float64)
         ref_cache = O.SelectionCache(mode)
         for t in range(rc.steps):
             hit_ref, c = ref_cache.decide(Q[t, b], theta)
@@ -133,4 +135,5 @@ def check_run(ts, rc, mode: int, theta: float, sel_steps=None, att_steps=None, d
                 ref_cache.prev_q = Q[t, b].copy()
             ref_cache.prev_S = sels[t, b]
             ref_cache.valid = True
+        del Kb, Vb
     return hits

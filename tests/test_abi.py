@@ -167,5 +167,5 @@ def test_sel_cache_argument_errors():
     assert lib.ts_sel_cache_create(1, 28, 128, 0, 0, ctypes.byref(h)) == ts.TS_ERR_INVALID_ARG
     assert lib.ts_sel_cache_create(1, 28, 128, 16, 2, ctypes.byref(h)) == ts.TS_ERR_INVALID_ARG
     assert lib.ts_sel_cache_create(1, 28, 128, 16, 0, None) == ts.TS_ERR_INVALID_ARG
-    assert lib.ts_sel_cache_reset(None, None) == ts.TS_ERR_INVALID_ARG
+    assert lib.ts_sel_cache_reset(None, None, None) == ts.TS_ERR_INVALID_ARG
     assert lib.ts_sel_cache_destroy(None) == ts.TS_OK

@@ -343,6 +343,55 @@ def test_selcache_reset(gpu_lib):
     assert cache.stats(2) == ([0, 0], [1, 1])
 
 
+def test_selcache_reset_one_sequence(gpu_lib):
+    """A per-sequence reset in the middle of a run (a new sequence taking
+    over batch slot 1): slot 1's next step misses, slots 0 and 2 keep
+    hitting. Every decision matches the oracle's cache, whose state for slot
+    1 alone is reset at the same step; hits repeat the previous selection,
+    misses select what the oracle selects, and the counters restart."""
+    ts = gpu_lib
+    rc = W.RunConfig("reset-one-of-three", steps=12, batch=3, num_q_heads=8, num_kv_heads=2,
+                     head_dim=128, min_len=600, max_len=1500, dtype="bf16", k=64, seed=43,
+                     jump_every=0)
+    x = W.gen_run(rc, device="cuda")
+    B, t_reset = rc.batch, 6
+    cache = ts.SelCache(B, rc.num_q_heads, rc.head_dim, rc.k)
+    mask = torch.tensor([0, 1, 0], dtype=torch.int32, device="cuda")
+    hits, sels = [], []
+    for t in range(rc.steps):
+        if t == t_reset:
+            cache.reset(seq_mask=mask)
+        _, idx, hit = cache.decode_step(x["queries"][t], x["k_pool"], x["v_pool"], x["seq_lens"],
+                                        rc.theta, page_table=x["page_table"])
+        hits.append(hit.clone())
+        sels.append(idx.clone())
+    torch.cuda.synchronize()
+    hits = torch.stack(hits).cpu().numpy()
+    sels = torch.stack(sels).cpu().numpy()
+    expect = np.ones((rc.steps, B), dtype=np.int32)
+    expect[0] = 0
+    expect[t_reset, 1] = 0
+    assert (hits == expect).all(), hits.T
+    h, m = cache.stats(B)
+    cache.close()
+    assert h == [rc.steps - 1, rc.steps - t_reset - 1, rc.steps - 1] and m == [1, 1, 1]
+    lens = x["seq_lens"].tolist()
+    kp, ptn, Q = np32(x["k_pool"]), x["page_table"].cpu().numpy(), np64(x["queries"])
+    for b in range(B):
+        Kb = O.paged_to_contiguous(kp, ptn[b], lens[b])
+        ref = O.SelectionCache(0)
+        for t in range(rc.steps):
+            if t == t_reset and b == 1:
+                ref.reset()
+            hit_ref, c = ref.decide(Q[t, b], rc.theta)
+            assert bool(hits[t, b]) == hit_ref, f"seq {b} step {t}: cos {c}"
+            if hits[t, b]:
+                assert np.array_equal(sels[t, b], sels[t - 1, b])
+            else:
+                check_selection(sels[t, b], _oracle_votes(Q[t, b], Kb, lens[b]), rc.k)
+            ref.prev_q, ref.prev_S, ref.valid = Q[t, b].copy(), sels[t, b], True
+
+
 @pytest.mark.parametrize("n_copy", [5500, 11500], ids=["global-list", "row-rescan"])
 def test_decode_step_crowded_threshold_bin(gpu_lib, n_copy):
     """Runs of identical keys give bitwise-equal votes, so the k-th vote's bin

@@ -7,7 +7,8 @@
   heavy keys and with 16 planted keys.
 * The tiny fp32 case (4/2 heads, d=64, 4096 tokens, 16 planted keys).
 * The 256-step selection-cache run over 8 paged sequences of 16K..256K
-  tokens (theta = 0.9): every decision, sampled selections and outputs.
+  tokens (theta = 0.9): every decision, every miss step's selection and
+  every step's output.
 
 The oracle runs on exact host copies of the same inputs.
 """
@@ -80,11 +81,13 @@ def test_score_votes_full_size(gpu_lib):
     assert abs(v.sum() - cfg.num_q_heads) < 1e-4 * cfg.num_q_heads
 
 
+@pytest.mark.timeout(1200)
 def test_selection_cache_run_full_size(gpu_lib):
-    """256 steps x 8 paged sequences: misses exactly at the jumps (t % 32 == 0)."""
+    """256 steps x 8 paged sequences: misses exactly at the jumps (t % 32 == 0);
+    every decision, the selection of every miss step (8 per sequence) and the
+    attention output of every step (2048 in all) against the oracle."""
     rc = W.SELCACHE_RUN
-    hits = check_run(gpu_lib, rc, 0, rc.theta, sel_steps=[0, 224],
-                     att_steps=[0, 1, 2, 31, 32, 33, 127, 255])
+    hits = check_run(gpu_lib, rc, 0, rc.theta, sel_steps=None, att_steps=None)
     for t in range(rc.steps):
         assert (hits[t] == (0 if t % rc.jump_every == 0 else 1)).all(), f"step {t}"
 

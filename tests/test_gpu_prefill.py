@@ -73,21 +73,31 @@ def test_prefill_score_matches_select_votes(gpu_lib):
     assert torch.equal(v1, v2)
 
 
-def test_prefill_full_size_sampled_rows(gpu_lib):
-    """512 queries over 65536 keys, 32/8 heads, d=128: sampled rows vs the oracle."""
+@pytest.mark.timeout(900)
+def test_prefill_full_size(gpu_lib):
+    """512 queries over 65536 keys, 32/8 heads, d=128, in the launch bench.py
+    times. Every row: zeros past its causal limit, a sum of Hq, and a
+    selection equal to the exact top-k (oracle rule) of the GPU's own vote
+    row. 64 rows spread over the chunk, the first and last included: votes
+    entry by entry and the decided-token rule against the oracle."""
     ts = gpu_lib
     cfg = W.PREFILL_64K
     x = W.gen_prefill(cfg, device="cuda")
     q0 = x["q_pos0"]
     votes, idx = ts.select_prefill(x["q"], x["k_cache"], q0, cfg.k)
     torch.cuda.synchronize()
-    # every row sums to Hq and is zero past its causal limit
     sums = votes.double().sum(dim=1)
     assert torch.allclose(sums, torch.full_like(sums, cfg.num_q_heads), rtol=1e-4)
-    rows = [0, 1, 63, 64, 255, 300, 510, 511]
-    Q, K = np64(x["q"]), np32(x["k_cache"])
-    refs = O.prefill_votes(Q, K, q0, rows=rows)
+    V32 = np32(votes)
     gi = idx.cpu().numpy()
+    for r in range(cfg.chunk):
+        n = q0 + r + 1
+        assert (V32[r, n:] == 0).all(), f"row {r}: votes past the causal limit"
+        assert np.array_equal(gi[r], O.top_k(V32[r, :n].astype(np.float64), cfg.k)), f"row {r}"
+    rows = sorted(set(np.linspace(0, cfg.chunk - 1, 64).round().astype(int).tolist()))
+    assert rows[0] == 0 and rows[-1] == cfg.chunk - 1 and len(rows) == 64
+    Q, K = np64(x["q"]), np64(x["k_cache"])
+    refs = O.prefill_votes(Q, K, q0, rows=rows)
     for r, ref in zip(rows, refs):
         _check_votes(votes[r], ref, q0 + r + 1, cfg.num_q_heads)
         check_selection(gi[r], ref, cfg.k)
@@ -152,8 +162,10 @@ def test_prefill_sparse_attention_skips_invalid(gpu_lib):
         check_attention(o[i], ref, 1e-2)
 
 
+@pytest.mark.timeout(900)
 def test_prefill_sparse_attention_full_size(gpu_lib):
-    """512 x 65536, top-4096 per query: sampled rows against the oracle."""
+    """512 x 65536, top-4096 per query: every row's output against the
+    oracle's attention over that row's own selection."""
     from tests.parity import check_attention
     ts = gpu_lib
     cfg = W.PREFILL_64K
@@ -162,8 +174,8 @@ def test_prefill_sparse_attention_full_size(gpu_lib):
     _, idx = ts.select_prefill(x["q"], x["k_cache"], q0, cfg.k)
     out = ts.sparse_attend_prefill(x["q"], x["k_cache"], x["v_cache"], q0, idx)
     torch.cuda.synchronize()
-    Q, K, V = np64(x["q"]), np32(x["k_cache"]), np32(x["v_cache"])
+    Q, K, V = np64(x["q"]), np64(x["k_cache"]), np64(x["v_cache"])
     gi, o = idx.cpu().numpy(), np64(out)
-    for i in [0, 1, 200, 511]:
+    for i in range(cfg.chunk):
         n = q0 + i + 1
         check_attention(o[i], O.sparse_attention(Q[i], K[:n], V[:n], gi[i]), 1e-2)
