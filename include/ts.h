@@ -286,6 +286,30 @@ ts_status ts_decode_step(ts_sel_cache* cache, const ts_kv_layout* layout /*[host
                          size_t ws_bytes, void* stream);
 
 /* ---------------------------------------------------------------------------
+ * ts_decode_step_noalloc — ts_decode_step for callers that cannot allocate
+ * device memory or pass a workspace (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc). Same arguments, kernels and
+ * results as ts_decode_step, without ws/ws_bytes: the workspace is a static
+ * device array of TS_NOALLOC_SCRATCH_BYTES (32 MiB) inside the library, one
+ * per GPU, held until the process ends; its address is looked up when a
+ * ts_sel_cache is created on that GPU. The call allocates nothing.
+ *   Steps whose ts_decode_step_workspace_size exceeds TS_NOALLOC_SCRATCH_BYTES
+ *   return TS_ERR_WORKSPACE (e.g. one Qwen2-7B-shape layer of 131072 tokens
+ *   needs about 17 MB and fits; batches of several such sequences do not).
+ *   The calling thread's current device must be the cache's device.
+ *   Every call on one GPU shares that GPU's array: calls that overlap in time
+ *   on one GPU (other streams, other threads) race and must be ordered by the
+ *   caller. A call leaves the array holding its intermediates; each call
+ *   clears what it needs cleared itself, in its kernels.
+ * ------------------------------------------------------------------------- */
+#define TS_NOALLOC_SCRATCH_BYTES (32u << 20)
+ts_status ts_decode_step_noalloc(ts_sel_cache* cache, const ts_kv_layout* layout /*[host]*/,
+                                 int32_t batch, const void* q, const void* k_cache,
+                                 const void* v_cache, const int32_t* page_table,
+                                 const int32_t* seq_lens, double theta, float* out,
+                                 int32_t* idx_out, int32_t* hit_out, void* stream);
+
+/* ---------------------------------------------------------------------------
  * ts_score_prefill — steps 1-2 for a chunk of `chunk` consecutive queries
  * (bf16 MFMA for the query-key products; fp32 softmax and votes).
  *   q        [chunk][Hq][d] bf16, query i at absolute position q_pos0 + i

@@ -33,6 +33,7 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 _LIB = None
 
 TS_OK, TS_ERR_INVALID_ARG, TS_ERR_UNSUPPORTED, TS_ERR_WORKSPACE, TS_ERR_HIP = range(5)
+NOALLOC_SCRATCH_BYTES = 32 << 20   # TS_NOALLOC_SCRATCH_BYTES of include/ts.h
 TS_F32, TS_BF16 = 0, 1
 
 # every symbol include/ts.h declares
@@ -47,7 +48,7 @@ EXPORTS = [
     "ts_quest_meta", "ts_quest_select_workspace_size", "ts_quest_select",
     "ts_quest_attend_workspace_size", "ts_quest_attend",
     "ts_sel_cache_create", "ts_sel_cache_reset", "ts_sel_cache_destroy", "ts_sel_cache_stats",
-    "ts_decode_step_workspace_size", "ts_decode_step",
+    "ts_decode_step_workspace_size", "ts_decode_step", "ts_decode_step_noalloc",
     "ts_score_prefill_workspace_size", "ts_score_prefill", "ts_select_prefill",
     "ts_profile_num_kernels", "ts_profile_kernel_name", "ts_profile_enable", "ts_profile_reset",
     "ts_profile_read",
@@ -112,6 +113,7 @@ def load():
         "ts_sel_cache_stats": ([P, I32, P, P, P], I32),
         "ts_decode_step_workspace_size": ([L, I32, I32, SZP], I32),
         "ts_decode_step": ([P, L, I32, P, P, P, P, P, F64, P, P, P, P, SZ, P], I32),
+        "ts_decode_step_noalloc": ([P, L, I32, P, P, P, P, P, F64, P, P, P, P], I32),
         "ts_score_prefill_workspace_size": ([L, I32, I32, I32, SZP], I32),
         "ts_score_prefill": ([L, I32, I32, P, P, I32, P, P, SZ, P], I32),
         "ts_select_prefill": ([L, I32, I32, P, P, I32, I32, P, P, P, SZ, P], I32),
@@ -415,6 +417,27 @@ class SelCache:
                                             _ptr(v_cache), _ptr(page_table), _ptr(seq_lens),
                                             float(theta), _ptr(out), _ptr(idx_out), _ptr(hit_out),
                                             _ptr(w), w.numel(), _stream(stream)), "ts_decode_step")
+        return out, idx_out, hit_out
+
+    def decode_step_noalloc(self, q, k_cache, v_cache, seq_lens, theta: float, out, hit_out,
+                            idx_out=None, page_table=None, scale=None, stream=None):
+        """The decode step on the library's static workspace (ts_decode_step_noalloc):
+        no device memory is allocated by this call, so the caller passes every
+        output (out [B][Hq][d] fp32, hit_out [B] int32, optional idx_out [B][k])."""
+        _need_cuda(q, k_cache, v_cache, seq_lens, page_table, out, idx_out, hit_out)
+        _kv(q, k_cache, v_cache, seq_lens, page_table)
+        L = make_layout(q, k_cache, page_table, scale)
+        B = q.shape[0]
+        if out is None or hit_out is None:
+            raise ValueError("decode_step_noalloc needs caller-provided out and hit_out")
+        _out(out, (B, self.num_q_heads, self.head_dim), torch.float32, "out")
+        _out(idx_out, (B, self.k), torch.int32, "idx_out")
+        _out(hit_out, (B,), torch.int32, "hit_out")
+        _check(self._lib.ts_decode_step_noalloc(self._h, ctypes.byref(L), B, _ptr(q), _ptr(k_cache),
+                                                _ptr(v_cache), _ptr(page_table), _ptr(seq_lens),
+                                                float(theta), _ptr(out), _ptr(idx_out),
+                                                _ptr(hit_out), _stream(stream)),
+               "ts_decode_step_noalloc")
         return out, idx_out, hit_out
 
 

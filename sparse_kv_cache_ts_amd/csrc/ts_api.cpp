@@ -471,6 +471,35 @@ ts_status check_ws(const void* ws, size_t have, size_t need) {
 #define TS_LAUNCH(expr, what) TS_TRY(hip_check((expr), what))
 #define TS_LAUNCH_K(kind, expr, what) TS_TRY(launch_timed((kind), st, [&]() { return (expr); }, what))
 
+// Workspace of ts_decode_step_noalloc: a file-scope device array, one copy per
+// GPU the library runs on, held until the process ends. Its device address is
+// looked up once per device (hipGetSymbolAddress, with that device current)
+// when a Selection Cache is created there; host code uses only that address.
+constexpr size_t kScratchBytes = TS_NOALLOC_SCRATCH_BYTES;
+static_assert(kScratchBytes == (size_t(32) << 20), "scratch size");
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+ts_status scratch_setup(int device) {
+  if (device < 0 || device >= kMaxDevices) return fail(TS_ERR_UNSUPPORTED, "device %d", device);
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (g_scratch_ptr[device]) return TS_OK;
+  void* ptr = nullptr;
+  TS_TRY(hip_check(hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)), "scratch address"));
+  if (!ptr) return fail(TS_ERR_HIP, "scratch address is NULL");
+  g_scratch_ptr[device] = ptr;
+  return TS_OK;
+}
+
+void* scratch_of(int device) {
+  if (device < 0 || device >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  return g_scratch_ptr[device];
+}
+
+
 }  // namespace
 
 extern "C" {
@@ -927,6 +956,14 @@ ts_status ts_sel_cache_create(int32_t max_batch, int32_t num_q_heads, int32_t he
     delete c;
     return fail(TS_ERR_HIP, "ts_sel_cache_create: %s", hipGetErrorString(e));
   }
+  // the no-allocation decode step's workspace on this device (looked up once)
+  if (scratch_setup(c->device) != TS_OK) {
+    const std::string why = g_last_error;
+    for (void* p : ptrs)
+      if (p) (void)hipFree(p);
+    delete c;
+    return fail(TS_ERR_HIP, "ts_sel_cache_create: %s", why.c_str());
+  }
   c->dev.prev_q = (float*)ptrs[0];
   c->dev.sel = (int32_t*)ptrs[1];
   c->dev.valid = (int32_t*)ptrs[2];
@@ -984,12 +1021,17 @@ ts_status ts_decode_step_workspace_size(const ts_kv_layout* L, int32_t batch, in
   return ok();
 }
 
-ts_status ts_decode_step(ts_sel_cache* cache, const ts_kv_layout* L, int32_t batch, const void* q,
+}  // extern "C"
+
+namespace {
+
+// Host checks of a decode step (both entry points): the layout, the cache's
+// shape, the pointers; then the workspace plan.
+ts_status decode_prepare(ts_sel_cache* cache, const ts_kv_layout* L, int batch, const void* q,
                          const void* k_cache, const void* v_cache, const int32_t* page_table,
-                         const int32_t* seq_lens, double theta, float* out, int32_t* idx_out,
-                         int32_t* hit_out, void* ws, size_t ws_bytes, void* stream) {
+                         const int32_t* seq_lens, double theta, const float* out, Geo& g,
+                         DecodePlan& p) {
   if (!cache) return fail(TS_ERR_INVALID_ARG, "cache is NULL");
-  Geo g;
   TS_TRY(check_layout(L, batch, &g));
   if (batch > cache->dev.max_batch)
     return fail(TS_ERR_INVALID_ARG, "batch %d > cache max_batch %d", batch, cache->dev.max_batch);
@@ -999,11 +1041,16 @@ ts_status ts_decode_step(ts_sel_cache* cache, const ts_kv_layout* L, int32_t bat
   if (!q || !k_cache || !v_cache || !seq_lens || !out)
     return fail(TS_ERR_INVALID_ARG, "NULL tensor pointer");
   if (g.paged && !page_table) return fail(TS_ERR_INVALID_ARG, "paged layout needs a page_table");
+  plan_decode(g, batch, cache->dev.k, p);
+  return TS_OK;
+}
+
+// The kernels of one decode step, on workspace `ws` (carved by plan p).
+ts_status decode_launch(ts_sel_cache* cache, const Geo& g, const DecodePlan& p, int batch,
+                        const void* q, const void* k_cache, const void* v_cache,
+                        const int32_t* page_table, const int32_t* seq_lens, double theta,
+                        float* out, int32_t* idx_out, int32_t* hit_out, void* ws, hipStream_t st) {
   const int k = cache->dev.k;
-  DecodePlan p;
-  plan_decode(g, batch, k, p);
-  TS_TRY(check_ws(ws, ws_bytes, p.total));
-  hipStream_t st = static_cast<hipStream_t>(stream);
   const int32_t* pt = g.paged ? page_table : nullptr;
 
   // 1+2. Selection-Cache decision per sequence, then the K-scan on misses,
@@ -1082,6 +1129,45 @@ ts_status ts_decode_step(ts_sel_cache* cache, const ts_kv_layout* L, int32_t bat
   cp.idx_out = idx_out;
   cp.hit_out = hit_out;
   TS_LAUNCH_K(kKCombine, launch_combine(cp, st), "combine");
+  return TS_OK;
+}
+
+
+}  // namespace
+
+extern "C" {
+
+ts_status ts_decode_step(ts_sel_cache* cache, const ts_kv_layout* L, int32_t batch, const void* q,
+                         const void* k_cache, const void* v_cache, const int32_t* page_table,
+                         const int32_t* seq_lens, double theta, float* out, int32_t* idx_out,
+                         int32_t* hit_out, void* ws, size_t ws_bytes, void* stream) {
+  Geo g;
+  DecodePlan p;
+  TS_TRY(decode_prepare(cache, L, batch, q, k_cache, v_cache, page_table, seq_lens, theta, out, g, p));
+  TS_TRY(check_ws(ws, ws_bytes, p.total));
+  TS_TRY(decode_launch(cache, g, p, batch, q, k_cache, v_cache, page_table, seq_lens, theta, out,
+                       idx_out, hit_out, ws, static_cast<hipStream_t>(stream)));
+  return ok();
+}
+
+ts_status ts_decode_step_noalloc(ts_sel_cache* cache, const ts_kv_layout* L, int32_t batch,
+                                 const void* q, const void* k_cache, const void* v_cache,
+                                 const int32_t* page_table, const int32_t* seq_lens, double theta,
+                                 float* out, int32_t* idx_out, int32_t* hit_out, void* stream) {
+  Geo g;
+  DecodePlan p;
+  TS_TRY(decode_prepare(cache, L, batch, q, k_cache, v_cache, page_table, seq_lens, theta, out, g, p));
+  if (p.total > kScratchBytes)
+    return fail(TS_ERR_WORKSPACE, "decode step needs %zu workspace bytes; the static scratch holds %zu",
+                p.total, kScratchBytes);
+  int dev = -1;
+  TS_TRY(hip_check(hipGetDevice(&dev), "hipGetDevice"));
+  if (dev != cache->device)
+    return fail(TS_ERR_INVALID_ARG, "current device %d is not the cache's device %d", dev, cache->device);
+  void* ws = scratch_of(dev);
+  if (!ws) return fail(TS_ERR_HIP, "no scratch address for device %d", dev);
+  TS_TRY(decode_launch(cache, g, p, batch, q, k_cache, v_cache, page_table, seq_lens, theta, out,
+                       idx_out, hit_out, ws, static_cast<hipStream_t>(stream)));
   return ok();
 }
 
