@@ -13,12 +13,22 @@ Inputs are resident in HBM before timing starts. The step rotates over
 serve the 134 MB K-scan from the previous step.
 
 One JSON line on stdout:
-  value          decode steps/s (miss steps; wall clock between synchronizes)
+  value          decode steps/s over exactly --steps miss steps (wall clock
+                 between synchronizations)
   roofline       the K-scan kernel's algorithmic bytes / its average duration,
                  measured with HIP events around each of its launches on its
-                 own stream (ts_profile_*), against MI355X's 8 TB/s
+                 own stream (ts_profile_*), against MI355X's 8 TB/s and
+                 against the read bandwidth measured on the box; with it the
+                 K-scan + gather figure (both kernels' bytes over their time)
   cpu_baseline   the fp64 oracle timed on this host's cores on a bounded
-                 sample of the same workload
+                 sample of the same workload (plus one-thread times of the
+                 tiny and 32K workloads)
+  extra          per-step median / p10 / p90 over at least 100 event-timed
+                 steps, eager and replayed from a HIP graph; hit steps; every
+                 other workload (tiny fp32, 32K, 4 x 128K, the 256-step paged
+                 selection-cache run split into hit and miss steps, the
+                 512 x 65536 prefill chunk, Quest pages, the dense baseline,
+                 a 28-layer decode loop); the GPU clock
 """
 from __future__ import annotations
 
@@ -162,8 +172,32 @@ def kv_bytes_per_token(cfg) -> int:
     return cfg.num_kv_heads * cfg.head_dim * (2 if cfg.dtype == "bf16" else 4)
 
 
-def measure_decode(ts, W, cfg, steps, warmup, copies, theta, profile, tag):
-    """Times `steps` decode steps; returns a dict of figures."""
+def _pct(xs, q):
+    ys = sorted(xs)
+    if not ys:
+        return None
+    i = min(len(ys) - 1, max(0, int(round(q * (len(ys) - 1)))))
+    return ys[i]
+
+
+def step_stats(us):
+    """median / p10 / p90 / mean of per-step times (us)."""
+    return {"median": round(_pct(us, 0.5), 2), "p10": round(_pct(us, 0.1), 2),
+            "p90": round(_pct(us, 0.9), 2), "mean": round(sum(us) / len(us), 2), "n": len(us)}
+
+
+def measure_decode(ts, W, cfg, steps, warmup, copies, theta, profile, tag, nstat=100, graph=False):
+    """Decode steps of one layer at `cfg` (selection every step with theta=1).
+
+    * `steps` steps timed on the wall clock between synchronizations (the
+      figure bench.py reports as its value);
+    * max(nstat, steps) steps each bracketed by HIP events on the stream:
+      median / p10 / p90 of the per-step time;
+    * with `profile`, per-kernel times from the library's own events;
+    * with `graph`, `copies` steps (one per K/V copy) captured in one HIP
+      graph and replayed: the per-step time without host launches.
+    K/V rotate over `copies` identical copies so that the Infinity Cache
+    cannot serve a step's reads from the step before."""
     import torch
 
     x = W.gen_decode(cfg, device="cuda")
@@ -183,21 +217,44 @@ def measure_decode(ts, W, cfg, steps, warmup, copies, theta, profile, tag):
     for i in range(warmup):
         step(i)
     torch.cuda.synchronize()
-    e0 = torch.cuda.Event(enable_timing=True)
-    e1 = torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
-    e0.record()
     for i in range(steps):
         step(i)
-    e1.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    gpu_ms = e0.elapsed_time(e1)
     hits = int(hit.sum().item())
-
     res = {"tag": tag, "wall_s": wall, "ms_per_step": 1e3 * wall / steps,
-           "gpu_ms_per_step": gpu_ms / steps, "steps_per_s": steps / wall,
-           "last_step_hits": hits}
+           "steps_per_s": steps / wall, "last_step_hits": hits}
+
+    # per-step event timing
+    n = max(nstat, steps)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(n + 1)]
+    ev[0].record()
+    for i in range(n):
+        step(i)
+        ev[i + 1].record()
+    torch.cuda.synchronize()
+    us = [1e3 * ev[i].elapsed_time(ev[i + 1]) for i in range(n)]
+    res["step_us"] = step_stats(us)
+
+    if graph:
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for c in range(copies):
+                step(c)
+        g.replay()
+        torch.cuda.synchronize()
+        reps = max(2, n // copies)
+        gv = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
+        gv[0].record()
+        for r in range(reps):
+            g.replay()
+            gv[r + 1].record()
+        torch.cuda.synchronize()
+        gus = [1e3 * gv[r].elapsed_time(gv[r + 1]) / copies for r in range(reps)]
+        res["graph_step_us"] = step_stats(gus)
+        del g
+
     if profile:
         ts.profile_reset()
         ts.profile_enable(True)
@@ -208,8 +265,8 @@ def measure_decode(ts, W, cfg, steps, warmup, copies, theta, profile, tag):
         res["profiled_ms_per_step"] = 1e3 * (time.perf_counter() - t1) / steps
         ts.profile_enable(False)
         kern = ts.profile_read()
-        res["kernels_us"] = {n: 1e3 * ms / c for n, (c, ms) in kern.items() if c}
-        res["kernel_launches_per_step"] = {n: c / steps for n, (c, ms) in kern.items() if c}
+        res["kernels_us"] = {n_: 1e3 * ms / c for n_, (c, ms) in kern.items() if c}
+        res["kernel_launches_per_step"] = {n_: c / steps for n_, (c, ms) in kern.items() if c}
     cache.close()
     del Ks, Vs
     torch.cuda.empty_cache()
@@ -366,8 +423,9 @@ def measure_selcache_run(ts, W):
     """The selection-cache decode run as a whole: 256 steps over 8 paged
     sequences of 16K..256K tokens (32/8 heads, d=128, bf16, page 16, top-4096)
     with slowly drifting queries and a fresh random query every 32 steps,
-    theta = 0.9, the stored query compared with the previous step's. Returns
-    the mean step time over the run and each sequence's hits."""
+    theta = 0.9, the stored query compared with the previous step's. Every
+    step is bracketed by HIP events; steps where some sequence missed are the
+    run's miss steps (there selection runs), the others hit steps."""
     import torch
     cfg = W.SELCACHE_RUN
     x = W.gen_run(cfg, device="cuda")
@@ -375,48 +433,189 @@ def measure_selcache_run(ts, W):
     kp, vp = x["k_pool"], x["v_pool"]
     B, Hq, d = cfg.batch, cfg.num_q_heads, cfg.head_dim
     out = torch.empty(B, Hq, d, dtype=torch.float32, device="cuda")
+    hit_steps = torch.empty(cfg.steps, B, dtype=torch.int32, device="cuda")
 
-    def run():
+    def run(events):
         cache = ts.SelCache(B, Hq, d, cfg.k)
+        if events:
+            events[0].record()
         for t in range(cfg.steps):
             cache.decode_step(qs[t], kp, vp, lens, cfg.theta, page_table=pt, out=out,
-                              want_idx=False)
+                              hit_out=hit_steps[t], want_idx=False)
+            if events:
+                events[t + 1].record()
         torch.cuda.synchronize()
         return cache
 
-    run().close()                                    # warm-up run
-    e0 = torch.cuda.Event(enable_timing=True)
-    e1 = torch.cuda.Event(enable_timing=True)
+    run(None).close()                                # warm-up run
     t0 = time.perf_counter()
-    e0.record()
-    cache = run()
-    e1.record()
-    torch.cuda.synchronize()
+    cache = run(None)
     wall = time.perf_counter() - t0
+    cache.close()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(cfg.steps + 1)]
+    cache = run(ev)
     hits, misses = cache.stats(B)
     cache.close()
+    us = [1e3 * ev[t].elapsed_time(ev[t + 1]) for t in range(cfg.steps)]
+    hs = hit_steps.cpu().tolist()
+    hit_us = [u for u, h in zip(us, hs) if all(h)]
+    miss_us = [u for u, h in zip(us, hs) if not all(h)]
+    n_list = lens.tolist()
+    bpt = cfg.num_kv_heads * d * 2
+    gathered = sum(min(cfg.k, n) for n in n_list) * bpt * 2
+    kscan = sum(n_list) * bpt
+    res = {"workload": f"{cfg.name}: {cfg.steps} steps, {B} paged sequences of "
+                       f"{cfg.min_len}..{cfg.max_len} tokens ({sum(n_list)} in all), "
+                       f"{Hq}/{cfg.num_kv_heads} heads, d={d}, bf16, page {cfg.page_size}, "
+                       f"top-{cfg.k}, theta {cfg.theta}, a fresh query every {cfg.jump_every} steps",
+           "us_per_step": round(1e6 * wall / cfg.steps, 2),
+           "event_us_per_step": step_stats(us),
+           "hit_step_us": step_stats(hit_us) if hit_us else None,
+           "miss_step_us": step_stats(miss_us) if miss_us else None,
+           "hits": hits, "misses": misses,
+           "hit_step_gathered_bytes": gathered, "miss_step_kscan_bytes": kscan}
+    if hit_us:
+        res["hit_step_GBps"] = round(gathered / (_pct(hit_us, 0.5) * 1e-6) / 1e9, 1)
+    run_bytes = (len(miss_us) * (kscan + gathered) + len(hit_us) * gathered) / cfg.steps
+    res["run_avg_algorithmic_bytes_per_step"] = int(run_bytes)
+    res["run_avg_hbm_frac"] = round(run_bytes / (1e-6 * sum(us) / len(us)) / 1e9 / HBM_PEAK_GBPS, 4)
     del x, kp, vp
     torch.cuda.empty_cache()
-    return {"workload": f"{cfg.name}: {cfg.steps} steps, {B} paged sequences of "
-                        f"{cfg.min_len}..{cfg.max_len} tokens, {Hq}/{cfg.num_kv_heads} heads, "
-                        f"d={d}, bf16, page {cfg.page_size}, top-{cfg.k}, theta {cfg.theta}, "
-                        f"a fresh query every {cfg.jump_every} steps",
-            "us_per_step": round(1e6 * wall / cfg.steps, 2),
-            "gpu_us_per_step": round(1e3 * e0.elapsed_time(e1) / cfg.steps, 2),
-            "hits": hits, "misses": misses}
-
-
-def measure_configs(ts, W, steps, warmup):
-    """Decode steps (selection every step) at the other decode shapes."""
-    res = {}
-    for name, cfg, copies in (("qwen2-7b-shape-32k", W.QWEN_32K, 6),
-                              ("llama3-8b-shape-4x128k", W.LLAMA_4x128K, 2)):
-        r, _ = measure_decode(ts, W, cfg, steps, warmup, copies, 1.0, False, name)
-        res[name] = {"batch": cfg.batch, "seq_len": cfg.seq_len, "k": cfg.k,
-                     "heads": f"{cfg.num_q_heads}/{cfg.num_kv_heads}",
-                     "us_per_step": round(1e3 * r["ms_per_step"], 2),
-                     "steps_per_s": round(r["steps_per_s"], 1)}
     return res
+
+
+def decode_bytes(cfg):
+    """Algorithmic bytes of one decode step with selection: K scanned once,
+    plus the gathered K and V rows of the selection."""
+    bpt = kv_bytes_per_token(cfg)
+    kscan = cfg.batch * cfg.seq_len * bpt
+    gather = cfg.batch * min(cfg.k, cfg.seq_len) * bpt * 2
+    return kscan, gather
+
+
+def config_entry(cfg, r, read_peak):
+    kscan, gather = decode_bytes(cfg)
+    med = r["step_us"]["median"]
+    e = {"batch": cfg.batch, "seq_len": cfg.seq_len, "k": cfg.k,
+         "heads": f"{cfg.num_q_heads}/{cfg.num_kv_heads}", "head_dim": cfg.head_dim,
+         "dtype": cfg.dtype, "steps_per_s": round(1e6 / med, 1),
+         "attention_layer_latency_us": r["step_us"],
+         "wall_us_per_step": round(1e3 * r["ms_per_step"], 2),
+         "algorithmic_bytes": kscan + gather,
+         "whole_step_hbm_frac": round((kscan + gather) / (med * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4)}
+    if read_peak:
+        e["whole_step_frac_of_measured_read_peak"] = round(
+            (kscan + gather) / (med * 1e-6) / 1e9 / read_peak, 4)
+    ku = r.get("kernels_us")
+    if ku and "score_pass1" in ku and "attend" in ku:
+        ts_, ta = ku["score_pass1"] * 1e-6, ku["attend"] * 1e-6
+        e["kernels_us"] = {kk: round(v, 2) for kk, v in ku.items()}
+        e["kscan_frac"] = round(kscan / ts_ / 1e9 / HBM_PEAK_GBPS, 4)
+        e["kscan_plus_gather_frac"] = round((kscan + gather) / (ts_ + ta) / 1e9 / HBM_PEAK_GBPS, 4)
+    return e
+
+
+def measure_configs(ts, W, steps, warmup, read_peak):
+    """Decode steps (selection every step) at the other decode workloads: the
+    tiny fp32 case, the Qwen2-7B shape at 32K tokens, the Llama-3-8B shape
+    with 4 x 128K tokens. K/V copies rotate so that about 768 MB are touched
+    between two uses of a copy (at least 3 copies)."""
+    res = {}
+    for name, cfg in (("tiny-4q2kv-d64-4k-f32", W.TINY),
+                      ("qwen2-7b-shape-32k", W.QWEN_32K),
+                      ("llama3-8b-shape-4x128k", W.LLAMA_4x128K)):
+        kv = 2 * cfg.batch * cfg.seq_len * kv_bytes_per_token(cfg)
+        copies = max(3, min(64, -(-768_000_000 // kv)))
+        r, _ = measure_decode(ts, W, cfg, steps, warmup, copies, 1.0, True, name)
+        res[name] = config_entry(cfg, r, read_peak)
+        res[name]["kv_copies"] = copies
+    return res
+
+
+def measure_read_peak(nbytes=1 << 30, reps=5):
+    """The read bandwidth this machine reaches without any of this library's code:
+    the best of a few torch reductions over 1 GiB of bf16 (a whole-tensor sum
+    and row-wise sums and maxima over 8192- and 65536-element rows, fp32
+    accumulation), each timed with HIP events, best of `reps`.
+    Returns (GB/s, the op that reached it)."""
+    import torch
+    x = torch.ones(nbytes // 2, dtype=torch.bfloat16, device="cuda")
+    ops = {
+        "sum": lambda: x.sum(dtype=torch.float32),
+        "rowsum8192": lambda: x.view(-1, 8192).sum(dim=1, dtype=torch.float32),
+        "rowsum65536": lambda: x.view(-1, 65536).sum(dim=1, dtype=torch.float32),
+        "rowmax8192": lambda: x.view(-1, 8192).amax(dim=1),
+    }
+    best, best_op = float("inf"), None
+    for name, op in ops.items():
+        for _ in range(2):
+            op()
+        torch.cuda.synchronize()
+        for _ in range(reps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            op()
+            e1.record()
+            torch.cuda.synchronize()
+            t = e0.elapsed_time(e1) * 1e-3
+            if t < best:
+                best, best_op = t, name
+    del x
+    torch.cuda.empty_cache()
+    return round(nbytes / best / 1e9, 1), best_op
+
+
+def gpu_clock():
+    """The GPU's reported current clocks (not pinned), or None."""
+    import subprocess
+    try:
+        r = subprocess.run(["rocm-smi", "--showclocks", "--json"], capture_output=True, text=True,
+                           timeout=20)
+        d = json.loads(r.stdout)
+        card = d[sorted(d)[0]]
+        pick = {k: v for k, v in card.items() if "sclk" in k.lower() or "mclk" in k.lower()}
+        return pick or None
+    except Exception:
+        return None
+
+
+def stored_fetch(path_name, key):
+    """A counter figure (bytes) recorded in a profiles/ summary, or None."""
+    try:
+        with open(os.path.join(ROOT, "profiles", path_name)) as fh:
+            for ln in fh:
+                if ln.strip().startswith(key):
+                    return int(ln.split(":", 1)[1].split()[0].replace(",", ""))
+    except (OSError, ValueError, IndexError):
+        return None
+    return None
+
+
+def cpu_single_thread(O, W, seconds=3.0):
+    """The oracle with one BLAS thread on the tiny fp32 workload and the
+    Qwen2-7B shape at 32K tokens: seconds per decode step (selection +
+    sparse attention), on host copies generated from the same seeds."""
+    try:
+        from threadpoolctl import threadpool_limits
+    except Exception:
+        return None
+    out = {}
+    with threadpool_limits(limits=1):
+        for name, cfg in (("tiny-4q2kv-d64-4k-f32", W.TINY), ("qwen2-7b-shape-32k", W.QWEN_32K)):
+            x = W.gen_decode(cfg, device="cpu")
+            q = x["q"][0].float().double().numpy()
+            K = x["k_cache"][0].float().numpy()
+            V = x["v_cache"][0].float().numpy()
+            n, t0 = 0, time.perf_counter()
+            while True:
+                S, _ = O.select(q, K, cfg.k)
+                O.sparse_attention(q, K, V, S)
+                n += 1
+                el = time.perf_counter() - t0
+                if el >= seconds or n >= 200:
+                    break
+            out[name] = {"s_per_step": round(el / n, 5), "steps": n, "threads": 1}
+    return out
 
 
 def cpu_baseline(O, W, cfg, x, seconds):
@@ -483,48 +682,64 @@ def main():
     ts.load()
 
     cfg = W.QWEN_128K
+    read_peak, read_op = measure_read_peak()
     miss, x = measure_decode(ts, W, cfg, args.steps, args.warmup, args.kv_copies, 1.0,
-                             not args.no_profile, "miss")
-    extra = {}
+                             not args.no_profile, "miss", graph=True)
+    extra = {"gpu_clock": gpu_clock(), "measured_read_peak_GBps": read_peak,
+             "measured_read_peak_op": f"torch {read_op} over 1 GiB of bf16 (best of several reductions)"}
+    kscan_bytes, gather_bytes = decode_bytes(cfg)
+    head = config_entry(cfg, miss, read_peak)
+    head["graph_replay_step_us"] = miss.get("graph_step_us")
+    head["eager_step_us"] = miss["step_us"]
+    extra["headline_miss_step"] = head
     if not args.no_hit:
         hitres, _ = measure_decode(ts, W, cfg, args.steps, args.warmup, args.kv_copies, 0.9,
-                                   not args.no_profile, "hit")
-        extra["hit_step"] = hitres
+                                   not args.no_profile, "hit", graph=True)
+        extra["hit_step"] = {"step_us": hitres["step_us"],
+                             "graph_step_us": hitres.get("graph_step_us"),
+                             "wall_us_per_step": round(1e3 * hitres["ms_per_step"], 2),
+                             "gathered_bytes": gather_bytes,
+                             "last_step_hits": hitres["last_step_hits"],
+                             "kernels_us": {k: round(v, 2) for k, v in hitres.get("kernels_us", {}).items()}}
 
-    N, bpt = cfg.seq_len, kv_bytes_per_token(cfg)
-    kscan_bytes = cfg.batch * N * bpt
-    gather_bytes = cfg.batch * cfg.k * bpt * 2
     roof = None
     if "kernels_us" in miss:
         ku = miss["kernels_us"]
         t_scan = ku["score_pass1"] * 1e-6
+        t_att = ku["attend"] * 1e-6
         achieved = kscan_bytes / t_scan / 1e9
+        kg = (kscan_bytes + gather_bytes) / (t_scan + t_att) / 1e9
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
                 "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
                 "traffic": stored_traffic(),
                 "kernel": "score_pass1 (K-scan)", "bytes_per_launch": kscan_bytes,
-                "avg_launch_us": round(ku["score_pass1"], 2)}
-        t_att = ku["attend"] * 1e-6
-        extra["kscan_plus_gather"] = {
-            "bytes": kscan_bytes + gather_bytes,
-            "GBps": round((kscan_bytes + gather_bytes) / (t_scan + t_att) / 1e9, 1),
-            "frac": round((kscan_bytes + gather_bytes) / (t_scan + t_att) / 1e9 / HBM_PEAK_GBPS, 4)}
+                "avg_launch_us": round(ku["score_pass1"], 2),
+                "frac_of_measured_read_peak": round(achieved / read_peak, 4) if read_peak else None,
+                "kscan_plus_gather": {"bytes": kscan_bytes + gather_bytes, "GBps": round(kg, 1),
+                                      "frac": round(kg / HBM_PEAK_GBPS, 4),
+                                      "frac_of_measured_read_peak":
+                                          round(kg / read_peak, 4) if read_peak else None}}
         extra["kernels_us"] = {kk: round(v, 2) for kk, v in ku.items()}
         extra["profiled_ms_per_step"] = round(miss["profiled_ms_per_step"], 4)
-    extra["gpu_event_ms_per_step"] = round(miss["gpu_ms_per_step"], 4)
-    extra["attention_layer_latency_us"] = round(1e3 * miss["ms_per_step"], 2)
+    extra["attention_layer_latency_us"] = miss["step_us"]
     extra["step_algorithmic_bytes"] = kscan_bytes + gather_bytes
     extra["whole_step_hbm_frac"] = round(
         (kscan_bytes + gather_bytes) / (miss["ms_per_step"] * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4)
 
     if not args.no_prefill:
         extra["prefill_chunk"] = measure_prefill(ts, W)
+        past_l2 = stored_fetch("prefill_sparse_attention_512x4096_fetch.txt", "fetched_past_l2_bytes")
+        if past_l2:
+            att_us = extra["prefill_chunk"]["sparse_attention_us"]
+            extra["prefill_chunk"]["sparse_attention_past_l2"] = {
+                "bytes": past_l2, "GBps": round(past_l2 / (att_us * 1e-6) / 1e9, 1),
+                "frac": round(past_l2 / (att_us * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4)}
     if not args.no_dense:
         dense = measure_dense(ts, W, cfg, args.steps, args.warmup, args.kv_copies)
-        step_us = 1e3 * miss["ms_per_step"]
+        step_us = miss["step_us"]["median"]
         dense["speedup_vs_miss_step"] = round(dense["us_per_call"] / step_us, 3)
         if "hit_step" in extra:
-            dense["speedup_vs_hit_step"] = round(dense["us_per_call"] / (1e3 * extra["hit_step"]["ms_per_step"]), 3)
+            dense["speedup_vs_hit_step"] = round(dense["us_per_call"] / extra["hit_step"]["step_us"]["median"], 3)
         if "kernels_us" in miss:
             sparse_att = miss["kernels_us"]["attend"] + miss["kernels_us"]["combine"]
             dense["sparse_attention_us"] = round(sparse_att, 2)
@@ -540,13 +755,16 @@ def main():
 
     if not args.no_configs:
         extra["other_decode_shapes"] = measure_configs(ts, W, max(1, args.steps // 2),
-                                                       max(1, args.warmup // 2))
+                                                       max(1, args.warmup // 2), read_peak)
         extra["selcache_run"] = measure_selcache_run(ts, W)
 
     cpu = None
     if not args.no_cpu_baseline:
         from oracle import ts_oracle as O
         cpu = cpu_baseline(O, W, cfg, x, args.cpu_seconds)
+        st = cpu_single_thread(O, W)
+        if st:
+            cpu["single_thread"] = st
 
     line = {
         "metric": "decode steps/sec + K-scan HBM GB/s (frac. of peak), Qwen2-7B shape, N=128K",
@@ -564,7 +782,7 @@ def main():
         "config": {"workload": "qwen2-7b-shape decode step, N=131072, batch 1, top-k 2048, "
                                "selection every step (theta=1.0)",
                    "num_q_heads": cfg.num_q_heads, "num_kv_heads": cfg.num_kv_heads,
-                   "head_dim": cfg.head_dim, "seq_len": N, "batch": cfg.batch, "k": cfg.k,
+                   "head_dim": cfg.head_dim, "seq_len": cfg.seq_len, "batch": cfg.batch, "k": cfg.k,
                    "kv_dtype": "bf16", "accumulate": "f32", "kv_copies": args.kv_copies},
         "roofline": roof,
         "cpu_baseline": cpu,
