@@ -318,9 +318,10 @@ ts_status ts_decode_step_noalloc(ts_sel_cache* cache, const ts_kv_layout* layout
  *   votes    [chunk][n_ctx] fp32 out: row i holds the soft vote over keys
  *            0 .. q_pos0 + i; entries past that are written as 0.
  *   Requires q_pos0 >= 0 and q_pos0 + chunk <= n_ctx.
- *   Built for bf16, head_dim 64 or 128, 4 query heads per KV head and at most
- *   8 KV heads; other shapes return TS_ERR_UNSUPPORTED. The workspace size
- *   does not depend on q_pos0.
+ *   Built for bf16, head_dim 64 or 128, 1 to 8 query heads per KV head (laid
+ *   out as 1, 2, 4 or 8 slots; unused slots are masked) and at most 8 KV
+ *   heads; other shapes return TS_ERR_UNSUPPORTED. The workspace size does
+ *   not depend on q_pos0.
  * ts_select_prefill additionally runs step 3 on every row:
  *   idx      [chunk][k] int32 out (row i selects from its q_pos0 + i + 1 keys).
  * ------------------------------------------------------------------------- */

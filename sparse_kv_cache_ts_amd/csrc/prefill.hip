@@ -9,9 +9,13 @@
 // a dense Q.K^T contraction (chunk x Hq rows against n_ctx keys), so it runs
 // on v_mfma_f32_16x16x32_bf16 tiles. Lane l of a wave holds A rows l%16
 // (8 consecutive d of k-step 8*(l/16)), B columns l%16 (one key) and C rows
-// 4*(l/16)..+3, column l%16. Rows are (query, head) pairs with the head
-// fastest, so for G = 4 a lane's four C rows are one query's four heads and
-// their softmax terms add up in registers.
+// 4*(l/16)..+3, column l%16. Rows are (query, head slot) pairs with the slot
+// fastest: a KV head's G query heads take GP slots per query, GP the power of
+// two >= G (G = 3 runs as 4, G = 5..7 as 8; the extra slots hold a zero query
+// row and are masked out of every sum). With GP = 4 a lane's four C rows are
+// one query's four heads, so their softmax terms add up in registers; GP = 2
+// and 1 give a lane two and four queries, and GP = 8 spreads a query over
+// two lanes 16 apart, whose sums meet by a lane swap.
 //
 // Pass 1 (prefill_lse_kernel): work-group = (KV head g, block of queries, key
 // split); 4 waves x 64 rows, each wave streams the same keys. Per tile of 16
@@ -37,14 +41,16 @@ __device__ __forceinline__ int xcd_flat(int b, int total) {
 }
 
 // Q fragment of row tile `rt` (16 rows) and k-step `ks` for this lane.
-// Row r of the group's row space is (query qbase + r / G, head g*G + r % G).
-template <int G, int D>
+// Row r of the group's row space is (query qbase + r / GP, slot r % GP);
+// slot s < G is head g*G + s, the others are zero rows.
+template <int GP, int D>
 __device__ __forceinline__ uint4 load_q_frag(const PrefillParams& p, int g, int qbase, int rt, int ks,
                                              int lane) {
   const int r = rt * 16 + (lane & 15);
-  const int qi = qbase + r / G;
-  const int head = g * G + r % G;
-  if (qi >= p.chunk) return make_uint4(0, 0, 0, 0);
+  const int qi = qbase + r / GP;
+  const int slot = r % GP;
+  if (qi >= p.chunk || slot >= p.G) return make_uint4(0, 0, 0, 0);
+  const int head = g * p.G + slot;
   const char* base = (const char*)p.q + (((size_t)qi * p.Hq + head) * D + ks * 32 + 8 * (lane >> 4)) * 2;
   return ld16(base);
 }
@@ -81,11 +87,11 @@ __device__ __forceinline__ void qk_tile(const bf16x8_t (&qf)[RT][KS], const uint
 // elements cost one fma, one exponential and one add. Masked elements are
 // -inf and add 0. M starts at a finite -1e30, so a row with nothing seen yet
 // rescales by exp2(0) = 1 and no inf - inf or 0 * inf arises.
-template <int G, int D>
+template <int GP, int D>
 __global__ __launch_bounds__(256) void prefill_lse_kernel(PrefillParams p) {
   constexpr int KS = D / 32;      // k-steps per tile
   constexpr int RT = kPrefillRT1;  // row tiles per wave
-  constexpr int QW = 16 * RT / G;  // queries per wave
+  constexpr int QW = 16 * RT / GP; // queries per wave
   constexpr int QB = 4 * QW;       // queries per work-group (4 waves)
   const int nqb = (p.chunk + QB - 1) / QB;
   const int f = xcd_flat(blockIdx.x, gridDim.x);
@@ -105,7 +111,7 @@ __global__ __launch_bounds__(256) void prefill_lse_kernel(PrefillParams p) {
 #pragma unroll
   for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) qf[rt][ks] = as_bf8(load_q_frag<G, D>(p, g, qbase, rt, ks, lane));
+    for (int ks = 0; ks < KS; ++ks) qf[rt][ks] = as_bf8(load_q_frag<GP, D>(p, g, qbase, rt, ks, lane));
 
   float M[RT][4], S[RT][4];
 #pragma unroll
@@ -135,7 +141,7 @@ __global__ __launch_bounds__(256) void prefill_lse_kernel(PrefillParams p) {
         float a = fmaf(s0[rt][i], sc2, -M[rt][i]), b = fmaf(s1[rt][i], sc2, -M[rt][i]);
         if (masked) {
           // causal edge or end of the range: query qi sees keys <= q_pos0 + qi
-          const int lim = min(kend - 1, p.q_pos0 + qbase + (rt * 16 + 4 * (lane >> 4) + i) / G);
+          const int lim = min(kend - 1, p.q_pos0 + qbase + (rt * 16 + 4 * (lane >> 4) + i) / GP);
           a = key <= lim ? a : -INFINITY;
           b = key + 16 <= lim ? b : -INFINITY;
         }
@@ -228,10 +234,11 @@ __global__ __launch_bounds__(256) void prefill_lse_kernel(PrefillParams p) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int r = rt * 16 + 4 * (lane >> 4) + i;
-        const int qi = qbase + r / G;
-        const int head = g * G + r % G;
-        if (qi < p.chunk)
-          p.lse_part[((size_t)qi * p.Hq + head) * p.nsplit1 + split] = make_float2(M[rt][i], S[rt][i]);
+        const int qi = qbase + r / GP;
+        const int slot = r % GP;
+        if (qi < p.chunk && slot < p.G)
+          p.lse_part[((size_t)qi * p.Hq + g * p.G + slot) * p.nsplit1 + split] =
+              make_float2(M[rt][i], S[rt][i]);
       }
   }
 }
@@ -255,17 +262,18 @@ __global__ __launch_bounds__(256) void prefill_merge_kernel(PrefillParams p) {
 // ---- pass 2 -----------------------------------------------------------------
 // Work-group = (block of QB queries, kPrefillKeys2 keys), one wave per KV head.
 // Per 16-key tile each wave adds exp2(scale2 * s - lse) over its G query heads
-// (a lane's four C rows are one query's four heads); after a barrier the KV-
-// head partials are summed in a fixed order into an LDS vote tile, which is
-// written to HBM once at the end. The loop issues no global stores, so its
-// waits are for the one K tile they need (prefetched a tile ahead).
-template <int G, int D>
+// (in registers, and for GP = 8 with the partner lane 16 away); after a
+// barrier the KV-head partials are summed in a fixed order into an LDS vote
+// tile, which is written to HBM once at the end. The loop issues no global
+// stores, so its waits are for the one K tile they need (prefetched a tile
+// ahead).
+template <int GP, int D>
 __global__ __launch_bounds__(512) void prefill_votes_kernel(PrefillParams p) {
   constexpr int KS = D / 32;
-  constexpr int RT = kPrefillRT2;  // row tiles per wave (rows of one KV head)
-  constexpr int QB = 16 * RT / G;  // queries per work-group
+  constexpr int RT = prefill_rt2(GP);  // row tiles per wave (rows of one KV head)
+  constexpr int QB = 16 * RT / GP;     // queries per work-group
   constexpr int KT = kPrefillKeys2;
-  static_assert(G == 4, "a lane's four C rows must be one query's four heads");
+  constexpr int QPL = GP >= 4 ? 1 : 4 / GP;   // queries per lane and row tile
   __shared__ float s_v[2][8][QB][32];           // [buffer][KV head][query][key of a tile pair]
   __shared__ float s_out[QB][KT];               // the work-group's votes
   const int nqb = (p.chunk + QB - 1) / QB;
@@ -286,16 +294,18 @@ __global__ __launch_bounds__(512) void prefill_votes_kernel(PrefillParams p) {
 #pragma unroll
   for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) qf[rt][ks] = as_bf8(load_q_frag<G, D>(p, g, qbase, rt, ks, lane));
+    for (int ks = 0; ks < KS; ++ks) qf[rt][ks] = as_bf8(load_q_frag<GP, D>(p, g, qbase, rt, ks, lane));
+  // rows past the chunk and padding slots get an infinite log-sum-exp: their
+  // terms are exp2(-inf) = 0
   float lse[RT][4];
 #pragma unroll
   for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int r = rt * 16 + 4 * (lane >> 4) + i;
-      const int qi = qbase + r / G;
-      const int head = g * G + r % G;
-      lse[rt][i] = (qi < p.chunk) ? p.lse[(size_t)qi * p.Hq + head] : INFINITY;
+      const int qi = qbase + r / GP;
+      const int slot = r % GP;
+      lse[rt][i] = (qi < p.chunk && slot < p.G) ? p.lse[(size_t)qi * p.Hq + g * p.G + slot] : INFINITY;
     }
   const float sc2 = p.scale2;
 
@@ -311,12 +321,26 @@ __global__ __launch_bounds__(512) void prefill_votes_kernel(PrefillParams p) {
     const int key = kb + (lane & 15);
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt) {
-      float v = 0.f;
+      float e[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) v += ex2(fmaf(sc[rt][i], sc2, -lse[rt][i]));
-      const int ql = rt * 4 + (lane >> 4);
-      if (!all && key > p.q_pos0 + qbase + ql) v = 0.f;
-      s_v[b][g][ql][half * 16 + (lane & 15)] = v;
+      for (int i = 0; i < 4; ++i) e[i] = ex2(fmaf(sc[rt][i], sc2, -lse[rt][i]));
+      if constexpr (GP >= 4) {
+        float v = (e[0] + e[1]) + (e[2] + e[3]);
+        if constexpr (GP == 8) v = xor_sum<16>(v);   // plus the query's other four slots
+        const int ql = GP == 8 ? rt * 2 + (lane >> 5) : rt * 4 + (lane >> 4);
+        if (!all && key > p.q_pos0 + qbase + ql) v = 0.f;
+        if (GP == 4 || ((lane >> 4) & 1) == 0) s_v[b][g][ql][half * 16 + (lane & 15)] = v;
+      } else {
+#pragma unroll
+        for (int u = 0; u < QPL; ++u) {
+          float v = 0.f;
+#pragma unroll
+          for (int i = 0; i < GP; ++i) v += e[u * GP + i];
+          const int ql = rt * (16 / GP) + (4 / GP) * (lane >> 4) + u;
+          if (!all && key > p.q_pos0 + qbase + ql) v = 0.f;
+          s_v[b][g][ql][half * 16 + (lane & 15)] = v;
+        }
+      }
     }
   };
   auto flush = [&](int t, int b, int nk) {
@@ -373,12 +397,15 @@ __global__ __launch_bounds__(512) void prefill_votes_kernel(PrefillParams p) {
 
 template <int D>
 static hipError_t launch_lse_g(const PrefillParams& p, hipStream_t s) {
-  const int qb = 64 * kPrefillRT1 / p.G;
+  const int gp = prefill_gp(p.G);
+  const int qb = 64 * kPrefillRT1 / gp;
   dim3 grid(((p.chunk + qb - 1) / qb) * p.Hkv * p.nsplit1);
-  switch (p.G) {
+  switch (gp) {
+    case 1: TS_KLAUNCH((prefill_lse_kernel<1, D>), grid, dim3(256), 0, s, p); break;
+    case 2: TS_KLAUNCH((prefill_lse_kernel<2, D>), grid, dim3(256), 0, s, p); break;
     case 4: TS_KLAUNCH((prefill_lse_kernel<4, D>), grid, dim3(256), 0, s, p); break;
-    // other group sizes are not built (rejected on the host)
-    default: return hipErrorInvalidValue;
+    case 8: TS_KLAUNCH((prefill_lse_kernel<8, D>), grid, dim3(256), 0, s, p); break;
+    default: return hipErrorInvalidValue;   // rejected on the host
   }
   return hipGetLastError();
 }
@@ -396,13 +423,16 @@ hipError_t launch_prefill_merge(const PrefillParams& p, hipStream_t s) {
 
 template <int D>
 static hipError_t launch_votes_g(const PrefillParams& p, hipStream_t s) {
-  const int qb = 16 * kPrefillRT2 / p.G;
+  const int gp = prefill_gp(p.G);
+  const int qb = 16 * prefill_rt2(gp) / gp;
   dim3 grid(((p.chunk + qb - 1) / qb) * p.nsplit2);
   dim3 block(64 * p.Hkv);
-  switch (p.G) {
+  switch (gp) {
+    case 1: TS_KLAUNCH((prefill_votes_kernel<1, D>), grid, block, 0, s, p); break;
+    case 2: TS_KLAUNCH((prefill_votes_kernel<2, D>), grid, block, 0, s, p); break;
     case 4: TS_KLAUNCH((prefill_votes_kernel<4, D>), grid, block, 0, s, p); break;
-    // other group sizes are not built (rejected on the host)
-    default: return hipErrorInvalidValue;
+    case 8: TS_KLAUNCH((prefill_votes_kernel<8, D>), grid, block, 0, s, p); break;
+    default: return hipErrorInvalidValue;   // rejected on the host
   }
   return hipGetLastError();
 }

@@ -1190,7 +1190,8 @@ ts_status plan_prefill(const ts_kv_layout* L, int chunk, int q_pos0, int n_ctx, 
   TS_TRY(check_layout(L, 1, &g));
   if (g.dtype != TS_BF16) return fail(TS_ERR_UNSUPPORTED, "prefill scoring needs bf16 q and K");
   if (g.paged) return fail(TS_ERR_UNSUPPORTED, "prefill scoring needs a contiguous K");
-  if (g.G != 4) return fail(TS_ERR_UNSUPPORTED, "prefill scoring is built for 4 query heads per KV head");
+  if (prefill_gp(g.G) == 0)
+    return fail(TS_ERR_UNSUPPORTED, "prefill scoring is built for at most 8 query heads per KV head");
   if (g.Hkv > 8) return fail(TS_ERR_UNSUPPORTED, "prefill scoring supports at most 8 KV heads");
   if (chunk < 1 || n_ctx < 1) return fail(TS_ERR_INVALID_ARG, "chunk and n_ctx must be >= 1");
   if (q_pos0 < 0 || (long)q_pos0 + chunk > n_ctx)
@@ -1208,7 +1209,7 @@ ts_status plan_prefill(const ts_kv_layout* L, int chunk, int q_pos0, int n_ctx, 
   p.D = g.d;
   p.scale2 = g.scale * kLog2eHost;
   // pass 1: about one work-group of 4 waves per CU
-  const int qb1 = cdiv(chunk, 64 * kPrefillRT1 / g.G);
+  const int qb1 = cdiv(chunk, 64 * kPrefillRT1 / prefill_gp(g.G));
   int ns1 = std::max(1, 256 / (qb1 * g.Hkv));
   p.key_split = cdiv(cdiv(n_ctx, ns1), 32) * 32;
   p.nsplit1 = cdiv(n_ctx, p.key_split);

@@ -24,9 +24,12 @@ constexpr float kLog2eHost = 1.4426950408889634f;
 // one KV head); every wave reads the same keys, so more rows per wave means
 // fewer key fragments through each CU's L1
 constexpr int kPrefillRT1 = 8;
+// query heads per KV head as the prefill kernels lay them out: G rounded up
+// to a power of two (0 when G > 8: not built)
+constexpr int prefill_gp(int G) { return G <= 1 ? 1 : G <= 2 ? 2 : G <= 4 ? 4 : G <= 8 ? 8 : 0; }
 // prefill vote pass: 16-row MFMA tiles per wave (one KV head); a work-group
-// covers 16 * kPrefillRT2 / G queries
-constexpr int kPrefillRT2 = 8;
+// covers 16 * prefill_rt2(GP) / GP queries (32, or 16 for GP = 8)
+constexpr int prefill_rt2(int GP) { return GP >= 4 ? 8 : 2 * GP; }
 constexpr int kPrefillKeys2 = 512; // keys per vote-pass work-group (its LDS vote tile)
 
 // ---- per-row control block (uint32 words) ----------------------------------

@@ -31,6 +31,13 @@ SMALL = [
     _cfg("c1-n777-h4x1-d128", 1, 777, 4, 1, 128, 700, 33),
     _cfg("c70-first-chunk-h16x4-d128", 70, 70, 16, 4, 128, 32, 34, q_pos0=0),
     _cfg("c257-n4099-h28x7-d128", 257, 4099, 28, 7, 128, 1000, 35),
+    # query-head groups other than 4: padded to 1, 2, 4 or 8 slots per KV head
+    _cfg("g1-c97-n2000-h8x8-d128", 97, 2000, 8, 8, 128, 300, 36),
+    _cfg("g2-c130-n3333-h8x4-d64-mid", 130, 3333, 8, 4, 64, 500, 37, q_pos0=1500),
+    _cfg("g3-c70-n1500-h6x2-d128", 70, 1500, 6, 2, 128, 200, 38),
+    _cfg("g7-c129-n5000-h28x4-d128", 129, 5000, 28, 4, 128, 1024, 39),
+    _cfg("g8-c64-n2500-h32x4-d64", 64, 2500, 32, 4, 64, 256, 40),
+    _cfg("g5-c33-n900-h10x2-d128", 33, 900, 10, 2, 128, 100, 41),
 ]
 
 
@@ -105,7 +112,7 @@ def test_prefill_full_size(gpu_lib):
 
 def test_prefill_rejects_unsupported(gpu_lib):
     ts = gpu_lib
-    q = torch.zeros(4, 6, 128, dtype=torch.bfloat16, device="cuda")   # G = 3
+    q = torch.zeros(4, 32, 128, dtype=torch.bfloat16, device="cuda")   # G = 16
     k = torch.zeros(100, 2, 128, dtype=torch.bfloat16, device="cuda")
     with pytest.raises(ts.TsError) as e:
         ts.score_prefill(q, k, 96)
@@ -160,6 +167,33 @@ def test_prefill_sparse_attention_skips_invalid(gpu_lib):
         sel = gi[i][(gi[i] >= 0) & (gi[i] < n)]
         ref = O.sparse_attention(Q[i], K[:n], V[:n], sel)
         check_attention(o[i], ref, 1e-2)
+
+
+@pytest.mark.timeout(900)
+def test_prefill_full_size_qwen_shape(gpu_lib):
+    """A 512-query chunk at the Qwen2-7B shape (28/4 heads: seven query heads
+    per KV head, laid out as eight slots), 65536 keys, top-4096: every row's
+    selection is the exact top-k of its vote row; 32 rows, the first and last
+    included, against the oracle's votes and decided-token rule."""
+    from dataclasses import replace
+    ts = gpu_lib
+    cfg = replace(W.PREFILL_64K, name="prefill-512x64k-qwen2-7b-shape", num_q_heads=28,
+                  num_kv_heads=4, seed=42)
+    x = W.gen_prefill(cfg, device="cuda")
+    q0 = x["q_pos0"]
+    votes, idx = ts.select_prefill(x["q"], x["k_cache"], q0, cfg.k)
+    torch.cuda.synchronize()
+    V32 = np32(votes)
+    gi = idx.cpu().numpy()
+    for r in range(cfg.chunk):
+        n = q0 + r + 1
+        assert (V32[r, n:] == 0).all()
+        assert np.array_equal(gi[r], O.top_k(V32[r, :n].astype(np.float64), cfg.k)), f"row {r}"
+    rows = sorted(set(np.linspace(0, cfg.chunk - 1, 32).round().astype(int).tolist()))
+    Q, K = np64(x["q"]), np64(x["k_cache"])
+    for r, ref in zip(rows, O.prefill_votes(Q, K, q0, rows=rows)):
+        _check_votes(votes[r], ref, q0 + r + 1, cfg.num_q_heads)
+        check_selection(gi[r], ref, cfg.k)
 
 
 @pytest.mark.timeout(900)
