@@ -645,6 +645,35 @@ def cpu_baseline(O, W, cfg, x, seconds):
                       f"{len(os.sched_getaffinity(0))} host cores"}
 
 
+def profile_only(ts, W, name, steps, warmup):
+    """One workload's steps alone, for kernel traces and hardware counters."""
+    import torch
+    if name == "prefill-512x64k":
+        cfg = W.PREFILL_64K
+        x = W.gen_prefill(cfg, device="cuda")
+        q0 = x["q_pos0"]
+        votes = torch.empty(cfg.chunk, cfg.n_ctx, dtype=torch.float32, device="cuda")
+        idx = torch.empty(cfg.chunk, cfg.k, dtype=torch.int32, device="cuda")
+        out = torch.empty(cfg.chunk, cfg.num_q_heads, cfg.head_dim, dtype=torch.float32, device="cuda")
+        ws = ts.Workspace()
+        for i in range(warmup + steps):
+            ts.select_prefill(x["q"], x["k_cache"], q0, cfg.k, votes=votes, idx=idx)
+            ts.sparse_attend_prefill(x["q"], x["k_cache"], x["v_cache"], q0, idx, out=out, ws=ws)
+        torch.cuda.synchronize()
+        print(json.dumps({"profile_only": name, "chunks": warmup + steps}), flush=True)
+        return
+    if name == "selcache-run":
+        r = measure_selcache_run(ts, W)
+        print(json.dumps({"profile_only": name, "us_per_step": r["us_per_step"]}), flush=True)
+        return
+    cfgs = {"qwen2-7b-shape-128k": (W.QWEN_128K, 6, 1.0), "qwen2-7b-shape-128k-hit": (W.QWEN_128K, 6, 0.9),
+            "qwen2-7b-shape-32k": (W.QWEN_32K, 12, 1.0), "llama3-8b-shape-4x128k": (W.LLAMA_4x128K, 3, 1.0),
+            "tiny-4q2kv-d64-4k-f32": (W.TINY, 64, 1.0)}
+    cfg, copies, theta = cfgs[name]
+    r, _ = measure_decode(ts, W, cfg, steps, warmup, copies, theta, False, name, nstat=1)
+    print(json.dumps({"profile_only": name, "us_per_step": round(1e3 * r["ms_per_step"], 2)}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -664,6 +693,12 @@ def main():
                     help="skip the 32K and 4x128K decode shapes and the 256-step selection-cache run")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 512 MiB copy kernel (for HBM byte counters)")
+    ap.add_argument("--profile-only", default=None,
+                    choices=["qwen2-7b-shape-128k", "qwen2-7b-shape-128k-hit", "qwen2-7b-shape-32k",
+                             "llama3-8b-shape-4x128k", "tiny-4q2kv-d64-4k-f32", "selcache-run",
+                             "prefill-512x64k"],
+                    help="only run --warmup then --steps steps of one workload (for rocprofv3 "
+                         "kernel traces and counters); prints one short JSON line")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -680,6 +715,9 @@ def main():
     import sparse_kv_cache_ts_amd as ts
     import workloads as W
     ts.load()
+    if args.profile_only:
+        profile_only(ts, W, args.profile_only, args.steps, args.warmup)
+        return
 
     cfg = W.QWEN_128K
     read_peak, read_op = measure_read_peak()
