@@ -18,11 +18,11 @@
 // two lanes 16 apart, whose sums meet by a lane swap.
 //
 // Pass 1 (prefill_lse_kernel): work-group = (KV head g, block of queries, key
-// split); 4 waves x 64 rows, each wave streams the same keys. Per tile of 16
-// keys a wave computes S with 16 MFMAs (4 row tiles x 4 k-steps for d=128),
-// then an online max/sum of exp2 per row with one exp per element. The 16
-// lanes that share a row are folded with DPP at the end; each (row, split)
-// leaves a partial.
+// split); 8 waves x 64 rows read the same keys, staged once in LDS. Per tile
+// of 16 keys a wave computes S with 16 MFMAs (4 row tiles x 4 k-steps for
+// d=128), then a lazily rescaled max/sum of exp2 per row with one exp per
+// element. The 16 lanes that share a row are folded at the end; each (row,
+// split) leaves a partial.
 // Merge (prefill_merge_kernel): partials -> lse per (query, head).
 // Pass 2 (prefill_votes_kernel): work-group = (block of 32 queries, key
 // split), one wave per KV head; each wave recomputes S for its 128 rows per
@@ -81,6 +81,16 @@ __device__ __forceinline__ void qk_tile(const bf16x8_t (&qf)[RT][KS], const uint
 }
 
 // ---- pass 1 -----------------------------------------------------------------
+// Work-group = (KV head g, block of queries, key split), 8 waves of 64 rows
+// (4 row tiles), two waves per SIMD so that one wave's vector work fills the
+// other's stalls. The work-group's keys go through LDS in chunks of
+// kPrefillChunk1 keys, double-buffered: every thread requests its share of
+// chunk c+2 while chunk c is computed and stores it one chunk later, one
+// barrier per chunk; the waves read their MFMA B fragments from LDS (the
+// schedule is spelled out at the loop). Staged key rows are
+// padded by 16 bytes, so the 16 rows read by one 16-lane pass start in
+// different banks.
+//
 // Keys go in groups of two 16-key tiles. Each row keeps a reference M (base-2
 // units, scale2 * s) and the sum S of exp2(scale2 * s - M); the reference only
 // moves when a score exceeds it by a margin (see update below), so most
@@ -88,24 +98,40 @@ __device__ __forceinline__ void qk_tile(const bf16x8_t (&qf)[RT][KS], const uint
 // -inf and add 0. M starts at a finite -1e30, so a row with nothing seen yet
 // rescales by exp2(0) = 1 and no inf - inf or 0 * inf arises.
 template <int GP, int D>
-__global__ __launch_bounds__(256) void prefill_lse_kernel(PrefillParams p) {
-  constexpr int KS = D / 32;      // k-steps per tile
-  constexpr int RT = kPrefillRT1;  // row tiles per wave
-  constexpr int QW = 16 * RT / GP; // queries per wave
-  constexpr int QB = 4 * QW;       // queries per work-group (4 waves)
+__global__ __launch_bounds__(512) void prefill_lse_kernel(PrefillParams p) {
+  constexpr int KS = D / 32;           // k-steps per tile
+  constexpr int RT = kPrefillRT1;      // row tiles per wave
+  constexpr int NW = 8;                // waves per work-group
+  constexpr int QW = 16 * RT / GP;     // queries per wave
+  constexpr int QB = NW * QW;          // queries per work-group
+  constexpr int CK = kPrefillChunk1;   // keys per LDS chunk
+  constexpr int CG = CK / 32;          // groups per chunk
+  constexpr int PITCH = D * 2 + 16;    // bytes per staged key row
+  constexpr int PPR = D * 2 / 16;      // 16-byte pieces per key row
+  constexpr int NLD = CK * PPR / (NW * 64);   // pieces per thread per chunk
+  static_assert(NLD * NW * 64 == CK * PPR, "chunk staging");
+  __shared__ __align__(16) unsigned char s_k[2][CK * PITCH];
+
   const int nqb = (p.chunk + QB - 1) / QB;
   const int f = xcd_flat(blockIdx.x, gridDim.x);
   const int qblk = f % nqb;
   const int g = (f / nqb) % p.Hkv;
   const int split = f / (nqb * p.Hkv);
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  const int qbase = qblk * QB + w * QW;   // first query of this wave
-  if (qbase >= p.chunk) return;           // no rows: this wave has nothing to write
-  const int qlast = min(qbase + QW, p.chunk) - 1;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int k0 = split * p.key_split;
   const int k1 = min(p.n_ctx, k0 + p.key_split);
-  const int kend = min(k1, p.q_pos0 + qlast + 1);     // keys no row of this wave sees start here
-  const int kall = p.q_pos0 + qbase + 1;              // keys below this every row sees
+  // the work-group streams the keys its last query sees; a wave computes only
+  // the groups its own rows see (waves past the chunk compute none, but still
+  // stage keys and meet every barrier)
+  const int kend_wg = min(k1, p.q_pos0 + min(qblk * QB + QB, p.chunk));
+  const int nch = kend_wg > k0 ? (kend_wg - k0 + CK - 1) / CK : 0;
+  const int qbase = qblk * QB + w * QW;   // first query of this wave
+  const bool rows = qbase < p.chunk;
+  const int qlast = min(qbase + QW, p.chunk) - 1;
+  const int kend = rows ? min(k1, p.q_pos0 + qlast + 1) : k0;   // keys no row of this wave sees start here
+  const int kall = p.q_pos0 + qbase + 1;                        // keys below this every row sees
+  const int ngw = kend > k0 ? (kend - k0 + 31) / 32 : 0;        // groups this wave computes
+  const int gfull = min(kall, kend) - k0 >= 32 ? (min(kall, kend) - k0) / 32 : 0;  // of them unmasked
 
   bf16x8_t qf[RT][KS];
 #pragma unroll
@@ -120,9 +146,33 @@ __global__ __launch_bounds__(256) void prefill_lse_kernel(PrefillParams p) {
     for (int i = 0; i < 4; ++i) { M[rt][i] = -1e30f; S[rt][i] = 0.f; }
   const float sc2 = p.scale2;
 
-  // one group of two 16-key tiles: scores, then the running max/sum update.
-  // Scores are scaled first (a product is a canonical float, so the maxima
-  // need no NaN-quieting extra instructions).
+  // this thread's pieces of the chunk starting at key kc (keys past the
+  // context clamp to its last key: in bounds, never used)
+  auto stage_load = [&](int kc, uint4 (&st)[NLD]) {
+#pragma unroll
+    for (int i = 0; i < NLD; ++i) {
+      const int pc = tid + i * NW * 64;
+      const int key = min(kc + pc / PPR, p.n_ctx - 1);
+      st[i] = ld16((const char*)p.k + (((size_t)key * p.Hkv + g) * D) * 2 + (pc % PPR) * 16);
+    }
+  };
+  auto stage_store = [&](unsigned char* buf, const uint4 (&st)[NLD]) {
+#pragma unroll
+    for (int i = 0; i < NLD; ++i) {
+      const int pc = tid + i * NW * 64;
+      *reinterpret_cast<uint4*>(buf + (pc / PPR) * PITCH + (pc % PPR) * 16) = st[i];
+    }
+  };
+  // B fragments of group j of a chunk (two 16-key tiles, all k-steps)
+  auto frags = [&](const unsigned char* buf, int j, uint4 (&f0)[KS], uint4 (&f1)[KS]) {
+    const unsigned char* r0 = buf + (j * 32 + (lane & 15)) * PITCH + (lane >> 4) * 16;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      f0[ks] = *reinterpret_cast<const uint4*>(r0 + ks * 64);
+      f1[ks] = *reinterpret_cast<const uint4*>(r0 + 16 * PITCH + ks * 64);
+    }
+  };
+
   // Lazy rescaling: M is a per-row reference, not necessarily the running
   // max. A group adds exp2(scale2 * s - M) directly unless some score of the
   // wave lies more than kLazy above its row's M (terms stay below 2^kLazy, so
@@ -130,6 +180,7 @@ __global__ __launch_bounds__(256) void prefill_lse_kernel(PrefillParams p) {
   // online update, which raises M to the max and rescales S. The first group
   // always does (M starts at a finite -1e30), and later ones rarely do.
   constexpr float kLazy = 20.f;
+  constexpr float kLazyBound = 1048576.f;   // 2^kLazy
   auto update = [&](const f32x4_t (&s0)[RT], const f32x4_t (&s1)[RT], int kb, bool masked) {
     const int key = kb + (lane & 15);
     float d0[RT][4], d1[RT][4];
@@ -169,48 +220,127 @@ __global__ __launch_bounds__(256) void prefill_lse_kernel(PrefillParams p) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) S[rt][i] += ex2(d0[rt][i]) + ex2(d1[rt][i]);
   };
-  auto group = [&](int kb, const uint4 (&ka)[KS], const uint4 (&kb2)[KS]) {
-    f32x4_t s0[RT], s1[RT];
-    qk_tile<RT, KS>(qf, ka, s0);
-    qk_tile<RT, KS>(qf, kb2, s1);
-    // a separate copy of the update for the groups every row sees in full
-    if (kb + 32 <= min(kall, kend)) update(s0, s1, kb, false);
-    else update(s0, s1, kb, true);
+
+  // Unmasked groups run as a software pipeline: the MFMAs of group j+1 are
+  // issued interleaved with the vector work of group j (a wave issues in
+  // order, so without the interleave a group's exponentials would wait for
+  // all of its MFMAs and the next group's MFMAs for all of its exponentials).
+  // That vector work is the lazy fast path: per row the group sum gs =
+  // exp2(d0) + exp2(d1), d = scale2 * s - M. A row whose gs is within
+  // 2^kLazy adds it; the others (a term above 2^kLazy - 1, an overflow, or
+  // the first group, where M = -1e30) are redone by exact(), so the terms
+  // added are bounded exactly as in update().
+  auto fast = [&](const f32x4_t (&s0)[RT], const f32x4_t (&s1)[RT]) {
+    float mx = 0.f;
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float gs = ex2(fmaf(s0[rt][i], sc2, -M[rt][i])) + ex2(fmaf(s1[rt][i], sc2, -M[rt][i]));
+        S[rt][i] = gs <= kLazyBound ? S[rt][i] + gs : S[rt][i];
+        mx = fmaxf(mx, gs);
+      }
+    return mx;
+  };
+  // the rows fast() left out (the same expression picks them): exact online
+  // update, M raised to the row's maximum and S rescaled
+  auto exact = [&](const f32x4_t (&s0)[RT], const f32x4_t (&s1)[RT]) {
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float gs = ex2(fmaf(s0[rt][i], sc2, -M[rt][i])) + ex2(fmaf(s1[rt][i], sc2, -M[rt][i]));
+        if (!(gs <= kLazyBound)) {
+          const float a = s0[rt][i] * sc2, b = s1[rt][i] * sc2;
+          const float m2 = fmaxf(M[rt][i], fmaxf(a, b));
+          S[rt][i] = S[rt][i] * ex2(M[rt][i] - m2) + (ex2(a - m2) + ex2(b - m2));
+          M[rt][i] = m2;
+        }
+      }
+  };
+  auto commit = [&](const f32x4_t (&s0)[RT], const f32x4_t (&s1)[RT], float mx) {
+    if (__builtin_expect(__any(!(mx <= kLazyBound)), 0)) exact(s0, s1);
+  };
+  // MFMAs of the next group (fragments n0, n1) into t0, t1, interleaved one
+  // MFMA to a few vector instructions of the current group's fast path
+  auto overlap = [&](const f32x4_t (&c0)[RT], const f32x4_t (&c1)[RT], const uint4 (&n0)[KS],
+                     const uint4 (&n1)[KS], f32x4_t (&t0)[RT], f32x4_t (&t1)[RT]) {
+    qk_tile<RT, KS>(qf, n0, t0);
+    qk_tile<RT, KS>(qf, n1, t1);
+    const float mx = fast(c0, c1);
+#pragma unroll
+    for (int m = 0; m < 2 * RT * KS; ++m) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
+      __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);   // then up to four VALU
+    }
+    return mx;
   };
 
-  // software pipeline over groups with two fragment sets (A, B) and
-  // unconditional prefetch one group ahead
-  const int ng = (kend > k0) ? (kend - k0 + 31) / 32 : 0;
-  uint4 a0[KS], a1[KS], b0[KS], b1[KS];
-  if (ng > 0) {
-    load_k_tile<D>(p, g, k0, lane, a0);
-    load_k_tile<D>(p, g, k0 + 16, lane, a1);
+  // Chunk c sits in s_k[c & 1]. Iteration c stores chunk c+1 (loaded during
+  // iteration c-1) into the other buffer, requests chunk c+2, computes its
+  // groups, and meets the one barrier of the iteration after its last read of
+  // chunk c: past that barrier chunk c+1 is visible to every wave and chunk
+  // c's buffer is free for chunk c+2. When this chunk and the next are both
+  // unmasked for the wave, the last group's vector work overlaps the MFMAs of
+  // the next chunk's first group (read after the barrier), so the pipeline
+  // runs on across chunks ("carried": sa holds those scores).
+  uint4 st[NLD];
+  if (nch > 0) {
+    stage_load(k0, st);
+    stage_store(s_k[0], st);
+    stage_load(k0 + CK, st);
   }
-  // (scheduling barriers keep the compiler from hoisting a group's MFMAs
-  // above the previous group's work, which would consume the prefetch at once)
-  int gi = 0;
-  for (; gi + 2 < ng; gi += 2) {
-    const int kb = k0 + gi * 32;
-    load_k_tile<D>(p, g, kb + 32, lane, b0);
-    load_k_tile<D>(p, g, kb + 48, lane, b1);
-    __builtin_amdgcn_sched_barrier(0);
-    group(kb, a0, a1);
-    __builtin_amdgcn_sched_barrier(0);
-    load_k_tile<D>(p, g, kb + 64, lane, a0);
-    load_k_tile<D>(p, g, kb + 80, lane, a1);
-    __builtin_amdgcn_sched_barrier(0);
-    group(kb + 32, b0, b1);
-    __builtin_amdgcn_sched_barrier(0);
+  __syncthreads();
+  uint4 fa0[KS], fa1[KS], fb0[KS], fb1[KS];
+  f32x4_t sa0[RT], sa1[RT], sb0[RT], sb1[RT];
+  bool carried = false;
+  for (int c = 0; c < nch; ++c) {
+    const int kc = k0 + c * CK;
+    const unsigned char* buf = s_k[c & 1];
+    unsigned char* nbuf = s_k[(c + 1) & 1];
+    if (c + 1 < nch) stage_store(nbuf, st);
+    stage_load(kc + 2 * CK, st);   // clamped in bounds past the end
+    if ((c + 1) * CG <= gfull) {
+      // the whole chunk is unmasked for this wave
+      if (!carried) {
+        frags(buf, 0, fa0, fa1);
+        qk_tile<RT, KS>(qf, fa0, sa0);
+        qk_tile<RT, KS>(qf, fa1, sa1);
+      }
+      static_assert(CG == 4, "the unrolled chunk below holds four groups");
+      frags(buf, 1, fb0, fb1);
+      float mx = overlap(sa0, sa1, fb0, fb1, sb0, sb1);
+      commit(sa0, sa1, mx);
+      frags(buf, 2, fa0, fa1);
+      mx = overlap(sb0, sb1, fa0, fa1, sa0, sa1);
+      commit(sb0, sb1, mx);
+      frags(buf, 3, fb0, fb1);
+      mx = overlap(sa0, sa1, fb0, fb1, sb0, sb1);
+      commit(sa0, sa1, mx);
+      __syncthreads();
+      carried = (c + 2) * CG <= gfull;   // the next chunk exists and is unmasked too
+      if (carried) {
+        frags(nbuf, 0, fa0, fa1);
+        mx = overlap(sb0, sb1, fa0, fa1, sa0, sa1);
+      } else {
+        mx = fast(sb0, sb1);
+      }
+      commit(sb0, sb1, mx);
+    } else {
+      for (int j = 0; j < CG; ++j) {
+        const int gi = c * CG + j;
+        if (gi < ngw) {
+          frags(buf, j, fa0, fa1);
+          qk_tile<RT, KS>(qf, fa0, sa0);
+          qk_tile<RT, KS>(qf, fa1, sa1);
+          update(sa0, sa1, kc + j * 32, gi >= gfull);
+        }
+      }
+      __syncthreads();
+      carried = false;
+    }
   }
-  if (gi + 1 < ng) {
-    const int kb = k0 + gi * 32;
-    load_k_tile<D>(p, g, kb + 32, lane, b0);
-    load_k_tile<D>(p, g, kb + 48, lane, b1);
-    group(kb, a0, a1);
-    group(kb + 32, b0, b1);
-  } else if (gi < ng) {
-    group(k0 + gi * 32, a0, a1);
-  }
+  if (!rows) return;
 
   // fold the 16 lanes (key columns) that share each row
 #pragma unroll
@@ -398,13 +528,13 @@ __global__ __launch_bounds__(512) void prefill_votes_kernel(PrefillParams p) {
 template <int D>
 static hipError_t launch_lse_g(const PrefillParams& p, hipStream_t s) {
   const int gp = prefill_gp(p.G);
-  const int qb = 64 * kPrefillRT1 / gp;
+  const int qb = prefill_qb1(gp);
   dim3 grid(((p.chunk + qb - 1) / qb) * p.Hkv * p.nsplit1);
   switch (gp) {
-    case 1: TS_KLAUNCH((prefill_lse_kernel<1, D>), grid, dim3(256), 0, s, p); break;
-    case 2: TS_KLAUNCH((prefill_lse_kernel<2, D>), grid, dim3(256), 0, s, p); break;
-    case 4: TS_KLAUNCH((prefill_lse_kernel<4, D>), grid, dim3(256), 0, s, p); break;
-    case 8: TS_KLAUNCH((prefill_lse_kernel<8, D>), grid, dim3(256), 0, s, p); break;
+    case 1: TS_KLAUNCH((prefill_lse_kernel<1, D>), grid, dim3(512), 0, s, p); break;
+    case 2: TS_KLAUNCH((prefill_lse_kernel<2, D>), grid, dim3(512), 0, s, p); break;
+    case 4: TS_KLAUNCH((prefill_lse_kernel<4, D>), grid, dim3(512), 0, s, p); break;
+    case 8: TS_KLAUNCH((prefill_lse_kernel<8, D>), grid, dim3(512), 0, s, p); break;
     default: return hipErrorInvalidValue;   // rejected on the host
   }
   return hipGetLastError();

@@ -1208,8 +1208,8 @@ ts_status plan_prefill(const ts_kv_layout* L, int chunk, int q_pos0, int n_ctx, 
   p.G = g.G;
   p.D = g.d;
   p.scale2 = g.scale * kLog2eHost;
-  // pass 1: about one work-group of 4 waves per CU
-  const int qb1 = cdiv(chunk, 64 * kPrefillRT1 / prefill_gp(g.G));
+  // pass 1: about one work-group of 8 waves per CU
+  const int qb1 = cdiv(chunk, prefill_qb1(prefill_gp(g.G)));
   int ns1 = std::max(1, 256 / (qb1 * g.Hkv));
   p.key_split = cdiv(cdiv(n_ctx, ns1), 32) * 32;
   p.nsplit1 = cdiv(n_ctx, p.key_split);

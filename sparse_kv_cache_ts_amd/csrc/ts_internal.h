@@ -20,13 +20,15 @@ constexpr int kMaxSplits = 1024;  // attention splits per (sequence, head)
 // attention kernel's ~150 registers per lane allow three 256-thread groups)
 constexpr long kAttendResidentWGs = 768;
 constexpr float kLog2eHost = 1.4426950408889634f;
-// prefill log-sum-exp pass: 16-row MFMA tiles per wave (4 waves per work-group,
-// one KV head); every wave reads the same keys, so more rows per wave means
-// fewer key fragments through each CU's L1
-constexpr int kPrefillRT1 = 8;
+// prefill log-sum-exp pass: 16-row MFMA tiles per wave (8 waves per
+// work-group, one KV head, the keys staged once per work-group in LDS)
+constexpr int kPrefillRT1 = 4;
+constexpr int kPrefillChunk1 = 128;   // keys per LDS chunk of the log-sum-exp pass
 // query heads per KV head as the prefill kernels lay them out: G rounded up
 // to a power of two (0 when G > 8: not built)
 constexpr int prefill_gp(int G) { return G <= 1 ? 1 : G <= 2 ? 2 : G <= 4 ? 4 : G <= 8 ? 8 : 0; }
+// queries per work-group of the log-sum-exp pass
+constexpr int prefill_qb1(int GP) { return 8 * 16 * kPrefillRT1 / GP; }
 // prefill vote pass: 16-row MFMA tiles per wave (one KV head); a work-group
 // covers 16 * prefill_rt2(GP) / GP queries (32, or 16 for GP = 8)
 constexpr int prefill_rt2(int GP) { return GP >= 4 ? 8 : 2 * GP; }
