@@ -37,6 +37,9 @@
  * it; accumulation is fp32); num_kv_heads divides num_q_heads; num_kv_heads <= 64 for
  * bf16, <= 32 for fp32 with head_dim 64 and <= 16 for fp32 with head_dim 128 (one scoring
  * work-group holds a token's rows of every KV head); other shapes return TS_ERR_UNSUPPORTED.
+ * Size limits (TS_ERR_UNSUPPORTED beyond them, so that every size the planner
+ * derives fits its integer type): max_len, n_ctx, chunk, k and row_stride
+ * <= 2^30; batch and max_batch <= 2^20; top-k rows <= 2^24; num_q_heads <= 256.
  */
 #ifndef TS_H
 #define TS_H
@@ -248,7 +251,8 @@ ts_status ts_dense_attend(const ts_kv_layout* layout /*[host]*/, int32_t batch, 
  * ------------------------------------------------------------------------- */
 typedef struct ts_sel_cache ts_sel_cache;
 
-/* Allocates the device state (hipMalloc) and zeroes it; synchronises the device. */
+/* Allocates the device state (hipMalloc) and zeroes it; synchronises the device.
+ * head_dim must be 64 or 128 (TS_ERR_UNSUPPORTED otherwise). */
 ts_status ts_sel_cache_create(int32_t max_batch, int32_t num_q_heads, int32_t head_dim, int32_t k,
                               int32_t compare_mode, ts_sel_cache** out /*[host]*/);
 /* Marks sequences invalid and clears their hit/miss counters, so that their

@@ -173,6 +173,7 @@ struct Geo {
 ts_status check_layout(const ts_kv_layout* L, int batch, Geo* g) {
   if (!L) return fail(TS_ERR_INVALID_ARG, "layout is NULL");
   if (batch < 1) return fail(TS_ERR_INVALID_ARG, "batch must be >= 1 (got %d)", batch);
+  if (batch > kMaxBatch) return fail(TS_ERR_UNSUPPORTED, "batch %d > %d", batch, kMaxBatch);
   if (L->num_q_heads < 1 || L->num_kv_heads < 1)
     return fail(TS_ERR_INVALID_ARG, "head counts must be >= 1");
   if (L->num_q_heads % L->num_kv_heads != 0)
@@ -183,6 +184,8 @@ ts_status check_layout(const ts_kv_layout* L, int batch, Geo* g) {
   if (L->dtype != TS_F32 && L->dtype != TS_BF16)
     return fail(TS_ERR_INVALID_ARG, "unknown dtype %d", L->dtype);
   if (L->max_len < 1) return fail(TS_ERR_INVALID_ARG, "max_len must be >= 1");
+  if (L->max_len > kMaxTokens)
+    return fail(TS_ERR_UNSUPPORTED, "max_len %d > %d", L->max_len, kMaxTokens);
   if (L->num_kv_heads > kMaxHeadsPerWG)
     return fail(TS_ERR_UNSUPPORTED, "num_kv_heads %d > %d", L->num_kv_heads, kMaxHeadsPerWG);
   if (L->num_q_heads > kMaxQHeads)
@@ -225,6 +228,21 @@ ts_status check_layout(const ts_kv_layout* L, int batch, Geo* g) {
   return TS_OK;
 }
 
+ts_status check_k(int k) {
+  if (k < 1) return fail(TS_ERR_INVALID_ARG, "k must be >= 1 (got %d)", k);
+  if (k > kMaxTokens) return fail(TS_ERR_UNSUPPORTED, "k %d > %d", k, kMaxTokens);
+  return TS_OK;
+}
+
+ts_status check_topk_shape(int rows, int row_stride, int k) {
+  if (rows < 1 || row_stride < 1)
+    return fail(TS_ERR_INVALID_ARG, "rows and row_stride must be >= 1 (got %d, %d)", rows, row_stride);
+  if (rows > kMaxRows) return fail(TS_ERR_UNSUPPORTED, "rows %d > %d", rows, kMaxRows);
+  if (row_stride > kMaxTokens)
+    return fail(TS_ERR_UNSUPPORTED, "row_stride %d > %d", row_stride, kMaxTokens);
+  return check_k(k);
+}
+
 // ---- workspace plans -----------------------------------------------------------
 
 struct ScorePlan {
@@ -259,7 +277,11 @@ void plan_attend(const Geo& g, int B, int k, Carve& c, AttendPlan& a) {
   int split = 256;
   while (split > 32 && cols * cdiv(k, split) < 512) split >>= 1;
   while (cdiv(k, split) > kMaxSplits) split <<= 1;
-  while (split < k && cols * cdiv(k, split) > kAttendResidentWGs) split += 64;
+  // the first split of split + 64 i (i >= 0) that reaches k or brings the
+  // grid within kAttendResidentWGs, i.e. cdiv(k, split) <= m
+  const long m = kAttendResidentWGs / cols;
+  const long target = m >= 1 ? std::min<long>(k, cdiv(k, m)) : k;
+  if (split < target) split += 64 * cdiv(target - split, 64);
   a.split = split;
   a.nsplit = cdiv(k, split);
   a.pm = c.take((size_t)B * g.Hq * a.nsplit * 4);
@@ -558,8 +580,7 @@ ts_status ts_score(const ts_kv_layout* L, int32_t batch, const void* q, const vo
 // ----------------------------------------------------------------- ts_topk
 
 ts_status ts_topk_workspace_size(int32_t rows, int32_t row_stride, int32_t k, size_t* bytes) {
-  if (rows < 1 || row_stride < 1 || k < 1)
-    return fail(TS_ERR_INVALID_ARG, "rows, row_stride and k must be >= 1");
+  TS_TRY(check_topk_shape(rows, row_stride, k));
   if (!bytes) return fail(TS_ERR_INVALID_ARG, "bytes is NULL");
   Carve c;
   TopkPlan t;
@@ -605,8 +626,7 @@ static ts_status run_topk(int rows, int row_stride, const float* votes, const in
 
 ts_status ts_topk(int32_t rows, int32_t row_stride, const float* votes, const int32_t* row_lens,
                   int32_t k, int32_t* idx, void* ws, size_t ws_bytes, void* stream) {
-  if (rows < 1 || row_stride < 1 || k < 1)
-    return fail(TS_ERR_INVALID_ARG, "rows, row_stride and k must be >= 1");
+  TS_TRY(check_topk_shape(rows, row_stride, k));
   if (!votes || !row_lens || !idx) return fail(TS_ERR_INVALID_ARG, "NULL tensor pointer");
   Carve c;
   TopkPlan t;
@@ -623,7 +643,7 @@ ts_status ts_sparse_attend_workspace_size(const ts_kv_layout* L, int32_t batch, 
                                           size_t* bytes) {
   Geo g;
   TS_TRY(check_layout(L, batch, &g));
-  if (k < 1) return fail(TS_ERR_INVALID_ARG, "k must be >= 1");
+  TS_TRY(check_k(k));
   if (!bytes) return fail(TS_ERR_INVALID_ARG, "bytes is NULL");
   Carve c;
   AttendPlan a;
@@ -638,7 +658,7 @@ ts_status ts_sparse_attend(const ts_kv_layout* L, int32_t batch, const void* q, 
                            void* stream) {
   Geo g;
   TS_TRY(check_layout(L, batch, &g));
-  if (k < 1) return fail(TS_ERR_INVALID_ARG, "k must be >= 1");
+  TS_TRY(check_k(k));
   if (!q || !k_cache || !v_cache || !seq_lens || !idx || !out)
     return fail(TS_ERR_INVALID_ARG, "NULL tensor pointer");
   if (g.paged && !page_table) return fail(TS_ERR_INVALID_ARG, "paged layout needs a page_table");
@@ -825,7 +845,8 @@ ts_status check_prefill_attend(const ts_kv_layout* L, int chunk, int q_pos0, int
                                Geo* g) {
   TS_TRY(check_layout(L, 1, g));
   if (g->paged) return fail(TS_ERR_UNSUPPORTED, "prefill attention needs a contiguous K/V");
-  if (chunk < 1 || n_ctx < 1 || k < 1) return fail(TS_ERR_INVALID_ARG, "chunk, n_ctx and k must be >= 1");
+  if (chunk < 1 || n_ctx < 1) return fail(TS_ERR_INVALID_ARG, "chunk and n_ctx must be >= 1");
+  TS_TRY(check_k(k));
   if (q_pos0 < 0 || (long)q_pos0 + chunk > n_ctx)
     return fail(TS_ERR_INVALID_ARG, "need 0 <= q_pos0 and q_pos0 + chunk <= n_ctx");
   if (n_ctx > g->max_len) return fail(TS_ERR_INVALID_ARG, "n_ctx exceeds layout max_len");
@@ -838,7 +859,9 @@ ts_status ts_sparse_attend_prefill_workspace_size(const ts_kv_layout* L, int32_t
   if (!bytes) return fail(TS_ERR_INVALID_ARG, "bytes is NULL");
   Geo g;
   TS_TRY(check_layout(L, 1, &g));
-  if (chunk < 1 || k < 1) return fail(TS_ERR_INVALID_ARG, "chunk and k must be >= 1");
+  if (chunk < 1) return fail(TS_ERR_INVALID_ARG, "chunk must be >= 1");
+  if (chunk > kMaxTokens) return fail(TS_ERR_UNSUPPORTED, "chunk %d > %d", chunk, kMaxTokens);
+  TS_TRY(check_k(k));
   Carve c;
   AttendPlan a;
   plan_attend(g, chunk, k, c, a);
@@ -934,6 +957,11 @@ ts_status ts_sel_cache_create(int32_t max_batch, int32_t num_q_heads, int32_t he
     return fail(TS_ERR_INVALID_ARG, "max_batch, num_q_heads, head_dim and k must be >= 1");
   if (compare_mode != 0 && compare_mode != 1)
     return fail(TS_ERR_INVALID_ARG, "compare_mode must be 0 or 1");
+  if (head_dim != 64 && head_dim != 128)
+    return fail(TS_ERR_UNSUPPORTED, "head_dim %d unsupported (64 or 128)", head_dim);
+  if (max_batch > kMaxBatch || num_q_heads > kMaxQHeads || k > kMaxTokens)
+    return fail(TS_ERR_UNSUPPORTED, "max_batch <= %d, num_q_heads <= %d and k <= %d", kMaxBatch,
+                kMaxQHeads, kMaxTokens);
   ts_sel_cache* c = new ts_sel_cache();
   std::memset(&c->dev, 0, sizeof(c->dev));
   c->dev.max_batch = max_batch;
@@ -1013,7 +1041,7 @@ ts_status ts_decode_step_workspace_size(const ts_kv_layout* L, int32_t batch, in
                                         size_t* bytes) {
   Geo g;
   TS_TRY(check_layout(L, batch, &g));
-  if (k < 1) return fail(TS_ERR_INVALID_ARG, "k must be >= 1");
+  TS_TRY(check_k(k));
   if (!bytes) return fail(TS_ERR_INVALID_ARG, "bytes is NULL");
   DecodePlan p;
   plan_decode(g, batch, k, p);
@@ -1197,7 +1225,7 @@ ts_status plan_prefill(const ts_kv_layout* L, int chunk, int q_pos0, int n_ctx, 
   if (q_pos0 < 0 || (long)q_pos0 + chunk > n_ctx)
     return fail(TS_ERR_INVALID_ARG, "need 0 <= q_pos0 and q_pos0 + chunk <= n_ctx");
   if (n_ctx > g.max_len) return fail(TS_ERR_INVALID_ARG, "n_ctx exceeds layout max_len");
-  if (select && k < 1) return fail(TS_ERR_INVALID_ARG, "k must be >= 1");
+  if (select) TS_TRY(check_k(k));
   PrefillParams& p = P->pp;
   p = PrefillParams{};
   p.chunk = chunk;
@@ -1246,7 +1274,9 @@ ts_status ts_score_prefill_workspace_size(const ts_kv_layout* L, int32_t chunk, 
                                           int32_t k, size_t* bytes) {
   if (!bytes) return fail(TS_ERR_INVALID_ARG, "bytes is NULL");
   PrefillPlan P;
-  TS_TRY(plan_prefill(L, chunk, n_ctx - chunk >= 0 ? n_ctx - chunk : 0, n_ctx, k, true, &P));
+  // sized for a chunk at the end of the context (the plan does not depend on q_pos0)
+  const long q0 = (long)n_ctx - chunk;
+  TS_TRY(plan_prefill(L, chunk, q0 >= 0 && q0 <= n_ctx ? (int)q0 : 0, n_ctx, k, true, &P));
   *bytes = P.total;
   return ok();
 }

@@ -15,6 +15,12 @@ constexpr int kVoteTile = 256;     // tokens per vote work-group (pass 2)
 constexpr int kTopkChunk = 2048;   // elements per top-k histogram/partition work-group
 constexpr int kMaxHeadsPerWG = 64; // Hkv * heads-per-slice held by one scoring WG
 constexpr int kMaxQHeads = 256;
+// size limits checked on the host, so that every index and size the planner
+// derives fits its integer type: tokens per sequence (max_len, n_ctx, k,
+// row_stride), sequences per call, and rows of a top-k call
+constexpr int kMaxTokens = 1 << 30;
+constexpr int kMaxBatch = 1 << 20;
+constexpr int kMaxRows = 1 << 24;
 constexpr int kMaxSplits = 1024;  // attention splits per (sequence, head)
 // attention work-groups resident at once on MI355X: 256 CUs x 3 (the bf16
 // attention kernel's ~150 registers per lane allow three 256-thread groups)
