@@ -126,7 +126,9 @@ def test_prefill_rejects_unsupported(gpu_lib):
     assert e.value.status == ts.TS_ERR_UNSUPPORTED
 
 
-ATT_CASES = [SMALL[0], SMALL[1], SMALL[3], SMALL[4]]
+# G = 4 in several shapes, then 1, 7 (the Qwen2-7B layout) and 8 query heads
+# per KV head, whose head slices the attention kernel lays out differently
+ATT_CASES = [SMALL[0], SMALL[1], SMALL[3], SMALL[4], SMALL[5], SMALL[8], SMALL[9]]
 
 
 @pytest.mark.parametrize("case", ATT_CASES, ids=lambda c: c[0].name)
@@ -174,7 +176,8 @@ def test_prefill_full_size_qwen_shape(gpu_lib):
     """A 512-query chunk at the Qwen2-7B shape (28/4 heads: seven query heads
     per KV head, laid out as eight slots), 65536 keys, top-4096: every row's
     selection is the exact top-k of its vote row; 32 rows, the first and last
-    included, against the oracle's votes and decided-token rule."""
+    included, against the oracle's votes and decided-token rule, and the
+    chunk's sparse attention on those rows against the oracle's."""
     from dataclasses import replace
     ts = gpu_lib
     cfg = replace(W.PREFILL_64K, name="prefill-512x64k-qwen2-7b-shape", num_q_heads=28,
@@ -194,6 +197,14 @@ def test_prefill_full_size_qwen_shape(gpu_lib):
     for r, ref in zip(rows, O.prefill_votes(Q, K, q0, rows=rows)):
         _check_votes(votes[r], ref, q0 + r + 1, cfg.num_q_heads)
         check_selection(gi[r], ref, cfg.k)
+    # the chunk's sparse attention at this shape, on the same 32 rows
+    from tests.parity import check_attention
+    out = ts.sparse_attend_prefill(x["q"], x["k_cache"], x["v_cache"], q0, idx)
+    torch.cuda.synchronize()
+    o, V = np64(out), np64(x["v_cache"])
+    for r in rows:
+        n = q0 + r + 1
+        check_attention(o[r], O.sparse_attention(Q[r], K[:n], V[:n], gi[r]), 1e-2)
 
 
 @pytest.mark.timeout(900)
