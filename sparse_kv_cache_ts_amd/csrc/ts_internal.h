@@ -46,7 +46,6 @@ enum CtrlWord : int {
   kCtlCandCount = 0,  // candidates appended to the row's candidate list
   kCtlPrefix = 1,     // top-12-bit bin that holds the k-th largest key
   kCtlNeed = 2,       // elements still to take inside that bin (0: the whole bin)
-  kCtlErr = 7,        // non-zero if a bounded wait gave up
   kCtlHistB = 16,     // 1024 bins of key bits 19..10 over the keys of bin b0 (the partition's candidates)
   kCtlHist0 = 16 + 1024,  // kHistCopiesMax copies of 4096 bins (key bits 31..20), 16 KB apart
   kCtlWords = kCtlHist0 + 4 * 4096,
