@@ -26,6 +26,10 @@ CASES = [
     _cfg("g7-d128-bf16-ragged", 3, 28, 4, 128, 3001, "bf16", 62),
     _cfg("g4-d64-bf16", 2, 32, 8, 64, 777, "bf16", 63, max_len=1000),
     _cfg("g16-d64-bf16", 1, 16, 1, 64, 999, "bf16", 64),
+    # head slices 3, 5 and 6 wide (G = 3, 5, 12)
+    _cfg("g3-d128-bf16-ragged", 2, 6, 2, 128, 2500, "bf16", 65),
+    _cfg("g5-d64-f32", 1, 20, 4, 64, 1500, "f32", 66),
+    _cfg("g12-d128-bf16", 1, 24, 2, 128, 3333, "bf16", 67),
 ]
 
 

@@ -32,6 +32,13 @@ SMALL = [
                 head_dim=128, min_len=2000, max_len=5000, dtype="bf16", k=1024, seed=73),
     W.RunConfig("quest-2seq-32x4-d64-p4", steps=1, batch=2, num_q_heads=32, num_kv_heads=4,
                 head_dim=64, min_len=100, max_len=900, dtype="bf16", k=64, seed=74, page_size=4),
+    # 3, 5 and 6 query heads per KV head
+    W.RunConfig("quest-2seq-6x2-d128-p16", steps=1, batch=2, num_q_heads=6, num_kv_heads=2,
+                head_dim=128, min_len=800, max_len=2500, dtype="bf16", k=256, seed=75),
+    W.RunConfig("quest-1seq-20x4-d64-p16-f32", steps=1, batch=1, num_q_heads=20, num_kv_heads=4,
+                head_dim=64, min_len=1500, max_len=1500, dtype="f32", k=320, seed=76),
+    W.RunConfig("quest-2seq-24x4-d128-p32", steps=1, batch=2, num_q_heads=24, num_kv_heads=4,
+                head_dim=128, min_len=1000, max_len=4000, dtype="bf16", k=512, seed=77, page_size=32),
 ]
 
 

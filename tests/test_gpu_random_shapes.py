@@ -3,9 +3,10 @@
 Sixteen combinations of batch (1-3, ragged lengths), KV heads (1-8), group
 size (1, 2, 4, 7, 8), head_dim (64, 128), dtype (bf16, fp32), sequence
 length (257 .. 20000), k (16 .. 5000) and cache layout (contiguous, or
-paged with 1-, 16- or 64-token pages), drawn once from a fixed seed. Every
-sequence's selection follows the decided-token rule and its attention is
-within the dtype's tolerance of the oracle's over the GPU's selection.
+paged with 1-, 16- or 64-token pages), drawn once from a fixed seed, plus
+eight fixed shapes with group sizes 3, 5, 6, 10 and 12. Every sequence's
+selection follows the decided-token rule and its attention is within the
+dtype's tolerance of the oracle's over the GPU's selection.
 """
 import random
 
@@ -37,6 +38,27 @@ def _cases(n=16, seed=2024):
         lens = [N] + [max(1, N - r.randrange(0, N)) for _ in range(B - 1)]
         out.append((i, B, Hkv * G, Hkv, d, dt, N, k, ps, lens))
     return out
+
+
+# Query-head groups whose head slices take the 3-, 5- and 6-wide kernel
+# instantiations (the slice is the largest divisor of G up to 8): G = 3, 5,
+# 6, and G = 10, 12 as two slices of 5 and 6; bf16 and fp32, contiguous and
+# paged, ragged batches, k above the length of a sequence.
+ODD_GROUPS = [
+    (100, 2, 6, 2, 128, "bf16", 3000, 200, 0, [3000, 1777]),
+    (101, 1, 12, 4, 64, "f32", 2049, 300, 0, [2049]),
+    (102, 1, 40, 8, 64, "bf16", 5000, 500, 16, [5000]),
+    (103, 2, 5, 1, 128, "bf16", 777, 1000, 0, [777, 300]),
+    (104, 1, 24, 4, 128, "f32", 2049, 300, 64, [2049]),
+    (105, 1, 48, 8, 128, "bf16", 4097, 2048, 0, [4097]),
+    (106, 3, 24, 2, 128, "bf16", 2000, 256, 1, [2000, 1999, 1]),
+    (107, 1, 20, 2, 64, "bf16", 6000, 1024, 16, [6000]),
+]
+
+
+@pytest.mark.parametrize("case", ODD_GROUPS, ids=lambda c: f"c{c[0]}-h{c[2]}x{c[3]}-d{c[4]}-{c[5]}-n{c[6]}-k{c[7]}-p{c[8]}")
+def test_decode_step_odd_groups(gpu_lib, case):
+    test_decode_step_random_shape(gpu_lib, case)
 
 
 @pytest.mark.parametrize("case", _cases(), ids=lambda c: f"c{c[0]}-h{c[2]}x{c[3]}-d{c[4]}-{c[5]}-n{c[6]}-k{c[7]}-p{c[8]}")
