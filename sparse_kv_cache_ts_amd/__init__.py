@@ -137,13 +137,14 @@ def _check(st: int, where: str):
         raise TsError(st, where, lib.ts_last_error().decode())
 
 
+# (every pointer argument is declared c_void_p, so plain integers pass as is)
 def _ptr(t: Optional[torch.Tensor]):
-    return None if t is None else ctypes.c_void_p(t.data_ptr())
+    return None if t is None else t.data_ptr()
 
 
 def _stream(stream=None):
     s = stream if stream is not None else torch.cuda.current_stream()
-    return ctypes.c_void_p(s.cuda_stream)
+    return s.cuda_stream
 
 
 def _on(stream):
@@ -355,6 +356,9 @@ class SelCache:
                                              ctypes.byref(h)), "ts_sel_cache_create")
         self._h = h
         self.ws = Workspace()
+        # (layout, workspace bytes) per argument shape: both follow from the
+        # shapes, dtypes and scale alone, so a decode loop builds them once
+        self._plans = {}
 
     def close(self):
         if self._h is not None and self._h.value:
@@ -394,12 +398,27 @@ class SelCache:
                "ts_decode_step_workspace_size")
         return n.value
 
+    def _plan(self, q, k_cache, page_table, scale, sized: bool):
+        key = (tuple(q.shape), q.dtype, tuple(k_cache.shape), k_cache.dtype,
+               None if page_table is None else (tuple(page_table.shape), page_table.dtype), scale)
+        plan = self._plans.get(key)
+        if plan is None:
+            L = make_layout(q, k_cache, page_table, scale)
+            plan = (L, self.workspace_size(L, q.shape[0]) if sized else None)
+            if len(self._plans) >= 64:
+                self._plans.clear()
+            self._plans[key] = plan
+        elif sized and plan[1] is None:
+            plan = (plan[0], self.workspace_size(plan[0], q.shape[0]))
+            self._plans[key] = plan
+        return plan
+
     def decode_step(self, q, k_cache, v_cache, seq_lens, theta: float, page_table=None, scale=None,
                     out=None, idx_out=None, hit_out=None, want_idx=True, stream=None):
         """One decode step: returns (out [B][Hq][d] fp32, idx [B][k] or None, hit [B] int32)."""
         _need_cuda(q, k_cache, v_cache, seq_lens, page_table, out, idx_out, hit_out)
         _kv(q, k_cache, v_cache, seq_lens, page_table)
-        L = make_layout(q, k_cache, page_table, scale)
+        L, nbytes = self._plan(q, k_cache, page_table, scale, True)
         B = q.shape[0]
         _out(out, (B, self.num_q_heads, self.head_dim), torch.float32, "out")
         _out(idx_out, (B, self.k), torch.int32, "idx_out")
@@ -412,7 +431,7 @@ class SelCache:
                 idx_out = torch.empty(B, self.k, dtype=torch.int32, device=dev)
             if hit_out is None:
                 hit_out = torch.empty(B, dtype=torch.int32, device=dev)
-            w = self.ws.get(self.workspace_size(L, B), dev)
+            w = self.ws.get(nbytes, dev)
             _check(self._lib.ts_decode_step(self._h, ctypes.byref(L), B, _ptr(q), _ptr(k_cache),
                                             _ptr(v_cache), _ptr(page_table), _ptr(seq_lens),
                                             float(theta), _ptr(out), _ptr(idx_out), _ptr(hit_out),
@@ -426,7 +445,7 @@ class SelCache:
         output (out [B][Hq][d] fp32, hit_out [B] int32, optional idx_out [B][k])."""
         _need_cuda(q, k_cache, v_cache, seq_lens, page_table, out, idx_out, hit_out)
         _kv(q, k_cache, v_cache, seq_lens, page_table)
-        L = make_layout(q, k_cache, page_table, scale)
+        L = self._plan(q, k_cache, page_table, scale, False)[0]
         B = q.shape[0]
         if out is None or hit_out is None:
             raise ValueError("decode_step_noalloc needs caller-provided out and hit_out")
