@@ -458,6 +458,30 @@ def measure_selcache_run(ts, W):
     cache.close()
     us = [1e3 * ev[t].elapsed_time(ev[t + 1]) for t in range(cfg.steps)]
     hs = hit_steps.cpu().tolist()
+    # the same run replayed from one HIP graph: the cache reset, then the 256
+    # steps, captured once (after an eager step that sizes the workspace); the
+    # replay's decisions must be the eager run's
+    cache = ts.SelCache(B, Hq, d, cfg.k)
+    cache.decode_step(qs[0], kp, vp, lens, cfg.theta, page_table=pt, out=out,
+                      hit_out=hit_steps[0], want_idx=False)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        cache.reset()
+        for t in range(cfg.steps):
+            cache.decode_step(qs[t], kp, vp, lens, cfg.theta, page_table=pt, out=out,
+                              hit_out=hit_steps[t], want_idx=False)
+    graph.replay()
+    torch.cuda.synchronize()
+    g0, g1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    g0.record()
+    graph.replay()
+    g1.record()
+    torch.cuda.synchronize()
+    graph_us = 1e3 * g0.elapsed_time(g1) / cfg.steps
+    graph_same = hit_steps.cpu().tolist() == hs
+    del graph
+    cache.close()
     hit_us = [u for u, h in zip(us, hs) if all(h)]
     miss_us = [u for u, h in zip(us, hs) if not all(h)]
     n_list = lens.tolist()
@@ -472,6 +496,7 @@ def measure_selcache_run(ts, W):
            "event_us_per_step": step_stats(us),
            "hit_step_us": step_stats(hit_us) if hit_us else None,
            "miss_step_us": step_stats(miss_us) if miss_us else None,
+           "graph_us_per_step": round(graph_us, 2), "graph_decisions_match_eager": graph_same,
            "hits": hits, "misses": misses,
            "hit_step_gathered_bytes": gathered, "miss_step_kscan_bytes": kscan}
     if hit_us:
@@ -506,6 +531,8 @@ def config_entry(cfg, r, read_peak):
     if read_peak:
         e["whole_step_frac_of_measured_read_peak"] = round(
             (kscan + gather) / (med * 1e-6) / 1e9 / read_peak, 4)
+    if r.get("graph_step_us"):
+        e["graph_replay_step_us"] = r["graph_step_us"]
     ku = r.get("kernels_us")
     if ku and "score_pass1" in ku and "attend" in ku:
         ts_, ta = ku["score_pass1"] * 1e-6, ku["attend"] * 1e-6
@@ -526,7 +553,7 @@ def measure_configs(ts, W, steps, warmup, read_peak):
                       ("llama3-8b-shape-4x128k", W.LLAMA_4x128K)):
         kv = 2 * cfg.batch * cfg.seq_len * kv_bytes_per_token(cfg)
         copies = max(3, min(64, -(-768_000_000 // kv)))
-        r, _ = measure_decode(ts, W, cfg, steps, warmup, copies, 1.0, True, name)
+        r, _ = measure_decode(ts, W, cfg, steps, warmup, copies, 1.0, True, name, graph=True)
         res[name] = config_entry(cfg, r, read_peak)
         res[name]["kv_copies"] = copies
     return res
