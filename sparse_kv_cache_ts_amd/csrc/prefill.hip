@@ -68,6 +68,12 @@ __device__ __forceinline__ void load_k_tile(const PrefillParams& p, int g, int k
   for (int ks = 0; ks < D / 32; ++ks) kf[ks] = ld16(base + ks * 64);
 }
 
+// compile-time flag of the vote pass: whether a tile's terms need the causal mask
+template <bool B>
+struct Masked {
+  static constexpr bool value = B;
+};
+
 template <int RT, int KS>
 __device__ __forceinline__ void qk_tile(const bf16x8_t (&qf)[RT][KS], const uint4 (&kf)[KS], f32x4_t (&s)[RT]) {
   // k-steps outer, row tiles inner: consecutive MFMAs are independent, so
@@ -390,13 +396,16 @@ __global__ __launch_bounds__(256) void prefill_merge_kernel(PrefillParams p) {
 }
 
 // ---- pass 2 -----------------------------------------------------------------
-// Work-group = (block of QB queries, kPrefillKeys2 keys), one wave per KV head.
-// Per 16-key tile each wave adds exp2(scale2 * s - lse) over its G query heads
-// (in registers, and for GP = 8 with the partner lane 16 away); after a
-// barrier the KV-head partials are summed in a fixed order into an LDS vote
-// tile, which is written to HBM once at the end. The loop issues no global
-// stores, so its waits are for the one K tile they need (prefetched a tile
-// ahead).
+// Work-group = (block of QB queries, spw2 consecutive splits of kPrefillKeys2
+// keys), one wave per KV head; the queries and their LSEs are loaded once and
+// serve every split (about one round of work-groups, one per CU, so these
+// loads and the vote-tile writes are paid once per CU rather than once per
+// split). Per 16-key tile each wave adds exp2(scale2 * s - lse) over its G
+// query heads (in registers, and for GP = 8 with the partner lane 16 away);
+// after a barrier the KV-head partials are summed in a fixed order into an
+// LDS vote tile, which is written to HBM at the end of the split. The tile
+// loop issues no global stores, so its waits are for the one K tile they need
+// (prefetched a tile ahead).
 template <int GP, int D>
 __global__ __launch_bounds__(512) void prefill_votes_kernel(PrefillParams p) {
   constexpr int KS = D / 32;
@@ -409,16 +418,14 @@ __global__ __launch_bounds__(512) void prefill_votes_kernel(PrefillParams p) {
   const int nqb = (p.chunk + QB - 1) / QB;
   const int f = xcd_flat(blockIdx.x, gridDim.x);
   const int qblk = f % nqb;
-  const int split = f / nqb;
+  const int split0 = (f / nqb) * p.spw2;
+  const int split1 = min(p.nsplit2, split0 + p.spw2);
   const int tid = threadIdx.x, lane = tid & 63, g = tid >> 6;   // one wave per KV head
   const int nw = blockDim.x >> 6;
   const int qbase = qblk * QB;
   const int qlast = min(qbase + QB, p.chunk) - 1;
-  const int k0 = split * KT;
-  const int k1 = min(p.n_ctx, k0 + KT);
-  const int kend = min(k1, p.q_pos0 + qlast + 1);   // keys from here on: zero votes
   const int kall = p.q_pos0 + qbase + 1;            // keys below this: no mask
-  const int nt = kend > k0 ? (kend - k0 + 15) / 16 : 0;
+  int k0 = 0;                                        // the current split's first key
 
   bf16x8_t qf[RT][KS];
 #pragma unroll
@@ -443,11 +450,11 @@ __global__ __launch_bounds__(512) void prefill_votes_kernel(PrefillParams p) {
   // two tiles a barrier, then the fixed-order sum over the KV heads into the
   // LDS vote tile (flush). Tile pairs alternate between the two buffers, so
   // one barrier per 32 keys suffices.
-  auto tile_c = [&](int t, const uint4 (&kf)[KS], int b, int half) {
+  auto tile_c = [&](int t, const uint4 (&kf)[KS], int b, int half, auto masked) {
     const int kb = k0 + t * 16;
     f32x4_t sc[RT];
     qk_tile<RT, KS>(qf, kf, sc);
-    const bool all = kb + 16 <= kall;
+    const bool all = !decltype(masked)::value || kb + 16 <= kall;
     const int key = kb + (lane & 15);
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt) {
@@ -491,37 +498,54 @@ __global__ __launch_bounds__(512) void prefill_votes_kernel(PrefillParams p) {
   // barriers keep the compiler from consuming a prefetch as soon as it is
   // issued.
   uint4 ka[KS], kb_[KS];
-  if (nt > 0) load_k_tile<D>(p, g, k0, lane, ka);
-  int t = 0, pb = 0;
-  for (; t + 2 < nt; t += 2) {
-    load_k_tile<D>(p, g, k0 + (t + 1) * 16, lane, kb_);
-    __builtin_amdgcn_sched_barrier(0);
-    tile_c(t, ka, pb, 0);
-    __builtin_amdgcn_sched_barrier(0);
-    load_k_tile<D>(p, g, k0 + (t + 2) * 16, lane, ka);
-    __builtin_amdgcn_sched_barrier(0);
-    tile_c(t + 1, kb_, pb, 1);
-    __builtin_amdgcn_sched_barrier(0);
-    flush(t, pb, 32);
-    pb ^= 1;
-  }
-  if (t + 1 < nt) {
-    load_k_tile<D>(p, g, k0 + (t + 1) * 16, lane, kb_);
-    tile_c(t, ka, pb, 0);
-    tile_c(t + 1, kb_, pb, 1);
-    flush(t, pb, 32);
-  } else if (t < nt) {
-    tile_c(t, ka, pb, 0);
-    flush(t, pb, 16);
-  }
-  __syncthreads();
-  // the vote tile, coalesced along each query's row; keys no query of the
-  // block sees are zero
-  const int nk = k1 - k0;
-  for (int e = tid; e < QB * nk; e += blockDim.x) {
-    const int ql = e / nk, c = e - ql * nk;
-    if (qbase + ql < p.chunk)
-      p.votes[(size_t)(qbase + ql) * p.n_ctx + k0 + c] = (k0 + c < kend) ? s_out[ql][c] : 0.f;
+  int pb = 0;
+  // the first tile of each split is requested before the previous split's
+  // vote tile is written
+  if (split0 < split1) load_k_tile<D>(p, g, split0 * KT, lane, ka);
+  for (int split = split0; split < split1; ++split) {
+    k0 = split * KT;
+    const int k1 = min(p.n_ctx, k0 + KT);
+    const int kend = min(k1, p.q_pos0 + qlast + 1);   // keys from here on: zero votes
+    const int nt = kend > k0 ? (kend - k0 + 15) / 16 : 0;
+    // tiles [0, nfull) hold only keys every query of the block sees: their
+    // terms need no causal mask
+    const int nfull = min(nt, max(kall - k0, 0) / 16);
+    auto pair = [&](int t, auto masked) {
+      load_k_tile<D>(p, g, k0 + (t + 1) * 16, lane, kb_);
+      __builtin_amdgcn_sched_barrier(0);
+      tile_c(t, ka, pb, 0, masked);
+      __builtin_amdgcn_sched_barrier(0);
+      load_k_tile<D>(p, g, k0 + (t + 2) * 16, lane, ka);
+      __builtin_amdgcn_sched_barrier(0);
+      tile_c(t + 1, kb_, pb, 1, masked);
+      __builtin_amdgcn_sched_barrier(0);
+      flush(t, pb, 32);
+      pb ^= 1;
+    };
+    int t = 0;
+    for (; t + 2 < nt; t += 2) {
+      if (t + 2 <= nfull) pair(t, Masked<false>{});
+      else pair(t, Masked<true>{});
+    }
+    if (t + 1 < nt) {
+      load_k_tile<D>(p, g, k0 + (t + 1) * 16, lane, kb_);
+      tile_c(t, ka, pb, 0, Masked<true>{});
+      tile_c(t + 1, kb_, pb, 1, Masked<true>{});
+      flush(t, pb, 32);
+    } else if (t < nt) {
+      tile_c(t, ka, pb, 0, Masked<true>{});
+      flush(t, pb, 16);
+    }
+    if (split + 1 < split1) load_k_tile<D>(p, g, (split + 1) * KT, lane, ka);
+    __syncthreads();
+    // the vote tile, coalesced along each query's row; keys no query of the
+    // block sees are zero. The next split's first flush, behind a barrier,
+    // is the first write to s_out after these reads.
+    const int nk = k1 - k0;
+    for (int ql = 0; ql <= qlast - qbase; ++ql) {
+      float* row = p.votes + (size_t)(qbase + ql) * p.n_ctx + k0;
+      for (int c = tid; c < nk; c += blockDim.x) row[c] = (k0 + c < kend) ? s_out[ql][c] : 0.f;
+    }
   }
 }
 
@@ -555,7 +579,7 @@ template <int D>
 static hipError_t launch_votes_g(const PrefillParams& p, hipStream_t s) {
   const int gp = prefill_gp(p.G);
   const int qb = 16 * prefill_rt2(gp) / gp;
-  dim3 grid(((p.chunk + qb - 1) / qb) * p.nsplit2);
+  dim3 grid(((p.chunk + qb - 1) / qb) * ((p.nsplit2 + p.spw2 - 1) / p.spw2));
   dim3 block(64 * p.Hkv);
   switch (gp) {
     case 1: TS_KLAUNCH((prefill_votes_kernel<1, D>), grid, block, 0, s, p); break;

@@ -1243,6 +1243,11 @@ ts_status plan_prefill(const ts_kv_layout* L, int chunk, int q_pos0, int n_ctx, 
   p.nsplit1 = cdiv(n_ctx, p.key_split);
   p.key_split2 = kPrefillKeys2;
   p.nsplit2 = cdiv(n_ctx, p.key_split2);
+  // vote pass: one round of work-groups, each over consecutive key splits
+  // of one query block (its queries and LSEs are loaded once)
+  const long qb2 = cdiv(chunk, 16 * prefill_rt2(prefill_gp(g.G)) / prefill_gp(g.G));
+  const long items2 = qb2 * p.nsplit2;
+  p.spw2 = (int)std::min<long>(p.nsplit2, std::max<long>(1, (items2 + kPrefillVoteWGs - 1) / kPrefillVoteWGs));
   Carve c;
   P->lse_part = c.take((size_t)chunk * g.Hq * p.nsplit1 * 8);
   P->lse = c.take((size_t)chunk * g.Hq * 4);

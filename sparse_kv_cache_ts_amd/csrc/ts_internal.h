@@ -38,7 +38,8 @@ constexpr int prefill_qb1(int GP) { return 8 * 16 * kPrefillRT1 / GP; }
 // prefill vote pass: 16-row MFMA tiles per wave (one KV head); a work-group
 // covers 16 * prefill_rt2(GP) / GP queries (32, or 16 for GP = 8)
 constexpr int prefill_rt2(int GP) { return GP >= 4 ? 8 : 2 * GP; }
-constexpr int kPrefillKeys2 = 512; // keys per vote-pass work-group (its LDS vote tile)
+constexpr int kPrefillKeys2 = 512; // keys per vote-pass split (the LDS vote tile)
+constexpr int kPrefillVoteWGs = 256;   // vote-pass work-groups that run at once (one per CU)
 
 // ---- per-row control block (uint32 words) ----------------------------------
 // Zeroed at the start of every call that uses it.
@@ -241,6 +242,7 @@ struct PrefillParams {
   int chunk, q_pos0, n_ctx, Hq, Hkv, G, D;
   int key_split, nsplit1;   // keys per work-group and splits of the log-sum-exp pass
   int key_split2, nsplit2;  // the same for the vote pass
+  int spw2;                 // vote pass: consecutive key splits per work-group
   float scale2;
 };
 
