@@ -41,6 +41,18 @@ SMALL = [
 ]
 
 
+# Chunks whose vote pass has more (query block, 512-key split) items than
+# work-groups that run at once, so each vote work-group walks several
+# consecutive splits: 3, 3 and 2 of them here, with a shorter last group
+# (1, 2 and 1 splits), a partial last split (64, 305 and 124 keys), and for
+# the mid-context chunk whole splits past every row's causal limit.
+MULTI_SPLIT = [
+    _cfg("c256-n40000-h32x8-d128", 256, 40000, 32, 8, 128, 2048, 42),
+    _cfg("g7-c200-n30001-h28x4-d128-mid", 200, 30001, 28, 4, 128, 1024, 43, q_pos0=20000),
+    _cfg("g2-c150-n50300-h16x8-d64", 150, 50300, 16, 8, 64, 1000, 44),
+]
+
+
 def _check_votes(votes_row, ref, n_vis, Hq):
     v = np64(votes_row)
     assert (v[n_vis:] == 0).all(), "votes past the causal limit must be 0"
@@ -67,6 +79,27 @@ def test_prefill_votes_and_select(gpu_lib, case):
         # selection from the GPU's own vote row must be exact top-k of it ...
         assert (gi[i] == O.top_k(np32(votes[i, :q0 + i + 1]).astype(np.float64), cfg.k)).all()
         # ... and agree with the oracle's selection on every decided token
+        check_selection(gi[i], ref, cfg.k)
+
+
+@pytest.mark.parametrize("case", MULTI_SPLIT, ids=lambda c: c[0].name)
+def test_prefill_multi_split_work_groups(gpu_lib, case):
+    """Every row of the chunk: votes entry by entry against the oracle, zeros
+    past the causal limit, and the selection (exact top-k of the GPU's own
+    row, decided tokens as in the oracle's)."""
+    ts = gpu_lib
+    cfg, q0 = case
+    x = W.gen_prefill(cfg, device="cuda")
+    votes, idx = ts.select_prefill(x["q"], x["k_cache"], q0, cfg.k)
+    torch.cuda.synchronize()
+    V32 = np32(votes)
+    assert (V32[:, q0 + cfg.chunk:] == 0).all()
+    gi = idx.cpu().numpy()
+    refs = O.prefill_votes(np64(x["q"]), np64(x["k_cache"]), q0)
+    for i, ref in enumerate(refs):
+        n = q0 + i + 1
+        _check_votes(votes[i], ref, n, cfg.num_q_heads)
+        assert np.array_equal(gi[i], O.top_k(V32[i, :n].astype(np.float64), cfg.k)), f"row {i}"
         check_selection(gi[i], ref, cfg.k)
 
 
