@@ -406,67 +406,71 @@ __global__ __launch_bounds__(256) void votes_kernel(VoteParams p) {
   const int li = tid & 7;                        // lane in the group (fast path)
   float4 lse4 = make_float4(0.f, 0.f, 0.f, 0.f);
   if (fast && Hq <= 32) lse4 = ldf4(p.lse + (size_t)b * Hq + min(4 * li, Hq - 4));
-  const int start = blockIdx.x * kVoteTile;
-  if (hitv || start >= len) return;
+  // tiles blockIdx.x, blockIdx.x + gridDim.x, ...: a capped grid keeps the
+  // launch small on a Selection-Cache hit (every work-group returns at once),
+  // and each work-group zeroes and flushes its histogram once
+  if (hitv || (int)blockIdx.x * kVoteTile >= len) return;
   if (!fast || Hq > 32)
     for (int h = tid; h < Hq; h += 256) s_lse[h] = p.lse[(size_t)b * Hq + h];
   if (p.do_hist)
     for (int i = tid; i < (1 << kHist0Bits); i += 256) s_hist[i] = 0u;
   __syncthreads();
 
-  if (fast) {
-    constexpr int TPG = 8;                       // tokens per lane group and round
-    constexpr int WT = kVoteTile / 4;            // tokens per wave
-    const int wv = tid >> 6, gi = (tid >> 3) & 7;
-    const int nr = (Hq + 31) / 32;               // 16-byte loads per lane and token
-    for (int c0 = 0; c0 < WT; c0 += 8 * TPG) {
-      float v[TPG];
+  for (int start = blockIdx.x * kVoteTile; start < len; start += gridDim.x * kVoteTile) {
+    if (fast) {
+      constexpr int TPG = 8;                       // tokens per lane group and round
+      constexpr int WT = kVoteTile / 4;            // tokens per wave
+      const int wv = tid >> 6, gi = (tid >> 3) & 7;
+      const int nr = (Hq + 31) / 32;               // 16-byte loads per lane and token
+      for (int c0 = 0; c0 < WT; c0 += 8 * TPG) {
+        float v[TPG];
 #pragma unroll
-      for (int t = 0; t < TPG; ++t) v[t] = 0.f;
-      for (int r = 0; r < nr; ++r) {
-        const int h = 32 * r + 4 * li;
-        const bool has = h < Hq;
-        float4 x[TPG];
+        for (int t = 0; t < TPG; ++t) v[t] = 0.f;
+        for (int r = 0; r < nr; ++r) {
+          const int h = 32 * r + 4 * li;
+          const bool has = h < Hq;
+          float4 x[TPG];
+#pragma unroll
+          for (int t = 0; t < TPG; ++t) {
+            const int j = start + wv * WT + c0 + t * 8 + gi;
+            x[t] = (has && j < len) ? ldf4(p.logits + ((size_t)b * p.Lpad + j) * Hq + h)
+                                    : make_float4(-INFINITY, -INFINITY, -INFINITY, -INFINITY);
+          }
+          if (has) {
+            float l0, l1, l2, l3;
+            if (Hq <= 32) {
+              l0 = lse4.x; l1 = lse4.y; l2 = lse4.z; l3 = lse4.w;
+            } else {
+              l0 = s_lse[h]; l1 = s_lse[h + 1]; l2 = s_lse[h + 2]; l3 = s_lse[h + 3];
+            }
+#pragma unroll
+            for (int t = 0; t < TPG; ++t)
+              v[t] += (ex2(x[t].x - l0) + ex2(x[t].y - l1)) + (ex2(x[t].z - l2) + ex2(x[t].w - l3));
+          }
+        }
 #pragma unroll
         for (int t = 0; t < TPG; ++t) {
+          // sum over the 8 lanes of the group (every lane gets it)
+          float sum = v[t];
+          sum += dpp_f<0xB1>(sum);
+          sum += dpp_f<0x4E>(sum);
+          sum += dpp_f<0x141>(sum);
           const int j = start + wv * WT + c0 + t * 8 + gi;
-          x[t] = (has && j < len) ? ldf4(p.logits + ((size_t)b * p.Lpad + j) * Hq + h)
-                                  : make_float4(-INFINITY, -INFINITY, -INFINITY, -INFINITY);
-        }
-        if (has) {
-          float l0, l1, l2, l3;
-          if (Hq <= 32) {
-            l0 = lse4.x; l1 = lse4.y; l2 = lse4.z; l3 = lse4.w;
-          } else {
-            l0 = s_lse[h]; l1 = s_lse[h + 1]; l2 = s_lse[h + 2]; l3 = s_lse[h + 3];
+          if (li == 0 && j < len) {
+            p.votes[(size_t)b * p.vote_stride + j] = sum;
+            if (p.do_hist) atomicAdd(&s_hist[float_key(sum) >> (32 - kHist0Bits)], 1u);
           }
-#pragma unroll
-          for (int t = 0; t < TPG; ++t)
-            v[t] += (ex2(x[t].x - l0) + ex2(x[t].y - l1)) + (ex2(x[t].z - l2) + ex2(x[t].w - l3));
         }
       }
-#pragma unroll
-      for (int t = 0; t < TPG; ++t) {
-        // sum over the 8 lanes of the group (every lane gets it)
-        float sum = v[t];
-        sum += dpp_f<0xB1>(sum);
-        sum += dpp_f<0x4E>(sum);
-        sum += dpp_f<0x141>(sum);
-        const int j = start + wv * WT + c0 + t * 8 + gi;
-        if (li == 0 && j < len) {
-          p.votes[(size_t)b * p.vote_stride + j] = sum;
-          if (p.do_hist) atomicAdd(&s_hist[float_key(sum) >> (32 - kHist0Bits)], 1u);
-        }
+    } else {
+      // any head count: one token per thread
+      for (int j = start + tid; j < min(len, start + kVoteTile); j += 256) {
+        const float* lg = p.logits + ((size_t)b * p.Lpad + j) * Hq;
+        float v = 0.f;
+        for (int h = 0; h < Hq; ++h) v += ex2(lg[h] - s_lse[h]);
+        p.votes[(size_t)b * p.vote_stride + j] = v;
+        if (p.do_hist) atomicAdd(&s_hist[float_key(v) >> (32 - kHist0Bits)], 1u);
       }
-    }
-  } else {
-    // any head count: one token per thread
-    for (int j = start + tid; j < min(len, start + kVoteTile); j += 256) {
-      const float* lg = p.logits + ((size_t)b * p.Lpad + j) * Hq;
-      float v = 0.f;
-      for (int h = 0; h < Hq; ++h) v += ex2(lg[h] - s_lse[h]);
-      p.votes[(size_t)b * p.vote_stride + j] = v;
-      if (p.do_hist) atomicAdd(&s_hist[float_key(v) >> (32 - kHist0Bits)], 1u);
     }
   }
   if (!p.do_hist) return;

@@ -302,6 +302,10 @@ void plan_topk(int rows, int row_stride, Carve& c, TopkPlan& t, bool own_ctrl) {
 
 // histogram copies for `wgs` work-groups adding into one row's first histogram
 int hist_copies_for(int wgs) { return std::max(1, std::min(kHistCopiesMax, wgs / 64)); }
+// vote work-groups per sequence: one per tile, at most kVoteWGsMax over the batch
+int vote_grid(int max_len, int batch) {
+  return std::max(1, std::min(cdiv(max_len, kVoteTile), kVoteWGsMax / std::max(batch, 1)));
+}
 int ctrl_words_for(int copies) { return kCtlHist0 + copies * (1 << kHist0Bits); }
 
 TopkParams topk_params(const TopkPlan& t, void* ws, int rows, int row_stride, int k,
@@ -573,7 +577,7 @@ ts_status ts_score(const ts_kv_layout* L, int32_t batch, const void* q, const vo
   LseParams lp = lse_params(g, s, batch, ws, seq_lens, nullptr);
   TS_LAUNCH_K(kKLse, launch_lse(lp, st), "log-sum-exp");
   VoteParams vp = vote_params(g, s, batch, ws, seq_lens, nullptr, votes, g.max_len, 0);
-  TS_LAUNCH_K(kKVotes, launch_votes(vp, cdiv(g.max_len, kVoteTile), st), "votes");
+  TS_LAUNCH_K(kKVotes, launch_votes(vp, vote_grid(g.max_len, batch), st), "votes");
   return ok();
 }
 
@@ -1083,7 +1087,7 @@ ts_status decode_launch(ts_sel_cache* cache, const Geo& g, const DecodePlan& p, 
 
   // 1+2. Selection-Cache decision per sequence, then the K-scan on misses,
   // and the reset of the top-k control blocks
-  const int vote_wgs = cdiv(g.max_len, kVoteTile);
+  const int vote_wgs = vote_grid(g.max_len, batch);
   const int copies = hist_copies_for(vote_wgs);
   const int32_t* hit = cache->dev.hit;
   // Fused, every K-scan work-group requests its first keys before the
