@@ -391,6 +391,7 @@ __global__ __launch_bounds__(64) void lse_kernel(LseParams p) {
 // Hq > 32) with one 16-byte load, a wave instruction reads eight consecutive
 // tokens' rows as one contiguous range, and the lanes' partial sums meet by
 // DPP. Each group takes 8 tokens, all loads issued before any exp2.
+template <bool WALK>
 __global__ __launch_bounds__(256) void votes_kernel(VoteParams p) {
   __shared__ float s_lse[kMaxQHeads];
   __shared__ uint32_t s_hist[1 << kHist0Bits];
@@ -406,17 +407,20 @@ __global__ __launch_bounds__(256) void votes_kernel(VoteParams p) {
   const int li = tid & 7;                        // lane in the group (fast path)
   float4 lse4 = make_float4(0.f, 0.f, 0.f, 0.f);
   if (fast && Hq <= 32) lse4 = ldf4(p.lse + (size_t)b * Hq + min(4 * li, Hq - 4));
-  // tiles blockIdx.x, blockIdx.x + gridDim.x, ...: a capped grid keeps the
-  // launch small on a Selection-Cache hit (every work-group returns at once),
-  // and each work-group zeroes and flushes its histogram once
-  if (hitv || (int)blockIdx.x * kVoteTile >= len) return;
+  // WALK: tiles blockIdx.x, blockIdx.x + gridDim.x, ... (a grid capped below
+  // the tile count keeps the launch small on a Selection-Cache hit, when every
+  // work-group returns at once; each work-group zeroes and flushes its
+  // histogram once); otherwise tile blockIdx.x only. (A bitwise or: both
+  // loads stay in flight together, no second round trip after the flag.)
+  if ((hitv != 0) | ((int)blockIdx.x * kVoteTile >= len)) return;
   if (!fast || Hq > 32)
     for (int h = tid; h < Hq; h += 256) s_lse[h] = p.lse[(size_t)b * Hq + h];
   if (p.do_hist)
     for (int i = tid; i < (1 << kHist0Bits); i += 256) s_hist[i] = 0u;
   __syncthreads();
 
-  for (int start = blockIdx.x * kVoteTile; start < len; start += gridDim.x * kVoteTile) {
+  int start = blockIdx.x * kVoteTile;
+  do {
     if (fast) {
       constexpr int TPG = 8;                       // tokens per lane group and round
       constexpr int WT = kVoteTile / 4;            // tokens per wave
@@ -472,7 +476,9 @@ __global__ __launch_bounds__(256) void votes_kernel(VoteParams p) {
         if (p.do_hist) atomicAdd(&s_hist[float_key(v) >> (32 - kHist0Bits)], 1u);
       }
     }
-  }
+    if constexpr (!WALK) break;
+    start += gridDim.x * kVoteTile;
+  } while (start < len);
   if (!p.do_hist) return;
   __syncthreads();
   uint32_t* gh = p.ctrl + (size_t)b * kCtrlStride + kCtlHist0 +
@@ -526,7 +532,8 @@ hipError_t launch_lse(const LseParams& p, hipStream_t s) {
 }
 
 hipError_t launch_votes(const VoteParams& p, int grid_x, hipStream_t s) {
-  TS_KLAUNCH(votes_kernel, dim3(grid_x, p.B), dim3(256), 0, s, p);
+  if (grid_x * kVoteTile < p.Lpad) TS_KLAUNCH(votes_kernel<true>, dim3(grid_x, p.B), dim3(256), 0, s, p);
+  else TS_KLAUNCH(votes_kernel<false>, dim3(grid_x, p.B), dim3(256), 0, s, p);
   return hipGetLastError();
 }
 
