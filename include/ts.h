@@ -243,7 +243,10 @@ ts_status ts_dense_attend(const ts_kv_layout* layout /*[host]*/, int32_t batch, 
  *   compare_mode 0: compare with the previous step's query (stored every step);
  *   compare_mode 1: compare with the query of the last miss (the anchor).
  * Per sequence it keeps the stored query (fp32, Hq*d), the last selection
- * ([k] int32), a valid flag and hit/miss counters, all in device memory.
+ * ([k] int32), a valid flag and hit/miss counters, all in device memory,
+ * plus per-head fp64 sums that a decode step's scoring kernel fills and its
+ * last kernel clears (the softmax denominators of step 2), so one cache must
+ * not serve two decode steps in flight at once.
  * A step hits when the state is valid and cos(q, stored) > theta (strict; the
  * cosine is accumulated in fp64 over the flattened Hq*d query; a zero norm
  * never hits). The first step, a step after reset and a step on an empty

@@ -631,6 +631,12 @@ __global__ __launch_bounds__(128) void combine_kernel(CombineParams p) {
                          : __float_as_uint(((const float*)p.q)[qo]);
     if (p.idx_out && lo + tid < hi) sel0 = p.cache.sel[(size_t)b * ck + lo + tid];
   }
+  // the step's fp64 log-sum-exp sums (read by the vote kernel, which ran
+  // before this one) start the next step at zero
+  if (upd && p.cache.lse_sum && tid < kLseCopies) {
+    p.cache.lse_sum[((size_t)b * p.Hq + h) * kLseCopies + tid] = 0.0;
+    if (h == 0 && tid == 0) p.cache.lse_big[b] = 0u;
+  }
   float pmv = -INFINITY, plv = 0.f;
   if (tid < ns) {
     pmv = p.pm[base + tid];

@@ -25,7 +25,10 @@
 //
 // lse_kernel: one wave per (sequence, head) folds the tile partials into the
 // head's log-sum-exp (a kernel boundary is the cross-work-group step: device-
-// scope fences cost far more on this multi-XCD part).
+// scope fences cost far more on this multi-XCD part). A decode step has no
+// such kernel: each K-scan work-group adds its tiles' terms L*2^M per head to
+// fp64 sums with atomics (no ordering is needed, the next kernel boundary
+// publishes them), and the vote kernel takes log2 of the sum.
 //
 // Pass 2 (votes_kernel) turns the logits into votes v[j] = sum_h
 // exp2(s[h,j] - lse[h]) and, for the decode path, adds them to the first
@@ -338,6 +341,18 @@ __global__ __launch_bounds__(256) void score_pass1_kernel(ScoreParams p) {
     }
     const int head = kv * p.G + slice * GS + hh;
     p.partials[((size_t)b * p.Hq + head) * p.ntiles + tile] = make_float2(M, L);
+    // decode steps: the head's sum over all tiles, L * 2^M in fp64, in copy
+    // tile % kLseCopies (a work-group's heads fall in different cache lines,
+    // and each line takes few atomics); the vote kernel adds the copies and
+    // takes log2. An atomic sum replaces a kernel boundary, at the cost of the
+    // last bits of the fp64 sum depending on the order the tiles arrive in.
+    if (p.lse_sum && L > 0.f) {
+      if (M > kLseMaxExp)
+        atomicOr(p.lse_big + b, 1u);
+      else
+        unsafeAtomicAdd(p.lse_sum + ((size_t)b * p.Hq + head) * kLseCopies + (tile & (kLseCopies - 1)),
+                  (double)L * exp2((double)M));
+    }
   }
   // control-block reset for the top-k of this step, spread over the
   // sequence's work-groups (all of them reach this point on a miss)
@@ -385,6 +400,20 @@ __global__ __launch_bounds__(64) void lse_kernel(LseParams p) {
   if (lane == 0) p.lse[(size_t)b * p.Hq + h] = Mw + log2f(Lw);
 }
 
+// A head's base-2 log-sum-exp from its tile partials (max, sum of exp2), in
+// the order the tiles lie; one thread, used only when the fp64 sums of a
+// decode step are out of range.
+__device__ __noinline__ float fold_tile_partials(const float2* pp, int nt) {
+  float M = -INFINITY;
+  for (int t = 0; t < nt; ++t) M = fmaxf(M, pp[t].x);
+  float L = 0.f;
+  for (int t = 0; t < nt; ++t) {
+    const float2 e = pp[t];
+    if (e.y > 0.f) L += e.y * ex2(e.x - M);
+  }
+  return M + log2f(L);
+}
+
 // votes: kVoteTile tokens per work-group. A token's logits for all heads are
 // contiguous (token-major), so when Hq is a multiple of 4 eight lanes share a
 // token: lane i of the group loads heads 4i..4i+3 (and 32 further on, for
@@ -406,18 +435,59 @@ __global__ __launch_bounds__(256) void votes_kernel(VoteParams p) {
   const int len = p.seq_lens[b];
   const int li = tid & 7;                        // lane in the group (fast path)
   float4 lse4 = make_float4(0.f, 0.f, 0.f, 0.f);
-  if (fast && Hq <= 32) lse4 = ldf4(p.lse + (size_t)b * Hq + min(4 * li, Hq - 4));
+  // decode steps: eight threads per head read its kLseCopies fp64 sums
+  // (heads tid / 8, then 32 further on for Hq > 32)
+  const bool own = p.lse_sum != nullptr;
+  constexpr int kPer = kLseCopies / 8;           // copies per thread
+  const int sh = tid >> 3, s8 = tid & 7;
+  double2 sum2[kPer / 2];
+  uint32_t big = 0;
+  auto load_sums = [&](int h) {
+    const double2* sp = reinterpret_cast<const double2*>(
+        p.lse_sum + ((size_t)b * Hq + min(h, Hq - 1)) * kLseCopies + s8 * kPer);
+#pragma unroll
+    for (int c = 0; c < kPer / 2; ++c) sum2[c] = sp[c];
+  };
+  if (own) {
+    load_sums(sh);
+    big = p.lse_big[b];
+  } else if (fast && Hq <= 32) {
+    lse4 = ldf4(p.lse + (size_t)b * Hq + min(4 * li, Hq - 4));
+  }
   // WALK: tiles blockIdx.x, blockIdx.x + gridDim.x, ... (a grid capped below
   // the tile count keeps the launch small on a Selection-Cache hit, when every
   // work-group returns at once; each work-group zeroes and flushes its
   // histogram once); otherwise tile blockIdx.x only. (A bitwise or: both
   // loads stay in flight together, no second round trip after the flag.)
   if ((hitv != 0) | ((int)blockIdx.x * kVoteTile >= len)) return;
-  if (!fast || Hq > 32)
+  if (own) {
+    for (int h0 = 0; h0 < Hq; h0 += 32) {
+      if (h0 > 0) load_sums(h0 + sh);
+      double sum = 0.0;
+#pragma unroll
+      for (int c = 0; c < kPer / 2; ++c) sum += sum2[c].x + sum2[c].y;
+      sum += __shfl_xor(sum, 1);
+      sum += __shfl_xor(sum, 2);
+      sum += __shfl_xor(sum, 4);
+      // in range: log2 of the sum; otherwise (a tile max above kLseMaxExp, or
+      // every term tiny) the tile partials are folded here
+      const int h = h0 + sh;
+      if (s8 == 0 && h < Hq)
+        s_lse[h] = (big == 0u && sum >= ldexp(1.0, kLseMinExp))
+                       ? (float)log2(sum)
+                       : fold_tile_partials(p.partials + ((size_t)b * Hq + h) * p.ntiles,
+                                            (len + p.tile - 1) / p.tile);
+    }
+  } else if (!fast || Hq > 32) {
     for (int h = tid; h < Hq; h += 256) s_lse[h] = p.lse[(size_t)b * Hq + h];
+  }
   if (p.do_hist)
     for (int i = tid; i < (1 << kHist0Bits); i += 256) s_hist[i] = 0u;
   __syncthreads();
+  if (own && fast && Hq <= 32) {
+    const int h0 = min(4 * li, Hq - 4);
+    lse4 = make_float4(s_lse[h0], s_lse[h0 + 1], s_lse[h0 + 2], s_lse[h0 + 3]);
+  }
 
   int start = blockIdx.x * kVoteTile;
   do {

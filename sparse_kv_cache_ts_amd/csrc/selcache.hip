@@ -32,6 +32,10 @@ __global__ __launch_bounds__(256) void sel_reset_kernel(SelCacheDev c, const int
   c.valid[b] = 0;
   c.hits[b] = 0;
   c.misses[b] = 0;
+  // zero between steps already; cleared here too so that a reset always
+  // leaves the sequence's state as created
+  for (int i = 0; i < c.Hq * kLseCopies; ++i) c.lse_sum[(size_t)b * c.Hq * kLseCopies + i] = 0.0;
+  c.lse_big[b] = 0u;
 }
 
 hipError_t launch_sel_reset(const SelCacheDev& c, const int32_t* mask, hipStream_t s) {

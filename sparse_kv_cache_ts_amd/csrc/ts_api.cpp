@@ -975,9 +975,10 @@ ts_status ts_sel_cache_create(int32_t max_batch, int32_t num_q_heads, int32_t he
   c->dev.mode = compare_mode;
   hipError_t e = hipGetDevice(&c->device);
   const size_t n = (size_t)max_batch;
-  void* ptrs[7] = {nullptr};
-  const size_t sizes[7] = {n * num_q_heads * head_dim * 4, n * k * 4, n * 4, n * 4, n * 8, n * 8, n * 8};
-  for (int i = 0; i < 7 && e == hipSuccess; ++i) {
+  void* ptrs[9] = {nullptr};
+  const size_t sizes[9] = {n * num_q_heads * head_dim * 4, n * k * 4, n * 4, n * 4, n * 8, n * 8, n * 8,
+                           n * num_q_heads * kLseCopies * 8, n * 4};
+  for (int i = 0; i < 9 && e == hipSuccess; ++i) {
     e = hipMalloc(&ptrs[i], sizes[i]);
     if (e == hipSuccess) e = hipMemset(ptrs[i], 0, sizes[i]);
   }
@@ -1003,6 +1004,8 @@ ts_status ts_sel_cache_create(int32_t max_batch, int32_t num_q_heads, int32_t he
   c->dev.cos = (double*)ptrs[4];
   c->dev.hits = (long long*)ptrs[5];
   c->dev.misses = (long long*)ptrs[6];
+  c->dev.lse_sum = (double*)ptrs[7];
+  c->dev.lse_big = (uint32_t*)ptrs[8];
   *out = c;
   return ok();
 }
@@ -1017,8 +1020,8 @@ ts_status ts_sel_cache_reset(ts_sel_cache* c, const int32_t* seq_mask, void* str
 ts_status ts_sel_cache_destroy(ts_sel_cache* c) {
   if (!c) return ok();
   hipError_t e = hipDeviceSynchronize();
-  void* ptrs[7] = {c->dev.prev_q, c->dev.sel, c->dev.valid, c->dev.hit, c->dev.cos, c->dev.hits,
-                   c->dev.misses};
+  void* ptrs[9] = {c->dev.prev_q, c->dev.sel, c->dev.valid, c->dev.hit, c->dev.cos, c->dev.hits,
+                   c->dev.misses, c->dev.lse_sum, c->dev.lse_big};
   for (void* p : ptrs) {
     hipError_t f = hipFree(p);
     if (e == hipSuccess) e = f;
@@ -1116,13 +1119,21 @@ ts_status decode_launch(ts_sel_cache* cache, const Geo& g, const DecodePlan& p, 
     TS_LAUNCH_K(kKPrologue, launch_prologue(pp, batch, st), "selection-cache decision");
     sp = score_params(g, p.s, batch, ws, q, k_cache, pt, seq_lens, hit);
   }
+  // each K-scan work-group adds its tiles' log-sum-exp terms to the cache's
+  // fp64 sums, and the vote kernel takes the log-sum-exp from them: no
+  // separate fold kernel in a decode step
+  sp.lse_sum = cache->dev.lse_sum;
+  sp.lse_big = cache->dev.lse_big;
   TS_LAUNCH_K(kKScore, launch_score_pass1(g.dtype, g.d, g.paged, sp, st), "score pass 1");
-  LseParams lp = lse_params(g, p.s, batch, ws, seq_lens, hit);
-  TS_LAUNCH_K(kKLse, launch_lse(lp, st), "log-sum-exp");
   // 3. votes + first radix histogram
   float* votes = at<float>(ws, p.votes);
   VoteParams vp = vote_params(g, p.s, batch, ws, seq_lens, hit, votes, g.max_len, 1);
   vp.hist_copies = copies;
+  vp.lse_sum = cache->dev.lse_sum;
+  vp.lse_big = cache->dev.lse_big;
+  vp.partials = at<float2>(ws, p.s.partials);
+  vp.ntiles = p.s.ntiles;
+  vp.tile = p.s.tile;
   TS_LAUNCH_K(kKVotes, launch_votes(vp, vote_wgs, st), "votes");
   // 4. top-k into the cache's stored selection: the partition here, its end
   // in the attention work-groups (or, for rows too long for that, in the

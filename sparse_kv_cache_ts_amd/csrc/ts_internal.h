@@ -16,6 +16,13 @@ constexpr int kVoteWGsMax = 2048;  // vote work-groups per launch at most (each 
 constexpr int kTopkChunk = 2048;   // elements per top-k histogram/partition work-group
 constexpr int kMaxHeadsPerWG = 64; // Hkv * heads-per-slice held by one scoring WG
 constexpr int kMaxQHeads = 256;
+// decode steps sum each head's K-scan tile terms L*2^M in fp64 (one of
+// kLseCopies copies per tile, to spread the atomics); the sum is exact enough
+// and in range while every tile max M <= kLseMaxExp and the sum >= 2^kLseMinExp,
+// otherwise the vote kernel folds the tile partials instead
+constexpr int kLseCopies = 64;   // tile t adds into copy t % 64 (a power of two)
+constexpr float kLseMaxExp = 960.f;
+constexpr int kLseMinExp = -960;
 // size limits checked on the host, so that every index and size the planner
 // derives fits its integer type: tokens per sequence (max_len, n_ctx, k,
 // row_stride), sequences per call, and rows of a top-k call
@@ -84,6 +91,11 @@ struct SelCacheDev {
   double* cos;        // [max_batch] cosine of the current step (NaN if not computed)
   long long* hits;    // [max_batch] counters
   long long* misses;  // [max_batch]
+  // per (sequence, head): kLseCopies fp64 sums of the K-scan tiles' terms
+  // sum_t(tile sum * 2^tile max) for the step in flight, zero between steps
+  // (the step's combine kernel clears them after the votes have used them)
+  double* lse_sum;    // [max_batch][Hq][kLseCopies]
+  uint32_t* lse_big;  // [max_batch] set when a tile max exceeds kLseMaxExp
   int max_batch, Hq, d, k, mode;
 };
 
@@ -118,6 +130,9 @@ struct ScoreParams {
   double theta;
   uint32_t* ctrl;           // [B][kCtrlStride]: the first ctrl_words words zeroed
   int ctrl_words;
+  // decode steps: each tile's term per head added to the fp64 sums (null: none)
+  double* lse_sum;          // [B][Hq][kLseCopies]
+  uint32_t* lse_big;        // [B]
 };
 
 struct LseParams {
@@ -130,7 +145,13 @@ struct LseParams {
 
 struct VoteParams {
   const float* logits;
-  const float* lse;         // [B][Hq]
+  const float* lse;         // [B][Hq], used when lse_sum is null
+  // decode steps: the log-sum-exp from the K-scan's fp64 sums; the tile
+  // partials are folded instead when a sum is out of the safe range
+  const double* lse_sum;    // [B][Hq][kLseCopies] or null
+  const uint32_t* lse_big;  // [B]
+  const float2* partials;   // [B][Hq][ntiles]
+  int ntiles, tile;
   const int32_t* seq_lens;
   const int32_t* hit;
   float* votes;             // [B][vote_stride]

@@ -450,3 +450,43 @@ def test_decode_step_paged_page_sizes(gpu_lib, ps):
         check_attention(o[b], O.sparse_attention(q64[b], K32[b, :n], V32[b, :n], gidx[b]), 1e-2)
     c1.close()
     c2.close()
+
+
+@pytest.mark.parametrize("kind", ["tile-max-above-range", "every-term-below-range"])
+def test_decode_step_logits_outside_fp64_sum_range(gpu_lib, kind):
+    """A decode step sums each head's exp2 terms in fp64 (2^M per K-scan tile);
+    when a tile's base-2 max exceeds 960, or when every term is below 2^-960,
+    the vote kernel folds the tile partials instead. Both cases, then a normal
+    step on the same cache (the sums and the flag must start it from zero),
+    against the oracle's selection and attention."""
+    ts = gpu_lib
+    cfg = _small_cfg(kind, 1, 4, 2, 64, 3000, "bf16", 64, 41, heavy=0)
+    x = W.gen_decode(cfg, device="cuda")
+    K = x["k_cache"].float()
+    q = x["q"].float()
+    if kind == "tile-max-above-range":
+        # 8 tokens whose key is 100 x the group's first query: base-2 logit
+        # 100 * |q|^2 / 8 * log2(e), about 1150, for that head
+        pos = torch.tensor([5, 700, 701, 1500, 2047, 2048, 2900, 2999], device="cuda")
+        for kv in range(2):
+            K[0, pos, kv, :] = 100.0 * q[0, 2 * kv]
+    else:
+        # every key points against both queries of its group: every logit is
+        # near -1500 (base 2), the sum of 2^s underflows in fp64
+        for kv in range(2):
+            u = q[0, 2 * kv] + q[0, 2 * kv + 1]
+            u = u / u.norm()
+            K[0, :, kv, :] = -1500.0 * u + torch.randn(K.shape[1], 64, device="cuda")
+    x["k_cache"] = K.to(torch.bfloat16).contiguous()
+    cache = ts.SelCache(1, 4, 64, cfg.k)
+    normal = W.gen_decode(_small_cfg("normal", 1, 4, 2, 64, 3000, "bf16", 64, 42), device="cuda")
+    for step, xs in enumerate([x, normal]):
+        out, idx, hit = cache.decode_step(xs["q"], xs["k_cache"], xs["v_cache"], xs["seq_lens"], 1.0)
+        torch.cuda.synchronize()
+        assert hit.cpu().tolist() == [0]
+        q64, K32, V32 = np64(xs["q"]), np32(xs["k_cache"]), np32(xs["v_cache"])
+        gidx = idx.cpu().numpy()
+        check_selection(gidx[0], _oracle_votes(q64[0], K32[0], 3000), cfg.k)
+        ref = O.sparse_attention(q64[0], K32[0, :3000], V32[0, :3000], gidx[0])
+        check_attention(np64(out)[0], ref, 1e-2)
+    cache.close()
