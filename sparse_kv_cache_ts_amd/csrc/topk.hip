@@ -92,46 +92,72 @@ __global__ __launch_bounds__(256) void topk_partition_kernel(TopkParams p) {
   __shared__ uint32_t s_sh[8];
   __shared__ uint32_t s_base;
   const int r = blockIdx.y;
-  const int hitv = p.hit ? p.hit[r] : 0;         // requested together with the length
-  const int len = row_length(p, r);
-  const int start = blockIdx.x * kTopkChunk;
-  if (hitv || start >= len) return;
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-  const uint32_t k_eff = (uint32_t)min(p.k, len);
+  const int start = blockIdx.x * kTopkChunk;
   uint32_t* ctrl = p.ctrl + (size_t)r * kCtrlStride;
-
-  // the row's keys of this chunk, coalesced: key i of thread t is start + i*256 + t
   const float* row = p.votes + (size_t)r * p.row_stride;
+  // The flag, the length, this chunk's keys and the first four histogram
+  // copies are requested at once: the keys and copies do not depend on the
+  // flag (a row is allocated to row_stride keys, so the loads clamped there
+  // stay in bounds; keys past the length are masked below). On a
+  // Selection-Cache hit these few KB are read for nothing.
+  const int hitv = p.hit ? p.hit[r] : 0;
+  const int len = row_length(p, r);
+  // the row's keys of this chunk, coalesced: key i of thread t is start + i*256 + t
   float v[PER];
 #pragma unroll
-  for (int i = 0; i < PER; ++i) {
-    const int e = start + i * 256 + tid;
-    v[i] = (e < len) ? row[e] : 0.f;
+  for (int i = 0; i < PER; ++i) v[i] = row[min(start + i * 256 + tid, p.row_stride - 1)];
+  // the bin b0 that holds the k-th largest key: the sum of the histogram
+  // copies. Votes: first the window of 1024 bins that can hold them (4 per
+  // thread, every copy, all loads issued at once)
+  uint32_t cw[4] = {0u, 0u, 0u, 0u};
+  if (p.hist_win) {
+    uint4 a[kHistCopiesMax];
+#pragma unroll
+    for (int cp = 0; cp < kHistCopiesMax; ++cp)
+      a[cp] = cp < p.hist_copies ? ld16(ctrl + kCtlHist0 + cp * (1 << kHist0Bits) + kHistWinLo + 4 * tid)
+                                 : make_uint4(0u, 0u, 0u, 0u);
+#pragma unroll
+    for (int cp = 0; cp < kHistCopiesMax; ++cp) {
+      cw[0] += a[cp].x; cw[1] += a[cp].y; cw[2] += a[cp].z; cw[3] += a[cp].w;
+    }
   }
-  // the bin b0 that holds the k-th largest key (16 of the 4096 bins per thread)
-  // (the sum of the histogram copies; all copy loads are issued first)
-  uint32_t c[16];
+  if (hitv || start >= len) return;
+  const uint32_t k_eff = (uint32_t)min(p.k, len);
 #pragma unroll
-  for (int i = 0; i < 16; ++i) c[i] = 0u;
-  for (int cp0 = 0; cp0 < p.hist_copies; cp0 += 4) {
-    uint4 a[4][4];
-#pragma unroll
-    for (int u = 0; u < 4; ++u)
-#pragma unroll
-      for (int q = 0; q < 4; ++q)
-        a[u][q] = (cp0 + u < p.hist_copies)
-                      ? ld16(ctrl + kCtlHist0 + (cp0 + u) * (1 << kHist0Bits) + tid * 16 + 4 * q)
-                      : make_uint4(0u, 0u, 0u, 0u);
-#pragma unroll
-    for (int u = 0; u < 4; ++u)
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        c[4 * q] += a[u][q].x; c[4 * q + 1] += a[u][q].y;
-        c[4 * q + 2] += a[u][q].z; c[4 * q + 3] += a[u][q].w;
-      }
-  }
+  for (int i = 0; i < PER; ++i)
+    if (start + i * 256 + tid >= len) v[i] = 0.f;
   uint32_t cnt_b0;
-  const uint2 rb = resolve_counts<16>(c, k_eff, s_sh, &cnt_b0);
+  uint2 rb = make_uint2(0u, 0u);
+  if (p.hist_win) {
+    // (0, 0) when the window holds fewer than k_eff keys
+    rb = resolve_counts<4>(cw, k_eff, s_sh, &cnt_b0);
+    rb.x += kHistWinLo;
+  }
+  if (rb.y == 0u) {
+    // all 4096 bins, 16 per thread, four copies per round
+    uint32_t c[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) c[i] = 0u;
+    for (int cp0 = 0; cp0 < p.hist_copies; cp0 += 4) {
+      uint4 a[4][4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          a[u][q] = (cp0 + u < p.hist_copies)
+                        ? ld16(ctrl + kCtlHist0 + (cp0 + u) * (1 << kHist0Bits) + tid * 16 + 4 * q)
+                        : make_uint4(0u, 0u, 0u, 0u);
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          c[4 * q] += a[u][q].x; c[4 * q + 1] += a[u][q].y;
+          c[4 * q + 2] += a[u][q].z; c[4 * q + 3] += a[u][q].w;
+        }
+    }
+    rb = resolve_counts<16>(c, k_eff, s_sh, &cnt_b0);
+  }
   const uint32_t b0 = rb.x, need = rb.y;
   const bool whole = (need == cnt_b0);     // the whole bin is selected: no candidates
   if (blockIdx.x == 0 && tid == 0) {

@@ -301,7 +301,10 @@ void plan_topk(int rows, int row_stride, Carve& c, TopkPlan& t, bool own_ctrl) {
 }
 
 // histogram copies for `wgs` work-groups adding into one row's first histogram
-int hist_copies_for(int wgs) { return std::max(1, std::min(kHistCopiesMax, wgs / 64)); }
+int hist_copies_for(int wgs) { return std::max(1, std::min(kHistCopiesRows, wgs / 64)); }
+// a decode step's votes: more copies (each taking 32 or more work-groups), the
+// partition reading only the window of bins that can hold them
+int vote_hist_copies_for(int wgs) { return std::max(1, std::min(kHistCopiesMax, wgs / 32)); }
 // vote work-groups per sequence: one per tile, at most kVoteWGsMax over the batch
 int vote_grid(int max_len, int batch) {
   return std::max(1, std::min(cdiv(max_len, kVoteTile), kVoteWGsMax / std::max(batch, 1)));
@@ -1091,7 +1094,7 @@ ts_status decode_launch(ts_sel_cache* cache, const Geo& g, const DecodePlan& p, 
   // 1+2. Selection-Cache decision per sequence, then the K-scan on misses,
   // and the reset of the top-k control blocks
   const int vote_wgs = vote_grid(g.max_len, batch);
-  const int copies = hist_copies_for(vote_wgs);
+  const int copies = vote_hist_copies_for(vote_wgs);
   const int32_t* hit = cache->dev.hit;
   // Fused, every K-scan work-group requests its first keys before the
   // decision is known: free on a miss, wasted on a hit. With a large K-scan
@@ -1107,9 +1110,7 @@ ts_status decode_launch(ts_sel_cache* cache, const Geo& g, const DecodePlan& p, 
     sp.ctrl_words = ctrl_words_for(copies);
   } else {
     PrologueParams pp{};
-    pp.ctrl = at<uint32_t>(ws, p.s.ctrl);
     pp.rows = batch;
-    pp.ctrl_words = ctrl_words_for(copies);
     pp.cache = cache->dev;
     pp.q = q;
     pp.dtype = g.dtype;
@@ -1118,6 +1119,11 @@ ts_status decode_launch(ts_sel_cache* cache, const Geo& g, const DecodePlan& p, 
     pp.theta = theta;
     TS_LAUNCH_K(kKPrologue, launch_prologue(pp, batch, st), "selection-cache decision");
     sp = score_params(g, p.s, batch, ws, q, k_cache, pt, seq_lens, hit);
+    // the control blocks of the sequences that miss are reset by their K-scan
+    // work-groups, spread over the grid (one prologue work-group per row
+    // would write every row's histogram copies alone)
+    sp.ctrl = at<uint32_t>(ws, p.s.ctrl);
+    sp.ctrl_words = ctrl_words_for(copies);
   }
   // each K-scan work-group adds its tiles' log-sum-exp terms to the cache's
   // fp64 sums, and the vote kernel takes the log-sum-exp from them: no
@@ -1141,6 +1147,7 @@ ts_status decode_launch(ts_sel_cache* cache, const Geo& g, const DecodePlan& p, 
   TopkParams tp = topk_params(p.t, ws, batch, g.max_len, k, votes, seq_lens, 0, hit,
                               cache->dev.sel);
   tp.hist_copies = copies;
+  tp.hist_win = 1;
   const int gx = cdiv(g.max_len, kTopkChunk);
   if (p.a.range > 0) {
     tp.hist_b = 1;     // the attention work-groups start their threshold search from it

@@ -57,13 +57,20 @@ enum CtrlWord : int {
   kCtlNeed = 2,       // elements still to take inside that bin (0: the whole bin)
   kCtlHistB = 16,     // 1024 bins of key bits 19..10 over the keys of bin b0 (the partition's candidates)
   kCtlHist0 = 16 + 1024,  // kHistCopiesMax copies of 4096 bins (key bits 31..20), 16 KB apart
-  kCtlWords = kCtlHist0 + 4 * 4096,
+  kCtlWords = kCtlHist0 + 16 * 4096,
 };
-// The first histogram is spread over up to 4 copies: work-group x of a row adds
-// into copy x % hist_copies, so the few hot bins (votes of similar size share
-// their top 12 bits) see 1/hist_copies of the device-scope atomics; readers
-// sum the copies.
-constexpr int kHistCopiesMax = 4;
+// The first histogram is spread over copies: work-group x of a row adds into
+// copy x % hist_copies, so the few hot bins (votes of similar size share their
+// top 12 bits) see 1/hist_copies of the device-scope atomics; readers sum the
+// copies. Up to 4 copies for arbitrary rows, up to 16 for a decode step's
+// votes, whose partition reads only the window of bins below.
+constexpr int kHistCopiesMax = 16;
+constexpr int kHistCopiesRows = 4;
+// A vote lies in [0, Hq] with Hq <= 256 < 512, so its bin (float_key >> 20 =
+// 2048 + 8 * biased exponent + top 3 mantissa bits) is at most 3135. The
+// window [kHistWinLo, kHistWinLo + 1024) holds every vote >= 2^-119; a
+// partition that finds fewer than k keys there reads all 4096 bins.
+constexpr int kHistWinLo = 3136 - 1024;
 constexpr int kCtrlStride = ((kCtlWords + 63) / 64) * 64;   // 256-byte rows
 constexpr int kHist0Bits = 12;
 constexpr int kCandCap = 8192;    // candidates kept per row; more falls back to a row rescan
@@ -173,6 +180,7 @@ struct TopkParams {
   int rows, row_stride, k, bm_stride;
   int hist_copies;          // copies of the first histogram (1 .. kHistCopiesMax)
   int hist_b;               // partition: also count bin b0's keys by bits 19..10 (kCtlHistB)
+  int hist_win;             // 1: keys are votes in [0, 256], read the bin window first
 };
 
 struct AttendParams {
