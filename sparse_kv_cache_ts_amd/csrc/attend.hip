@@ -603,18 +603,27 @@ __global__ __launch_bounds__(256) void attend_kernel(AttendParams p) {
 // values, this thread's (max, sum) pair, the query row for the cache update)
 // is loaded up front, so the kernel waits on memory about once.
 __global__ __launch_bounds__(128) void combine_kernel(CombineParams p) {
-  constexpr int SB = 64;                 // splits whose acc values are held in registers
+  // thread t takes dimensions 4*(t % nq) .. +3 (nq = d/4 quads) of the splits
+  // t / nq, t / nq + nsg, ... (nsg = 128 / nq split groups): 16-byte loads,
+  // SB of them held in registers; the groups meet in LDS at the end
+  constexpr int SB = 16;
   __shared__ float s_w[kMaxSplits];
   __shared__ float s_red[4];
+  __shared__ __align__(16) float s_o[4 * 128];
   const int h = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
   const int lane = tid & 63, wv = tid >> 6;
   const int ns = p.nsplit;
   const size_t base = ((size_t)b * p.Hq + h) * ns;
   const bool own_d = tid < p.d;
-  const float* pa = p.pacc + base * p.d + tid;
-  float a[SB];
+  const int nq = p.d >> 2, nsg = 128 / nq;
+  const int dq = tid % nq, sg = tid / nq;
+  const float4* pa = reinterpret_cast<const float4*>(p.pacc + base * p.d) + dq;
+  float4 a[SB];
 #pragma unroll
-  for (int s = 0; s < SB; ++s) a[s] = (own_d && s < ns) ? pa[(size_t)s * p.d] : 0.f;
+  for (int i = 0; i < SB; ++i) {
+    const int s = sg + i * nsg;
+    a[i] = s < ns ? pa[(size_t)s * nq] : make_float4(0.f, 0.f, 0.f, 0.f);
+  }
   // the cache update's inputs (decision, query element, first selection
   // entry of this head's share) are requested now, not after the merge
   const bool upd = p.cache.prev_q != nullptr;
@@ -667,31 +676,35 @@ __global__ __launch_bounds__(128) void combine_kernel(CombineParams p) {
   __syncthreads();
   const float L = s_red[2] + s_red[3];
   // every split's acc was written (zeros for an empty split, whose weight is 0)
-  float o0 = 0.f, o1 = 0.f, o2 = 0.f, o3 = 0.f;
+  float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
+  auto add = [&](const float4 (&x)[SB], int s0) {
 #pragma unroll
-  for (int s = 0; s < SB; s += 4) {
-    if (s < ns) {
-      o0 = fmaf(a[s], s_w[s], o0);
-      o1 = fmaf(a[s + 1], s < ns - 1 ? s_w[s + 1] : 0.f, o1);
-      o2 = fmaf(a[s + 2], s < ns - 2 ? s_w[s + 2] : 0.f, o2);
-      o3 = fmaf(a[s + 3], s < ns - 3 ? s_w[s + 3] : 0.f, o3);
-    }
-  }
-  // more splits (dense attention): further register blocks of SB loads each
-  for (int s0 = SB; s0 < ns; s0 += SB) {
-#pragma unroll
-    for (int s = 0; s < SB; ++s) a[s] = (own_d && s0 + s < ns) ? pa[(size_t)(s0 + s) * p.d] : 0.f;
-#pragma unroll
-    for (int s = 0; s < SB; s += 4) {
-      if (s0 + s < ns) {
-        o0 = fmaf(a[s], s_w[s0 + s], o0);
-        o1 = fmaf(a[s + 1], s0 + s + 1 < ns ? s_w[s0 + s + 1] : 0.f, o1);
-        o2 = fmaf(a[s + 2], s0 + s + 2 < ns ? s_w[s0 + s + 2] : 0.f, o2);
-        o3 = fmaf(a[s + 3], s0 + s + 3 < ns ? s_w[s0 + s + 3] : 0.f, o3);
+    for (int i = 0; i < SB; ++i) {
+      const int s = s0 + sg + i * nsg;
+      if (s < ns) {
+        const float w = s_w[s];
+        o.x = fmaf(x[i].x, w, o.x); o.y = fmaf(x[i].y, w, o.y);
+        o.z = fmaf(x[i].z, w, o.z); o.w = fmaf(x[i].w, w, o.w);
       }
     }
+  };
+  add(a, 0);
+  // more splits (dense attention): further register blocks of SB loads each
+  for (int s0 = SB * nsg; s0 < ns; s0 += SB * nsg) {
+#pragma unroll
+    for (int i = 0; i < SB; ++i) {
+      const int s = s0 + sg + i * nsg;
+      a[i] = s < ns ? pa[(size_t)s * nq] : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+    add(a, s0);
   }
-  if (own_d) p.out[((size_t)b * p.Hq + h) * p.d + tid] = (L > 0.f) ? ((o0 + o1) + (o2 + o3)) / L : 0.f;
+  *reinterpret_cast<float4*>(s_o + sg * p.d + 4 * dq) = o;
+  __syncthreads();
+  if (own_d) {
+    float sum = 0.f;
+    for (int g = 0; g < nsg; ++g) sum += s_o[g * p.d + tid];
+    p.out[((size_t)b * p.Hq + h) * p.d + tid] = (L > 0.f) ? sum / L : 0.f;
+  }
 
   // Selection-Cache state update, spread over the head blocks of a sequence
   if (!upd) return;
