@@ -400,6 +400,9 @@ __global__ __launch_bounds__(64) void lse_kernel(LseParams p) {
   if (lane == 0) p.lse[(size_t)b * p.Hq + h] = Mw + log2f(Lw);
 }
 
+// read in place of a Selection-Cache flag where a call has none
+__device__ const int g_zero_flag = 0;
+
 // A head's base-2 log-sum-exp from its tile partials (max, sum of exp2), in
 // the order the tiles lie; one thread, used only when the fp64 sums of a
 // decode step are out of range.
@@ -430,8 +433,9 @@ __global__ __launch_bounds__(256) void votes_kernel(VoteParams p) {
   const int Hq = p.Hq;
   const bool fast = (Hq & 3) == 0 && Hq <= kMaxQHeads;
   // the decision, the length and (fast path) this lane's four log-sum-exps
-  // are requested together
-  const int hitv = p.hit ? p.hit[b] : 0;
+  // are requested together (the flag is read through a pointer that is never
+  // null, so its load does not sit behind a branch of its own)
+  const int hitv = *(p.hit ? p.hit + b : &g_zero_flag);
   const int len = p.seq_lens[b];
   const int li = tid & 7;                        // lane in the group (fast path)
   float4 lse4 = make_float4(0.f, 0.f, 0.f, 0.f);
