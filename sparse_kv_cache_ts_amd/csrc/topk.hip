@@ -86,6 +86,9 @@ __global__ __launch_bounds__(256) void topk_hist0_kernel(TopkParams p) {
 }
 
 // ---- step 2: partition into selected bits / threshold-bin candidates --------
+// read in place of a Selection-Cache flag where a call has none
+__device__ const int g_zero_flag = 0;
+
 __global__ __launch_bounds__(256) void topk_partition_kernel(TopkParams p) {
   constexpr int PER = kTopkChunk / 256;           // 8 keys per thread
   constexpr int SHIFT = 32 - kHist0Bits;
@@ -101,7 +104,7 @@ __global__ __launch_bounds__(256) void topk_partition_kernel(TopkParams p) {
   // flag (a row is allocated to row_stride keys, so the loads clamped there
   // stay in bounds; keys past the length are masked below). On a
   // Selection-Cache hit these few KB are read for nothing.
-  const int hitv = p.hit ? p.hit[r] : 0;
+  const int hitv = *(p.hit ? p.hit + r : &g_zero_flag);   // never a null pointer: no branch
   const int len = row_length(p, r);
   // the row's keys of this chunk, coalesced: key i of thread t is start + i*256 + t
   float v[PER];
