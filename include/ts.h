@@ -283,6 +283,9 @@ ts_status ts_sel_cache_stats(ts_sel_cache* cache, int32_t n, int64_t* hits /*[ho
  *   idx_out  [batch][k] int32 or NULL: the selection used this step
  *   hit_out  [batch] int32 or NULL: 1 where the stored selection was reused
  * The layout's num_q_heads and head_dim must match the cache; batch <= max_batch.
+ * Each head's softmax denominator (step 2) is summed in fp64 by device
+ * atomics in arrival order, so repeated calls on the same inputs agree up to
+ * the last bits of that sum (an fp32 vote could move by one ulp, rarely).
  * ------------------------------------------------------------------------- */
 ts_status ts_decode_step_workspace_size(const ts_kv_layout* layout /*[host]*/, int32_t batch,
                                         int32_t k, size_t* bytes /*[host] out*/);
