@@ -490,3 +490,31 @@ def test_decode_step_logits_outside_fp64_sum_range(gpu_lib, kind):
         ref = O.sparse_attention(q64[0], K32[0, :3000], V32[0, :3000], gidx[0])
         check_attention(np64(out)[0], ref, 1e-2)
     cache.close()
+
+
+def test_decode_step_fewer_votes_than_k_above_window(gpu_lib):
+    """Every head's softmax sits on 8 planted keys (key = 200 x the head's own
+    query, one query head per KV head): all other votes are exactly zero, so
+    fewer than k keys fall in the partition's bin window [2112, 3136) and it
+    reads all 4096 bins; the k-th vote is 0 and the zero votes tie."""
+    ts = gpu_lib
+    cfg = _small_cfg("fewer-than-k", 1, 2, 2, 64, 3000, "bf16", 64, 43, heavy=0)
+    x = W.gen_decode(cfg, device="cuda")
+    K = x["k_cache"].float()
+    q = x["q"].float()
+    pos = torch.tensor([3, 400, 401, 999, 1500, 2047, 2048, 2999], device="cuda")
+    for kv in range(2):
+        K[0, pos, kv, :] = 200.0 * q[0, kv]
+    x["k_cache"] = K.to(torch.bfloat16).contiguous()
+    cache = ts.SelCache(1, 2, 64, cfg.k)
+    out, idx, hit = cache.decode_step(x["q"], x["k_cache"], x["v_cache"], x["seq_lens"], 1.0)
+    torch.cuda.synchronize()
+    q64, K32, V32 = np64(x["q"]), np32(x["k_cache"]), np32(x["v_cache"])
+    v_ref = _oracle_votes(q64[0], K32[0], 3000)
+    assert (v_ref > 0).sum() == 8
+    gidx = idx.cpu().numpy()
+    check_selection(gidx[0], v_ref, cfg.k)
+    assert set(pos.tolist()) <= set(gidx[0].tolist())
+    ref = O.sparse_attention(q64[0], K32[0, :3000], V32[0, :3000], gidx[0])
+    check_attention(np64(out)[0], ref, 1e-2)
+    cache.close()
