@@ -99,11 +99,11 @@ __global__ __launch_bounds__(256) void topk_partition_kernel(TopkParams p) {
   const int start = blockIdx.x * kTopkChunk;
   uint32_t* ctrl = p.ctrl + (size_t)r * kCtrlStride;
   const float* row = p.votes + (size_t)r * p.row_stride;
-  // The flag, the length, this chunk's keys and the first four histogram
-  // copies are requested at once: the keys and copies do not depend on the
-  // flag (a row is allocated to row_stride keys, so the loads clamped there
-  // stay in bounds; keys past the length are masked below). On a
-  // Selection-Cache hit these few KB are read for nothing.
+  // The flag, the length, this chunk's keys and (decode votes) the bin
+  // window of every histogram copy are requested at once: the keys and copies
+  // do not depend on the flag (a row is allocated to row_stride keys, so the
+  // loads clamped there stay in bounds; keys past the length are masked
+  // below). On a Selection-Cache hit these few KB are read for nothing.
   const int hitv = *(p.hit ? p.hit + r : &g_zero_flag);   // never a null pointer: no branch
   const int len = row_length(p, r);
   // the row's keys of this chunk, coalesced: key i of thread t is start + i*256 + t
