@@ -33,7 +33,7 @@
 // Pass 2 (votes_kernel) turns the logits into votes v[j] = sum_h
 // exp2(s[h,j] - lse[h]) and, for the decode path, adds them to the first
 // radix histogram of the top-k (an LDS histogram per work-group, flushed with
-// global atomics into one of up to four copies).
+// global atomics into one of several copies: up to 16 in a decode step).
 #include "selcache.h"
 
 namespace ts {
