@@ -24,22 +24,30 @@ __global__ __launch_bounds__(256) void prologue_kernel(PrologueParams p) {
 
 // Selection-Cache reset of the sequences whose mask entry is non-zero (all
 // sequences when the mask is null): they become invalid, so their next step
-// misses, and their counters restart from zero.
+// misses, and their counters restart from zero. The per-head log-sum-exp
+// sums are zero between steps already; they are cleared here too (one
+// element per thread, grid-stride) so that a reset always leaves the
+// sequence's state as created.
 __global__ __launch_bounds__(256) void sel_reset_kernel(SelCacheDev c, const int32_t* mask) {
-  const int b = blockIdx.x * 256 + threadIdx.x;
-  if (b >= c.max_batch) return;
-  if (mask && mask[b] == 0) return;
-  c.valid[b] = 0;
-  c.hits[b] = 0;
-  c.misses[b] = 0;
-  // zero between steps already; cleared here too so that a reset always
-  // leaves the sequence's state as created
-  for (int i = 0; i < c.Hq * kLseCopies; ++i) c.lse_sum[(size_t)b * c.Hq * kLseCopies + i] = 0.0;
-  c.lse_big[b] = 0u;
+  const long per = (long)c.Hq * kLseCopies;
+  const long n = (long)c.max_batch * per;
+  for (long i = (long)blockIdx.x * 256 + threadIdx.x; i < n; i += (long)gridDim.x * 256) {
+    const int b = (int)(i / per);
+    if (mask && mask[b] == 0) continue;
+    c.lse_sum[i] = 0.0;
+    if (i - (long)b * per == 0) {
+      c.valid[b] = 0;
+      c.hits[b] = 0;
+      c.misses[b] = 0;
+      c.lse_big[b] = 0u;
+    }
+  }
 }
 
 hipError_t launch_sel_reset(const SelCacheDev& c, const int32_t* mask, hipStream_t s) {
-  TS_KLAUNCH(sel_reset_kernel, dim3((c.max_batch + 255) / 256), dim3(256), 0, s, c, mask);
+  const long n = (long)c.max_batch * c.Hq * kLseCopies;
+  const int grid = (int)std::min<long>((n + 255) / 256, 1024);
+  TS_KLAUNCH(sel_reset_kernel, dim3(grid), dim3(256), 0, s, c, mask);
   return hipGetLastError();
 }
 
