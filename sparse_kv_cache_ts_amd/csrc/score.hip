@@ -452,6 +452,9 @@ __global__ __launch_bounds__(256) void votes_kernel(VoteParams p) {
 #pragma unroll
     for (int c = 0; c < kPer / 2; ++c) sum2[c] = sp[c];
   };
+  // a decision taken by an earlier kernel (large grids, where the reads on a
+  // hit would add up): return before requesting anything
+  if (p.hit_first && ((hitv != 0) | ((int)blockIdx.x * kVoteTile >= len))) return;
   if (own) {
     load_sums(sh);
     big = p.lse_big[b];

@@ -106,6 +106,9 @@ __global__ __launch_bounds__(256) void topk_partition_kernel(TopkParams p) {
   // below). On a Selection-Cache hit these few KB are read for nothing.
   const int hitv = *(p.hit ? p.hit + r : &g_zero_flag);   // never a null pointer: no branch
   const int len = row_length(p, r);
+  // a decision taken by an earlier kernel (large grids, where the reads on a
+  // hit would add up): return before requesting anything
+  if (p.hit_first && (hitv || start >= len)) return;
   // the row's keys of this chunk, coalesced: key i of thread t is start + i*256 + t
   float v[PER];
 #pragma unroll

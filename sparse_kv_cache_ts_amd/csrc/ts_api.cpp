@@ -1140,6 +1140,7 @@ ts_status decode_launch(ts_sel_cache* cache, const Geo& g, const DecodePlan& p, 
   vp.partials = at<float2>(ws, p.s.partials);
   vp.ntiles = p.s.ntiles;
   vp.tile = p.s.tile;
+  vp.hit_first = kscan_wgs >= kFusedDecisionMaxWGs;
   TS_LAUNCH_K(kKVotes, launch_votes(vp, vote_wgs, st), "votes");
   // 4. top-k into the cache's stored selection: the partition here, its end
   // in the attention work-groups (or, for rows too long for that, in the
@@ -1148,6 +1149,7 @@ ts_status decode_launch(ts_sel_cache* cache, const Geo& g, const DecodePlan& p, 
                               cache->dev.sel);
   tp.hist_copies = copies;
   tp.hist_win = 1;
+  tp.hit_first = kscan_wgs >= kFusedDecisionMaxWGs;
   const int gx = cdiv(g.max_len, kTopkChunk);
   if (p.a.range > 0) {
     tp.hist_b = 1;     // the attention work-groups start their threshold search from it

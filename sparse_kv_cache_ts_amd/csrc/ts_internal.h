@@ -159,6 +159,7 @@ struct VoteParams {
   const uint32_t* lse_big;  // [B]
   const float2* partials;   // [B][Hq][ntiles]
   int ntiles, tile;
+  int hit_first;            // 1: return on a hit before requesting any data
   const int32_t* seq_lens;
   const int32_t* hit;
   float* votes;             // [B][vote_stride]
@@ -181,6 +182,8 @@ struct TopkParams {
   int hist_copies;          // copies of the first histogram (1 .. kHistCopiesMax)
   int hist_b;               // partition: also count bin b0's keys by bits 19..10 (kCtlHistB)
   int hist_win;             // 1: keys are votes in [0, 256], read the bin window first
+  int hit_first;            // 1: return on a hit before requesting any data (the
+                            // decision came from an earlier kernel; large grids)
 };
 
 struct AttendParams {
